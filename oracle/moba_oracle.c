@@ -1,0 +1,407 @@
+/*
+ * moba_oracle.c -- plain, slow, obviously-correct CPU reference of the
+ * Mixture of Block Attention (MoBA) forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the package's smoke check and the
+ * benchmark's CPU-baseline leg do.  It shares no code, header or table with
+ * the HIP library.
+ *
+ * Source of every step: "Optimizing Mixture of Block Attention" (Xiao, Guo,
+ * Mazaheri, Han), summary pages:
+ *   - task definition ("Definizione del Compito"): O = softmax(QK^T/sqrt(d))V
+ *     restricted to the selected blocks; N keys split into n = N/B blocks;
+ *     each query keeps its top-k blocks;
+ *   - statistical model ("Architettura del Modello Statistico", router score
+ *     equation): block score s_j = q . kbar_j, kbar_j the mean of the keys of
+ *     block j;
+ *   - key convolution ("Progettazione della Convoluzione delle Chiavi
+ *     (Appendice B)", formal-form equation): depthwise causal conv over the
+ *     sequence, one filter per channel, left padding; the page's form adds
+ *     the input back after a SiLU.
+ * Causal rules not on the pages (own block always kept, future blocks
+ * masked, token-causal inside the own block, lower block index wins ties) are
+ * the plainest reading of a decoder model and are stated at each step.
+ *
+ * Precision: all sums and dot products accumulate in fp64, sequentially, in
+ * the order written.  Exception (a quantised result): the key convolution's
+ * output is rounded to the I/O dtype, so it is computed in fp32 with fmaf in
+ * a fixed order (taps from the oldest to the newest token) exactly as the
+ * kernel computes it, and both sides take the rounding decision in the same
+ * precision.  Build with -ffp-contract=off and without -ffast-math.
+ *
+ * Tensors are fp32 arrays [tokens][heads][d] holding the exact values of the
+ * I/O dtype (bf16 inputs are decoded to fp32 by the caller).  Sequences are
+ * given as cu[0..nseq] over the token axis; each sequence is independent.
+ *
+ * Parity status: every function here is pinned by CPU tests (see the
+ * oracle tests): conv against a library conv1d in fp64 and special cases,
+ * centroids against a library mean, routing against brute-force argsort and
+ * hand-computed integer cases, attention against library SDPA (dense and
+ * explicit-mask) and closed-form special cases.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------- bf16 round-to-nearest-even (IEEE definition) ---------- */
+static float round_to_bf16(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u) {          /* inf / nan */
+        if (u & 0x007fffffu) u |= 0x00400000u;        /* quiet nan */
+        u &= 0xffff0000u;
+    } else {
+        uint32_t lsb = (u >> 16) & 1u;
+        u = (u + 0x7fffu + lsb) & 0xffff0000u;
+    }
+    float r;
+    memcpy(&r, &u, 4);
+    return r;
+}
+
+/* ---------- a tiny work-sharing pool over (sequence, head) jobs ---------- */
+typedef void (*job_fn)(void *ctx, int job);
+typedef struct {
+    job_fn fn;
+    void *ctx;
+    int njobs;
+    volatile int next;
+    pthread_mutex_t mu;
+} pool_t;
+
+static void *pool_worker(void *arg)
+{
+    pool_t *p = (pool_t *)arg;
+    for (;;) {
+        pthread_mutex_lock(&p->mu);
+        int j = p->next++;
+        pthread_mutex_unlock(&p->mu);
+        if (j >= p->njobs) break;
+        p->fn(p->ctx, j);
+    }
+    return NULL;
+}
+
+static void run_jobs(job_fn fn, void *ctx, int njobs, int nthreads)
+{
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > njobs) nthreads = njobs;
+    pool_t p;
+    p.fn = fn;
+    p.ctx = ctx;
+    p.njobs = njobs;
+    p.next = 0;
+    pthread_mutex_init(&p.mu, NULL);
+    if (nthreads <= 1) {
+        pool_worker(&p);
+    } else {
+        pthread_t *th = (pthread_t *)malloc(sizeof(pthread_t) * (size_t)nthreads);
+        for (int i = 0; i < nthreads; ++i) pthread_create(&th[i], NULL, pool_worker, &p);
+        for (int i = 0; i < nthreads; ++i) pthread_join(th[i], NULL);
+        free(th);
+    }
+    pthread_mutex_destroy(&p.mu);
+}
+
+static int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+/* =====================================================================
+ * Step 1: key convolution (summary page, Appendice B, formal form).
+ *   conv_t = sum_{l=0}^{W-1} w[h][c][l] * k_{t-l}   (zero before the
+ *            sequence start: causal, left padded, per sequence)
+ *   mode 0 ("plain"):        k'_t = conv_t
+ *   mode 1 (page's form):    k'_t = k_t + SiLU(conv_t)
+ * The tap sum is fp32 fmaf from the oldest tap (l = W-1) to l = 0, started
+ * at +0; taps before the sequence start are skipped.  k' is rounded to the
+ * I/O dtype (bf16 RNE when round_bf16 != 0).
+ * ===================================================================== */
+typedef struct {
+    const float *k, *w;
+    float *out;
+    const int *cu;
+    int H, d, W, mode, round_bf16;
+} conv_ctx;
+
+static void conv_job(void *vctx, int job)
+{
+    conv_ctx *c = (conv_ctx *)vctx;
+    int s = job / c->H, h = job % c->H;
+    int t0 = c->cu[s], t1 = c->cu[s + 1];
+    for (int t = t0; t < t1; ++t) {
+        for (int ch = 0; ch < c->d; ++ch) {
+            const float *wv = c->w + ((size_t)h * c->d + ch) * c->W;
+            float acc = 0.0f;
+            for (int l = c->W - 1; l >= 0; --l) {
+                if (t - l < t0) continue;
+                float x = c->k[((size_t)(t - l) * c->H + h) * c->d + ch];
+                acc = fmaf(wv[l], x, acc);
+            }
+            float r;
+            if (c->mode == 0) {
+                r = acc;
+            } else {
+                double a = (double)acc;
+                double silu = a / (1.0 + exp(-a));
+                r = (float)((double)c->k[((size_t)t * c->H + h) * c->d + ch] + silu);
+            }
+            if (c->round_bf16) r = round_to_bf16(r);
+            c->out[((size_t)t * c->H + h) * c->d + ch] = r;
+        }
+    }
+}
+
+int moba_oracle_key_conv(const float *k, const float *w, int H, int d, int W,
+                         int mode, int round_bf16, const int *cu, int nseq,
+                         float *out, int nthreads)
+{
+    if (W < 1 || (mode != 0 && mode != 1)) return 1;
+    conv_ctx c = {k, w, out, cu, H, d, W, mode, round_bf16};
+    run_jobs(conv_job, &c, nseq * H, nthreads);
+    return 0;
+}
+
+/* =====================================================================
+ * Step 2: block centroids (summary page, statistical model, router-score
+ * equation: kbar_j = (1/B) sum_{k in block j} k).
+ * Block j of a sequence covers local tokens [jB, min((j+1)B, L)); a final
+ * partial block is averaged over the keys it holds.  The sum is fp64 in
+ * token order, divided once, rounded once to fp32.
+ * Output rows are [global block][H][d] with blocks sequence-major.
+ * ===================================================================== */
+typedef struct {
+    const float *k;
+    float *cent;
+    const int *cu;
+    const int *boff;
+    int H, d, B;
+} cent_ctx;
+
+static void cent_job(void *vctx, int job)
+{
+    cent_ctx *c = (cent_ctx *)vctx;
+    int s = job / c->H, h = job % c->H;
+    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    int n = ceil_div(L, c->B);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)c->d);
+    for (int j = 0; j < n; ++j) {
+        int a = j * c->B, b = (j + 1) * c->B < L ? (j + 1) * c->B : L;
+        for (int ch = 0; ch < c->d; ++ch) acc[ch] = 0.0;
+        for (int u = a; u < b; ++u)
+            for (int ch = 0; ch < c->d; ++ch)
+                acc[ch] += (double)c->k[((size_t)(t0 + u) * c->H + h) * c->d + ch];
+        float *dst = c->cent + ((size_t)(c->boff[s] + j) * c->H + h) * c->d;
+        for (int ch = 0; ch < c->d; ++ch) dst[ch] = (float)(acc[ch] / (double)(b - a));
+    }
+    free(acc);
+}
+
+static int *block_offsets(const int *cu, int nseq, int B)
+{
+    int *boff = (int *)malloc(sizeof(int) * (size_t)(nseq + 1));
+    boff[0] = 0;
+    for (int s = 0; s < nseq; ++s) boff[s + 1] = boff[s] + ceil_div(cu[s + 1] - cu[s], B);
+    return boff;
+}
+
+int moba_oracle_total_blocks(const int *cu, int nseq, int B)
+{
+    int tot = 0;
+    for (int s = 0; s < nseq; ++s) tot += ceil_div(cu[s + 1] - cu[s], B);
+    return tot;
+}
+
+int moba_oracle_centroids(const float *k, int H, int d, int B, const int *cu,
+                          int nseq, float *cent, int nthreads)
+{
+    if (B < 1) return 1;
+    int *boff = block_offsets(cu, nseq, B);
+    cent_ctx c = {k, cent, cu, boff, H, d, B};
+    run_jobs(cent_job, &c, nseq * H, nthreads);
+    free(boff);
+    return 0;
+}
+
+/* =====================================================================
+ * Step 3-4: router scores and causal top-k selection.
+ *   s_{t,j} = q_t . kbar_j  (router-score equation), fp64, sequential over
+ *   channels, for the past blocks j < i = floor(t_local / B) only (future
+ *   blocks are masked).  The own block i is always kept and does not
+ *   compete.  Of the i past blocks, the first m = min(k-1, i) in the total
+ *   order (score descending, block index ascending) are kept.
+ *   Output row: ascending block ids (local to the sequence), own block
+ *   included, padded with -1 to length k.
+ *   Near-tie record (for i >= k): a = (k-1)-th best past score, b = k-th
+ *   best; exempt = |a-b| <= 1e-5 * max(|a|,|b|,1e-30).
+ * ===================================================================== */
+typedef struct {
+    const float *q, *cent;
+    int *idx;
+    double *gap_a, *gap_b;
+    unsigned char *exempt;
+    const int *cu, *boff;
+    int H, d, B, K;
+} route_ctx;
+
+/* strict "a ranks before b": higher score first, lower index on ties */
+static int ranks_before(double sa, int ja, double sb, int jb)
+{
+    if (sa > sb) return 1;
+    if (sa < sb) return 0;
+    return ja < jb;
+}
+
+static int cmp_int(const void *a, const void *b)
+{
+    int x = *(const int *)a, y = *(const int *)b;
+    return (x > y) - (x < y);
+}
+
+static void route_job(void *vctx, int job)
+{
+    route_ctx *c = (route_ctx *)vctx;
+    int s = job / c->H, h = job % c->H;
+    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    int n = ceil_div(L, c->B);
+    double *sc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+    int *order = (int *)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
+    int *row = (int *)malloc(sizeof(int) * (size_t)c->K);
+    for (int tl = 0; tl < L; ++tl) {
+        size_t t = (size_t)(t0 + tl);
+        int i = tl / c->B;
+        const float *qv = c->q + (t * c->H + h) * c->d;
+        /* scores of the past blocks */
+        for (int j = 0; j < i; ++j) {
+            const float *cv = c->cent + ((size_t)(c->boff[s] + j) * c->H + h) * c->d;
+            double acc = 0.0;
+            for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)cv[ch];
+            sc[j] = acc;
+        }
+        /* selection sort of the first m+1 places in the total order */
+        int m = (c->K - 1) < i ? (c->K - 1) : i;
+        int need = (m + 1) < i ? (m + 1) : i;
+        for (int j = 0; j < i; ++j) order[j] = j;
+        for (int p = 0; p < need; ++p) {
+            int best = p;
+            for (int r = p + 1; r < i; ++r)
+                if (ranks_before(sc[order[r]], order[r], sc[order[best]], order[best])) best = r;
+            int tmp = order[p]; order[p] = order[best]; order[best] = tmp;
+        }
+        for (int p = 0; p < m; ++p) row[p] = order[p];
+        row[m] = i;
+        qsort(row, (size_t)(m + 1), sizeof(int), cmp_int);
+        for (int p = m + 1; p < c->K; ++p) row[p] = -1;
+        int *dst = c->idx + (t * c->H + h) * c->K;
+        for (int p = 0; p < c->K; ++p) dst[p] = row[p];
+        size_t r = t * c->H + h;
+        if (c->gap_a) {
+            if (i >= c->K && c->K >= 2) {
+                double a = sc[order[c->K - 2]], b = sc[order[c->K - 1]];
+                double mx = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+                if (mx < 1e-30) mx = 1e-30;
+                c->gap_a[r] = a;
+                c->gap_b[r] = b;
+                c->exempt[r] = (fabs(a - b) <= 1e-5 * mx) ? 1 : 0;
+            } else {
+                c->gap_a[r] = NAN;
+                c->gap_b[r] = NAN;
+                c->exempt[r] = 0;
+            }
+        }
+    }
+    free(sc);
+    free(order);
+    free(row);
+}
+
+int moba_oracle_route(const float *q, const float *cent, int H, int d, int B,
+                      int K, const int *cu, int nseq, int *idx, double *gap_a,
+                      double *gap_b, unsigned char *exempt, int nthreads)
+{
+    if (B < 1 || K < 1) return 1;
+    int *boff = block_offsets(cu, nseq, B);
+    route_ctx c = {q, cent, idx, gap_a, gap_b, exempt, cu, boff, H, d, B, K};
+    run_jobs(route_job, &c, nseq * H, nthreads);
+    free(boff);
+    return 0;
+}
+
+/* =====================================================================
+ * Step 5: attention over the selected blocks (task definition:
+ * O = softmax(QK^T / sqrt(d)) V restricted to the selected blocks).
+ *   Key set of query t (block i): every key of each listed past block
+ *   j (0 <= j < i) plus the keys u <= t of its own block i (token-causal).
+ *   Entries equal to -1 are padding; entries > i are ignored (future).
+ *   z_u = scale * (q_t . k_u) in fp64; M = max z; l = sum exp(z - M);
+ *   O_t = sum exp(z_u - M) v_u / l;  LSE_t = M + ln l.
+ * The own block is always attended, listed or not.
+ * ===================================================================== */
+typedef struct {
+    const float *q, *k, *v;
+    const int *idx;
+    double *o, *lse;
+    const int *cu;
+    int H, d, B, K;
+    double scale;
+} attn_ctx;
+
+static void attn_job(void *vctx, int job)
+{
+    attn_ctx *c = (attn_ctx *)vctx;
+    int s = job / c->H, h = job % c->H;
+    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    int maxkeys = c->K * c->B + c->B;
+    double *z = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int *keys = (int *)malloc(sizeof(int) * (size_t)maxkeys);
+    for (int tl = 0; tl < L; ++tl) {
+        size_t t = (size_t)(t0 + tl);
+        int i = tl / c->B;
+        const int *row = c->idx + (t * c->H + h) * c->K;
+        int nk = 0;
+        /* listed past blocks, in row order */
+        for (int p = 0; p < c->K; ++p) {
+            int j = row[p];
+            if (j < 0 || j >= i) continue;
+            for (int u = j * c->B; u < (j + 1) * c->B && u < L; ++u) keys[nk++] = u;
+        }
+        /* own block, causal */
+        for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
+        const float *qv = c->q + (t * c->H + h) * c->d;
+        double M = -INFINITY;
+        for (int e = 0; e < nk; ++e) {
+            const float *kv = c->k + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
+            double acc = 0.0;
+            for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)kv[ch];
+            z[e] = c->scale * acc;
+            if (z[e] > M) M = z[e];
+        }
+        double l = 0.0;
+        for (int e = 0; e < nk; ++e) l += exp(z[e] - M);
+        double *ov = c->o + (t * c->H + h) * c->d;
+        for (int ch = 0; ch < c->d; ++ch) ov[ch] = 0.0;
+        for (int e = 0; e < nk; ++e) {
+            double p = exp(z[e] - M);
+            const float *vv = c->v + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
+            for (int ch = 0; ch < c->d; ++ch) ov[ch] += p * (double)vv[ch];
+        }
+        for (int ch = 0; ch < c->d; ++ch) ov[ch] /= l;
+        if (c->lse) c->lse[t * c->H + h] = M + log(l);
+    }
+    free(z);
+    free(keys);
+}
+
+int moba_oracle_attend(const float *q, const float *k, const float *v,
+                       const int *idx, int H, int d, int B, int K,
+                       const int *cu, int nseq, double scale, double *o,
+                       double *lse, int nthreads)
+{
+    if (B < 1 || K < 1) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    attn_ctx c = {q, k, v, idx, o, lse, cu, H, d, B, K, scale};
+    run_jobs(attn_job, &c, nseq * H, nthreads);
+    return 0;
+}

@@ -1,0 +1,382 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these checks re-types the oracle's own loops: each compares it with a
+library routine (torch conv1d / mean / scaled_dot_product_attention, numpy
+matmul + stable argsort), a closed form, a hand-worked example
+(tests/golden), or an invariant that a dropped term, wrong sign, wrong index
+or transposed operand would break.
+
+Source: "Optimizing Mixture of Block Attention" summary page -- task
+definition ("Definizione del Compito"), router-score equation
+("Architettura del Modello Statistico"), key convolution ("Appendice B").
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, dtype=np.float32):
+    g = np.random.default_rng(seed)
+    return g.standard_normal(shape).astype(dtype)
+
+
+def _bf16(a: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(a).to(torch.bfloat16).float().numpy()
+
+
+# ---------------------------------------------------------------- conv ----
+def _conv_ref64(k, w, cu):
+    """Library conv1d in fp64, per sequence (weights flipped: torch's conv1d
+    correlates, the page's form convolves k_{t-l} with w_l)."""
+    T, H, d = k.shape
+    W = w.shape[-1]
+    out = np.zeros((T, H, d), dtype=np.float64)
+    wt = torch.from_numpy(w[:, :, ::-1].copy()).double().reshape(H * d, 1, W)
+    for s in range(len(cu) - 1):
+        x = torch.from_numpy(k[cu[s]:cu[s + 1]]).double().reshape(-1, H * d).T[None]
+        x = F.pad(x, (W - 1, 0))
+        y = F.conv1d(x, wt, groups=H * d)[0].T.reshape(-1, H, d)
+        out[cu[s]:cu[s + 1]] = y.numpy()
+    return out
+
+
+@pytest.mark.parametrize("W", [1, 3, 4, 8])
+def test_conv_plain_matches_library_conv1d(W):
+    T, H, d = 70, 3, 8
+    k = _rand((T, H, d), 1)
+    w = _rand((H, d, W), 2) * np.float32(1 / math.sqrt(W))
+    cu = [0, 70]
+    ours = oracle.key_conv(k, w, cu, mode=0, round_bf16=False)
+    ref = _conv_ref64(k, w, cu)
+    # fp32 fmaf chain of W taps: relative error <= W * 2^-24 of sum |w x|
+    bound = (W + 1) * 2.0 ** -24 * _conv_ref64(np.abs(k), np.abs(w), cu)
+    assert np.all(np.abs(ours - ref) <= bound + 1e-30)
+
+
+def test_conv_plain_bf16_rounding_matches_fp64_rounding():
+    T, H, d, W = 400, 4, 16, 3
+    k = _bf16(_rand((T, H, d), 3))
+    w = _rand((H, d, W), 4) * np.float32(1 / math.sqrt(W))
+    cu = [0, T]
+    ours = oracle.key_conv(k, w, cu, mode=0, round_bf16=True)
+    ref = _bf16(_conv_ref64(k, w, cu).astype(np.float32))
+    same = ours == ref
+    assert same.mean() > 0.999
+    # where they differ it is by one bf16 step at a rounding boundary
+    diff = np.abs(ours - ref)[~same]
+    assert np.all(diff <= np.abs(ref[~same]) * 2.0 ** -7 + 1e-30)
+    # outputs are bf16 values
+    assert np.array_equal(ours, _bf16(ours))
+
+
+def test_conv_special_cases():
+    T, H, d, W = 20, 2, 4, 4
+    k = _bf16(_rand((T, H, d), 5))
+    cu = [0, T]
+    # identity filter (tap 0 = current token) reproduces k exactly
+    w = np.zeros((H, d, W), np.float32)
+    w[:, :, 0] = 1
+    assert np.array_equal(oracle.key_conv(k, w, cu), k)
+    # e_l shifts by l with zero fill at the sequence start
+    for l in range(W):
+        w = np.zeros((H, d, W), np.float32)
+        w[:, :, l] = 1
+        out = oracle.key_conv(k, w, cu)
+        assert np.array_equal(out[l:], k[:T - l])
+        assert np.all(out[:l] == 0)
+    # W = 1 is a per-channel scale
+    w1 = _rand((H, d, 1), 6)
+    out = oracle.key_conv(k, w1, cu, round_bf16=False)
+    assert np.array_equal(out, (k * w1[None, :, :, 0]).astype(np.float32))
+
+
+def test_conv_varlen_equals_separate_sequences():
+    H, d, W = 2, 8, 3
+    lens = [5, 17, 1, 9]
+    cu = list(np.cumsum([0] + lens))
+    k = _bf16(_rand((cu[-1], H, d), 7))
+    w = _rand((H, d, W), 8)
+    whole = oracle.key_conv(k, w, cu)
+    for s in range(len(lens)):
+        part = oracle.key_conv(k[cu[s]:cu[s + 1]], w, [0, lens[s]])
+        assert np.array_equal(whole[cu[s]:cu[s + 1]], part)
+
+
+def test_conv_silu_residual_matches_library():
+    T, H, d, W = 50, 2, 8, 5
+    k = _rand((T, H, d), 9)
+    w = _rand((H, d, W), 10) * np.float32(0.5)
+    cu = [0, T]
+    ours = oracle.key_conv(k, w, cu, mode=1, round_bf16=False)
+    conv = torch.from_numpy(_conv_ref64(k, w, cu))
+    ref = (torch.from_numpy(k).double() + F.silu(conv)).numpy()
+    assert np.allclose(ours, ref, rtol=2e-6, atol=2e-6)
+    # zero filter -> k' = k exactly
+    w0 = np.zeros_like(w)
+    assert np.array_equal(oracle.key_conv(k, w0, cu, mode=1, round_bf16=False), k)
+
+
+# ----------------------------------------------------------- centroids ----
+def test_centroids_match_library_mean():
+    H, d, B = 3, 8, 16
+    lens = [64, 40, 16, 7]             # includes partial last blocks
+    cu = list(np.cumsum([0] + lens))
+    k = _bf16(_rand((cu[-1], H, d), 11))
+    cent = oracle.centroids(k, B, cu)
+    rows = []
+    for s, L in enumerate(lens):
+        for j in range((L + B - 1) // B):
+            a, b = cu[s] + j * B, min(cu[s] + (j + 1) * B, cu[s + 1])
+            rows.append(torch.from_numpy(k[a:b]).double().mean(dim=0).float().numpy())
+    ref = np.stack(rows)
+    assert cent.shape == ref.shape
+    assert np.array_equal(cent, ref)
+    assert oracle.total_blocks(cu, B) == len(rows)
+
+
+def test_centroid_of_constant_block_is_that_key():
+    H, d, B = 1, 4, 8
+    k = np.zeros((16, H, d), np.float32)
+    k[:8] = np.array([0.1, -3.5, 7.25, 1e-3], np.float32)
+    k[8:] = _rand((8, H, d), 12)
+    cent = oracle.centroids(k, B, [0, 16])
+    assert np.array_equal(cent[0, 0], k[0, 0])
+
+
+# ------------------------------------------------------------- routing ----
+def _route_brute(q, cent, B, K, cu):
+    """Full fp64 score matrix (matmul), causal mask, stable argsort."""
+    T, H, d = q.shape
+    idx = np.full((T, H, K), -1, np.int32)
+    boff = 0
+    for s in range(len(cu) - 1):
+        L = cu[s + 1] - cu[s]
+        n = (L + B - 1) // B
+        for h in range(H):
+            S = q[cu[s]:cu[s + 1], h].astype(np.float64) @ cent[boff:boff + n, h].astype(np.float64).T
+            for tl in range(L):
+                i = tl // B
+                past = S[tl, :i]
+                order = np.argsort(-past, kind="stable")[:min(K - 1, i)]
+                row = sorted(order.tolist() + [i])
+                idx[cu[s] + tl, h, :len(row)] = row
+        boff += n
+    return idx
+
+
+@pytest.mark.parametrize("B,K,lens", [(4, 3, [64]), (8, 2, [40, 24]),
+                                      (4, 16, [32]), (16, 4, [100, 3, 50])])
+def test_route_matches_bruteforce(B, K, lens):
+    H, d = 2, 8
+    cu = list(np.cumsum([0] + lens))
+    q = _bf16(_rand((cu[-1], H, d), 13))
+    k = _bf16(_rand((cu[-1], H, d), 14))
+    cent = oracle.centroids(k, B, cu)
+    idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    assert np.array_equal(idx, _route_brute(q, cent, B, K, cu))
+
+
+def test_route_invariants():
+    H, d, B, K = 2, 8, 4, 5
+    lens = [61, 30]
+    cu = list(np.cumsum([0] + lens))
+    q = _rand((cu[-1], H, d), 15)
+    k = _rand((cu[-1], H, d), 16)
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    for s, L in enumerate(lens):
+        for tl in range(L):
+            i = tl // B
+            for h in range(H):
+                row = idx[cu[s] + tl, h]
+                valid = row[row >= 0]
+                assert i in valid                         # own block kept
+                assert np.all(valid <= i)                 # no future block
+                assert len(valid) == min(K, i + 1)        # |S| = min(k, i+1)
+                assert np.all(np.diff(valid) > 0)         # ascending, distinct
+                assert np.all(row[len(valid):] == -1)     # -1 padding at end
+
+
+def test_route_ties_go_to_lower_index():
+    # q = ones; block j's keys chosen so several blocks have equal sums.
+    B, K, d = 2, 3, 2
+    T = 10
+    q = np.ones((T, 1, d), np.float32)
+    blocks = [[1, 1], [2, 0], [0, 2], [1, 1], [5, 5]]   # sums: 2,2,2,2,10
+    k = np.zeros((T, 1, d), np.float32)
+    for j, (a, b) in enumerate(blocks):
+        k[2 * j, 0] = [a, 0]
+        k[2 * j + 1, 0] = [0, b]
+    cent = oracle.centroids(k, B, [0, T])
+    idx, ga, gb, ex = oracle.route(q, cent, B, K, [0, T])
+    # query block 4 (t=8,9): past blocks 0..3 all score 1 -> take 0 and 1
+    assert idx[8, 0].tolist() == [0, 1, 4]
+    assert idx[9, 0].tolist() == [0, 1, 4]
+    assert ex[8, 0] and ga[8, 0] == gb[8, 0]
+    # query block 3: past 0..2 tie -> 0, 1
+    assert idx[6, 0].tolist() == [0, 1, 3]
+
+
+def test_route_top_k_at_least_blocks_selects_all_past():
+    H, d, B = 1, 4, 4
+    T = 32
+    q = _rand((T, H, d), 17)
+    k = _rand((T, H, d), 18)
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, [0, T]), B, 8, [0, T])
+    for t in range(T):
+        i = t // B
+        assert idx[t, 0, :i + 1].tolist() == list(range(i + 1))
+
+
+# ----------------------------------------------------------- attention ----
+def _mask_from_idx(idx_row_sets, L, B):
+    m = np.zeros((L, L), bool)
+    for t in range(L):
+        i = t // B
+        for j in idx_row_sets[t]:
+            if j < 0:
+                continue
+            if j < i:
+                m[t, j * B:min((j + 1) * B, L)] = True
+        m[t, i * B:t + 1] = True
+    return m
+
+
+def test_attend_dense_when_topk_covers_all_blocks():
+    H, d, B, T = 2, 16, 8, 48
+    q, k, v = (_rand((T, H, d), s) for s in (19, 20, 21))
+    cu = [0, T]
+    K = T // B
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    o, lse = oracle.attend(q, k, v, idx, B, K, cu)
+    tq, tk, tv = (torch.from_numpy(x).double().permute(1, 0, 2)[None] for x in (q, k, v))
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0].permute(1, 0, 2)
+    assert np.allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+    S = (tq @ tk.transpose(-1, -2))[0] / math.sqrt(d)
+    S = S.masked_fill(torch.triu(torch.ones(T, T, dtype=torch.bool), 1), -math.inf)
+    assert np.allclose(lse, torch.logsumexp(S, -1).T.numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,K", [(4, 3), (8, 2), (4, 1)])
+def test_attend_matches_masked_sdpa(B, K):
+    H, d, T = 2, 8, 40
+    q, k, v = (_bf16(_rand((T, H, d), s)) for s in (22, 23, 24))
+    cu = [0, T]
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    scale = 0.37
+    o, lse = oracle.attend(q, k, v, idx, B, K, cu, scale=scale)
+    for h in range(H):
+        m = torch.from_numpy(_mask_from_idx([idx[t, h].tolist() for t in range(T)], T, B))
+        tq, tk, tv = (torch.from_numpy(x[:, h]).double() for x in (q, k, v))
+        ref = F.scaled_dot_product_attention(tq[None], tk[None], tv[None],
+                                             attn_mask=m[None], scale=scale)[0]
+        assert np.allclose(o[:, h], ref.numpy(), rtol=1e-12, atol=1e-12)
+        S = (tq @ tk.T * scale).masked_fill(~m, -math.inf)
+        assert np.allclose(lse[:, h], torch.logsumexp(S, -1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_attend_v_ones_gives_ones_and_v_identity_gives_probabilities():
+    H, d, B, K = 1, 32, 4, 3
+    T = 32                                          # T <= d so V = I fits
+    q, k = _rand((T, H, d), 25), _rand((T, H, d), 26)
+    cu = [0, T]
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    o, _ = oracle.attend(q, k, np.ones((T, H, d), np.float32), idx, B, K, cu)
+    assert np.allclose(o, 1.0, rtol=0, atol=1e-14)
+    eye = np.eye(T, d, dtype=np.float32)[:, None, :]
+    p, _ = oracle.attend(q, k, eye, idx, B, K, cu)
+    p = p[:, 0, :T]
+    assert np.allclose(p.sum(-1), 1.0, atol=1e-14)
+    support = _mask_from_idx([idx[t, 0].tolist() for t in range(T)], T, B)
+    assert np.all(p[~support] == 0)
+    assert np.all(p[support] > 0)
+
+
+def test_attend_single_block_is_dense_causal():
+    H, d, T = 1, 8, 24
+    B = 32                                           # one (partial) block
+    q, k, v = (_rand((T, H, d), s) for s in (27, 28, 29))
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, [0, T]), B, 2, [0, T])
+    o, _ = oracle.attend(q, k, v, idx, B, 2, [0, T])
+    tq, tk, tv = (torch.from_numpy(x).double().permute(1, 0, 2)[None] for x in (q, k, v))
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True)[0].permute(1, 0, 2)
+    assert np.allclose(o, ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------- golden + whole pass ----
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLD, "hand_worked_B2_d2.json")))
+    arr = lambda key: np.array(g[key], np.float32)[:, None, :]
+    k, q, v = arr("k"), arr("q"), arr("v")
+    B, K, cu = g["B"], g["top_k"], [0, 6]
+    cent = oracle.centroids(k, B, cu)
+    assert np.array_equal(cent[:, 0], np.array(g["centroids"], np.float32))
+    idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    assert idx[:, 0].tolist() == g["idx"]
+    assert ex[:, 0].tolist() == g["exempt"]
+    o, lse = oracle.attend(q, k, v, idx, B, K, cu, scale=math.log(2.0))
+    num = np.array(g["o_num"], np.float64)
+    assert np.allclose(o[:, 0, 0], num[:, 0] / num[:, 1], rtol=1e-14, atol=1e-14)
+    assert np.allclose(o[:, 0, 1], 1.0, rtol=1e-14)
+    assert np.allclose(lse[:, 0], np.log(np.array(g["lse_of"], np.float64)), rtol=1e-14)
+    kc = oracle.key_conv(k, np.array(g["conv_w"], np.float32)[None], cu)
+    assert np.array_equal(kc[:, 0], np.array(g["k_conv"], np.float32))
+
+
+def test_forward_heads_batches_and_sequences_are_independent():
+    H, d, B, K, W = 3, 8, 4, 3, 3
+    lens = [24, 13, 32]
+    cu = list(np.cumsum([0] + lens))
+    q, k, v = (_bf16(_rand((cu[-1], H, d), s)) for s in (30, 31, 32))
+    w = _rand((H, d, W), 33)
+    full = oracle.forward(q, k, v, B, K, cu, conv_w=w)
+    for s in range(len(lens)):
+        sl = slice(cu[s], cu[s + 1])
+        for h in range(H):
+            part = oracle.forward(q[sl, h:h + 1], k[sl, h:h + 1], v[sl, h:h + 1],
+                                  B, K, [0, lens[s]], conv_w=w[h:h + 1])
+            assert np.array_equal(full["idx"][sl, h:h + 1], part["idx"])
+            assert np.array_equal(full["o"][sl, h:h + 1], part["o"])
+    again = oracle.forward(q, k, v, B, K, cu, conv_w=w, nthreads=1)
+    assert np.array_equal(full["o"], again["o"]) and np.array_equal(full["idx"], again["idx"])
+
+
+# ----------------------------------------------------------- workloads ----
+def test_workload_generator_is_seeded_and_shaped():
+    s = workloads.spec("C1")
+    a, b = workloads.make(s), workloads.make(s)
+    assert torch.equal(a["q"], b["q"]) and torch.equal(a["v"], b["v"])
+    assert a["q"].shape == (1, 1024, 1, 64) and a["q"].dtype == torch.float32
+    s5 = workloads.spec("C5").scaled(1024)
+    x = workloads.make(s5)
+    assert x["q"].shape == (1024, 16, 128) and x["q"].dtype == torch.bfloat16
+    assert x["cu_seqlens"][0] == 0 and x["cu_seqlens"][-1] == 1024
+    assert x["conv_w"].shape == (16, 128, 4)
+
+
+def test_effective_flops_match_counts_from_oracle_idx():
+    s = workloads.Spec("t", 7, 2, 200, 2, 8, 16, 4, "f32")
+    x = workloads.make(s)
+    cu = workloads.segments(s)
+    idx, *_ = oracle.route(x["q"], oracle.centroids(x["k"], s.block_size, cu),
+                           s.block_size, s.top_k, cu)
+    keys = 0
+    for b in range(s.batch):
+        for tl in range(s.seq):
+            i = tl // s.block_size
+            for h in range(s.heads):
+                row = idx[b * s.seq + tl, h]
+                keys += s.block_size * int(np.sum((row >= 0) & (row < i)))
+                keys += tl - i * s.block_size + 1
+    assert workloads.eff_flops(s)["total"] == 4 * s.head_dim * keys
+    pairs = int(np.sum((idx >= 0) & (idx < (np.arange(s.seq) // s.block_size)[None, :, None, None].repeat(2, 0).reshape(-1, 1, 1))))
+    assert workloads.routed_pairs(s) == pairs
