@@ -1,0 +1,289 @@
+"""MI355X (gfx950) Mixture of Block Attention forward -- Python binding.
+
+A thin ctypes layer over ``libmoba_amd.so`` (C ABI in ``include/moba.h``).
+It only marshals arguments: it checks tensor devices, dtypes and layouts,
+allocates outputs and workspaces with torch (device memory only) and passes
+``data_ptr()`` values and torch's current HIP stream.  Every step of the
+computation runs in the library's HIP kernels.  If the library is missing
+the calls raise -- there is no CPU fallback.
+
+Names follow the C ABI: ``moba_key_conv``, ``moba_centroids``,
+``moba_route_topk``, ``moba_attn_fwd`` (plus its three stages
+``moba_attn_index``, ``moba_attn_routed``, ``moba_attn_combine``) and the
+convenience ``moba_fwd`` that chains them.
+
+Tensors are ``[batch, seq, heads, head_dim]`` (uniform batch) or
+``[total_tokens, heads, head_dim]`` with ``cu_seqlens`` (a python list or CPU
+int tensor of num_seqs + 1 offsets).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+__all__ = [
+    "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
+    "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
+    "moba_attn_fwd_workspace_bytes", "moba_total_blocks", "library_path",
+    "MobaError",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmoba_amd.so")
+_lib = None
+
+MOBA_F32, MOBA_BF16 = 0, 1
+_CONV_MODES = {"plain": 0, "silu_residual": 1}
+
+
+class MobaError(RuntimeError):
+    pass
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seq", ctypes.c_int32),
+        ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("cu_seqlens", ctypes.POINTER(ctypes.c_int32)),
+        ("num_seqs", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("top_k", ctypes.c_int32), ("dtype", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise MobaError(
+            f"{_LIB_PATH} is not built; run __graft_entry__.build() or "
+            "python block_sparse_long_key_amd/build.py")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    SH = ctypes.POINTER(_Shape)
+    sig = {
+        "moba_key_conv": [SH, P, P, I32, I32, P, P, P],
+        "moba_centroids": [SH, P, P, P],
+        "moba_route_topk": [SH, P, P, P, P],
+        "moba_attn_fwd": [SH, P, P, P, P, F32, P, P, P, SZ, P],
+        "moba_attn_index": [SH, P, P, SZ, P],
+        "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
+        "moba_attn_combine": [SH, P, P, P, P, F32, P, P, P, SZ, P],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = ctypes.c_int
+    lib.moba_attn_fwd_workspace_bytes.argtypes = [SH]
+    lib.moba_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moba_total_blocks.argtypes = [SH]
+    lib.moba_total_blocks.restype = ctypes.c_int64
+    lib.moba_status_string.argtypes = [ctypes.c_int]
+    lib.moba_status_string.restype = ctypes.c_char_p
+    lib.moba_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        msg = _load().moba_status_string(rc).decode()
+        raise MobaError(f"{what} failed: {msg} (status {rc})")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOBA_BF16
+    if t.dtype == torch.float32:
+        return MOBA_F32
+    raise MobaError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _make_shape(x: torch.Tensor, block_size: int, top_k: int,
+                cu_seqlens: Optional[Sequence[int]]):
+    if x.dim() == 4:
+        if cu_seqlens is not None:
+            raise MobaError("cu_seqlens needs [total_tokens, heads, head_dim] tensors")
+        b, n, h, d = x.shape
+        sh = _Shape(b, n, h, d, None, 0, block_size, top_k, _dtype_code(x))
+        return sh, None
+    if x.dim() == 3:
+        t, h, d = x.shape
+        if cu_seqlens is None:
+            cu = [0, t]
+        else:
+            cu = [int(c) for c in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        sh = _Shape(1, t, h, d, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                    len(cu) - 1, block_size, top_k, _dtype_code(x))
+        return sh, arr
+    raise MobaError("expected [batch, seq, heads, head_dim] or [tokens, heads, head_dim]")
+
+
+def _dev(*ts: torch.Tensor):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise MobaError("tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise MobaError("tensors must be contiguous")
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _rows(x: torch.Tensor) -> Tuple[int, ...]:
+    return tuple(x.shape[:-1])
+
+
+def moba_total_blocks(x: torch.Tensor, block_size: int, cu_seqlens=None) -> int:
+    sh, keep = _make_shape(x, block_size, 1, cu_seqlens)
+    n = _load().moba_total_blocks(ctypes.byref(sh))
+    if n < 0:
+        raise MobaError("invalid shape")
+    return int(n)
+
+
+def moba_attn_fwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
+                                  cu_seqlens=None) -> int:
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    return int(_load().moba_attn_fwd_workspace_bytes(ctypes.byref(sh)))
+
+
+def moba_key_conv(k: torch.Tensor, w: torch.Tensor, block_size: int,
+                  mode: str = "plain", cu_seqlens=None, with_centroids: bool = False,
+                  out: Optional[torch.Tensor] = None, cent: Optional[torch.Tensor] = None,
+                  stream=None):
+    """k' = causal depthwise conv of k (w: fp32 [heads, head_dim, W]).
+
+    Returns k' (and the block centroids of k' when ``with_centroids``).
+    """
+    _dev(k, w)
+    sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
+    if w.dtype != torch.float32 or w.dim() != 3 or w.shape[0] != k.shape[-2] or w.shape[1] != k.shape[-1]:
+        raise MobaError("w must be fp32 [heads, head_dim, width]")
+    if out is None:
+        out = torch.empty_like(k)
+    if with_centroids and cent is None:
+        nb = moba_total_blocks(k, block_size, cu_seqlens)
+        cent = torch.empty((nb, k.shape[-2], k.shape[-1]), dtype=torch.float32, device=k.device)
+    rc = _load().moba_key_conv(ctypes.byref(sh), _p(k), _p(w), w.shape[2],
+                               _CONV_MODES[mode], _p(out),
+                               _p(cent if with_centroids else None), _stream(stream))
+    _check(rc, "moba_key_conv")
+    return (out, cent) if with_centroids else out
+
+
+def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Block means of k: fp32 [total_blocks, heads, head_dim]."""
+    _dev(k)
+    sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
+    if out is None:
+        nb = moba_total_blocks(k, block_size, cu_seqlens)
+        out = torch.empty((nb, k.shape[-2], k.shape[-1]), dtype=torch.float32, device=k.device)
+    _check(_load().moba_centroids(ctypes.byref(sh), _p(k), _p(out), _stream(stream)),
+           "moba_centroids")
+    return out
+
+
+def moba_route_topk(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k: int,
+                    cu_seqlens=None, out: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """Causal top-k block ids: int32 [..., heads, top_k], ascending, -1 padded."""
+    _dev(q, cent)
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    if out is None:
+        out = torch.empty(_rows(q) + (top_k,), dtype=torch.int32, device=q.device)
+    _check(_load().moba_route_topk(ctypes.byref(sh), _p(q), _p(cent), _p(out), _stream(stream)),
+           "moba_route_topk")
+    return out
+
+
+def _workspace(q, block_size, top_k, cu_seqlens, workspace):
+    need = moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    return workspace
+
+
+def moba_attn_index(idx, q, block_size, top_k, workspace, cu_seqlens=None, stream=None):
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _check(_load().moba_attn_index(ctypes.byref(sh), _p(idx), _p(workspace),
+                                   workspace.numel(), _stream(stream)), "moba_attn_index")
+
+
+def moba_attn_routed(q, k, v, block_size, top_k, workspace, scale=None, cu_seqlens=None,
+                     stream=None):
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _check(_load().moba_attn_routed(ctypes.byref(sh), _p(q), _p(k), _p(v),
+                                    float(scale or 0.0), _p(workspace), workspace.numel(),
+                                    _stream(stream)), "moba_attn_routed")
+
+
+def moba_attn_combine(q, k, v, idx, block_size, top_k, workspace, o, lse=None, scale=None,
+                      cu_seqlens=None, stream=None):
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _check(_load().moba_attn_combine(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
+                                     float(scale or 0.0), _p(o), _p(lse), _p(workspace),
+                                     workspace.numel(), _stream(stream)), "moba_attn_combine")
+
+
+def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                  block_size: int, top_k: int, scale: Optional[float] = None,
+                  cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
+                  return_lse: bool = True, out: Optional[torch.Tensor] = None,
+                  stream=None):
+    """Attention over the listed blocks + the causal own block.
+
+    Returns (o, lse) with lse fp32 [..., heads] (None if not requested).
+    """
+    _dev(q, k, v, idx)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise MobaError("q, k, v must share shape and dtype")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != _rows(q) + (top_k,):
+        raise MobaError("idx must be int32 [..., heads, top_k]")
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    if out is None:
+        out = torch.empty_like(q)
+    lse = torch.empty(_rows(q), dtype=torch.float32, device=q.device) if return_lse else None
+    workspace = _workspace(q, block_size, top_k, cu_seqlens, workspace)
+    rc = _load().moba_attn_fwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
+                               float(scale or 0.0), _p(out), _p(lse), _p(workspace),
+                               workspace.numel(), _stream(stream))
+    _check(rc, "moba_attn_fwd")
+    return out, lse
+
+
+def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, top_k: int,
+             conv_w: Optional[torch.Tensor] = None, conv_mode: str = "plain",
+             cu_seqlens=None, scale: Optional[float] = None,
+             workspace: Optional[torch.Tensor] = None):
+    """The whole MoBA forward: [key conv] -> centroids -> route -> attention.
+
+    Returns (o, lse, idx, k_used) where k_used is k' when a conv ran.
+    """
+    if conv_w is not None:
+        kk, cent = moba_key_conv(k, conv_w, block_size, conv_mode, cu_seqlens,
+                                 with_centroids=True)
+    else:
+        kk = k
+        cent = moba_centroids(k, block_size, cu_seqlens)
+    idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens)
+    o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
+    return o, lse, idx, kk

@@ -1,0 +1,60 @@
+"""Build the gfx950 MoBA library (``libmoba_amd.so``) in-tree with hipcc.
+
+Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
+parallel) and linked into ``block_sparse_long_key_amd/libmoba_amd.so``.
+Flags: gfx950 only, -O3, and packed-fp32 instructions disabled (hipcc's host
+pass warns that it does not know that feature; the warning is harmless).
+"""
+from __future__ import annotations
+
+import glob
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libmoba_amd.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objs = []
+    procs = []
+    for src in srcs:
+        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        objs.append(obj)
+        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT)))
+    failed = False
+    for src, p in procs:
+        out = p.communicate()[0].decode(errors="replace")
+        lines = [l for l in out.splitlines() if "packed-fp32-ops" not in l]
+        if p.returncode != 0:
+            failed = True
+            sys.stderr.write(f"hipcc failed on {src}:\n" + "\n".join(lines) + "\n")
+        elif verbose and lines:
+            print("\n".join(lines))
+    if failed:
+        raise RuntimeError("HIP compilation failed")
+    tmp = LIB + ".tmp"
+    subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                           *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

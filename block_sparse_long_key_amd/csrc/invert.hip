@@ -1,0 +1,189 @@
+// invert.hip -- query-major block selections -> key-block-major query lists.
+//
+// "Optimizing Mixture of Block Attention", summary page, section "Tre Kernel
+// Fusi": the top-k stage ends by turning the per-query block ids into a
+// varlen layout indexed by key block, which the gather-and-densify forward
+// consumes.  This is that step, written as a counting sort with no global
+// atomics:
+//   count   -- one workgroup per (sequence, head, chunk of 16 query blocks):
+//              LDS histogram of the routed past blocks; row of the count
+//              matrix cm[chunk][j] for the lists j this chunk can reach;
+//   scan    -- one workgroup per (sequence, head): list totals, list offsets,
+//              per-chunk positions (in place), and the work items (runs of
+//              <= 128 entries of one list) for the routed attention;
+//   scatter -- same grid as count: entries (token << 5 | slot) written at the
+//              chunk's positions with LDS cursors.
+// The own block is not listed (the own-block kernel handles it); -1 and
+// out-of-range ids are skipped.  Order inside a list is not deterministic,
+// which the routed attention does not depend on (each row of a tile is
+// computed independently).
+#include "moba_internal.h"
+
+namespace moba {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScanThreads = 1024;
+
+__device__ __forceinline__ int32_t* cm_base(const SegTable& st, int32_t* cmat, int s, int h)
+{
+    return cmat + st.cmbase[s] + (int64_t)h * seq_nchunk(st, s) * seq_nblk(st, s);
+}
+
+__global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const int32_t* __restrict__ idx,
+                                                            int32_t* __restrict__ cmat)
+{
+    extern __shared__ int32_t hist[];
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int s = seq_of_chunk(st, c);
+    const int cl = c - st.cbase[s];
+    const int n = seq_nblk(st, s), L = seq_len(st, s), t0 = st.cu[s];
+    const int B = st.B, K = st.K, H = st.H;
+    const int ib0 = cl * kInvChunkBlocks, ib1 = min(n, ib0 + kInvChunkBlocks);
+    const int nl = ib1;                       // lists reachable: j < ib1
+    for (int j = threadIdx.x; j < nl; j += kThreads) hist[j] = 0;
+    __syncthreads();
+    const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
+    const int nent = (tl1 - tl0) * K;
+    const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
+    for (int e = threadIdx.x; e < nent; e += kThreads) {
+        const int r = e / K, slot = e - r * K;
+        const int j = src[(size_t)r * H * K + slot];
+        const int i = (tl0 + r) / B;
+        if (j >= 0 && j < i) atomicAdd(&hist[j], 1);
+    }
+    __syncthreads();
+    int32_t* dst = cm_base(st, cmat, s, h) + (int64_t)cl * n;
+    for (int j = threadIdx.x; j < nl; j += kThreads) dst[j] = hist[j];
+}
+
+__global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int32_t* __restrict__ cmat,
+                                                               Item* __restrict__ items)
+{
+    extern __shared__ int32_t lds[];
+    const int s = blockIdx.x, h = blockIdx.y;
+    const int n = seq_nblk(st, s), nch = seq_nchunk(st, s);
+    int32_t* tot = lds;               // [n] list totals -> entry offsets
+    int32_t* ioff = lds + n;          // [n] item offsets
+    __shared__ int32_t part_e[kScanThreads], part_i[kScanThreads];
+    int32_t* cm = cm_base(st, cmat, s, h);
+    const int64_t ib = st.ibase[s] + (int64_t)h * seq_item_cap(st, s);
+    const int64_t cap = seq_item_cap(st, s);
+
+    // list totals (chunk c reaches list j iff j < (c+1)*16)
+    for (int j = threadIdx.x; j < n; j += kScanThreads) {
+        int t = 0;
+        for (int c = j / kInvChunkBlocks; c < nch; ++c) t += cm[(int64_t)c * n + j];
+        tot[j] = t;
+    }
+    __syncthreads();
+    // block scan over contiguous ranges
+    const int per = (n + kScanThreads - 1) / kScanThreads;
+    const int j0 = threadIdx.x * per, j1 = min(n, j0 + per);
+    int se = 0, si = 0;
+    for (int j = j0; j < j1; ++j) { se += tot[j]; si += (tot[j] + kItemRows - 1) / kItemRows; }
+    part_e[threadIdx.x] = se;
+    part_i[threadIdx.x] = si;
+    __syncthreads();
+    for (int off = 1; off < kScanThreads; off <<= 1) {
+        int ve = threadIdx.x >= off ? part_e[threadIdx.x - off] : 0;
+        int vi = threadIdx.x >= off ? part_i[threadIdx.x - off] : 0;
+        __syncthreads();
+        part_e[threadIdx.x] += ve;
+        part_i[threadIdx.x] += vi;
+        __syncthreads();
+    }
+    int be = part_e[threadIdx.x] - se, bi = part_i[threadIdx.x] - si;   // exclusive
+    const int n_items = part_i[kScanThreads - 1];
+    for (int j = j0; j < j1; ++j) {
+        const int t = tot[j];
+        tot[j] = be;
+        ioff[j] = bi;
+        be += t;
+        bi += (t + kItemRows - 1) / kItemRows;
+        // keep the list total in the scan result: ioff/tot of j+1 give it
+    }
+    __syncthreads();
+    // per-chunk positions (in place) and items, coalesced over j
+    const int g0 = st.boff[s];
+    for (int j = threadIdx.x; j < n; j += kScanThreads) {
+        const int beg = tot[j];
+        int run = beg;
+        for (int c = j / kInvChunkBlocks; c < nch; ++c) {
+            const int v = cm[(int64_t)c * n + j];
+            cm[(int64_t)c * n + j] = run;
+            run += v;
+        }
+        const int total = run - beg;
+        const int nit = (total + kItemRows - 1) / kItemRows;
+        for (int r = 0; r < nit; ++r) {
+            Item it;
+            it.begin = beg + r * kItemRows;
+            it.count = min(kItemRows, total - r * kItemRows);
+            it.g = g0 + j;
+            it.h = h;
+            items[ib + ioff[j] + r] = it;
+        }
+    }
+    // unused capacity: empty items
+    for (int64_t r = n_items + threadIdx.x; r < cap; r += kScanThreads) {
+        Item it;
+        it.begin = 0; it.count = 0; it.g = 0; it.h = h;
+        items[ib + r] = it;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ cmat,
+                                                              uint32_t* __restrict__ entries)
+{
+    extern __shared__ int32_t cur[];
+    const int c = blockIdx.x, h = blockIdx.y;
+    const int s = seq_of_chunk(st, c);
+    const int cl = c - st.cbase[s];
+    const int n = seq_nblk(st, s), L = seq_len(st, s), t0 = st.cu[s];
+    const int B = st.B, K = st.K, H = st.H;
+    const int ib0 = cl * kInvChunkBlocks, ib1 = min(n, ib0 + kInvChunkBlocks);
+    const int32_t* pos = cm_base(st, const_cast<int32_t*>(cmat), s, h) + (int64_t)cl * n;
+    for (int j = threadIdx.x; j < ib1; j += kThreads) cur[j] = pos[j];
+    __syncthreads();
+    uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K;
+    const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
+    const int nent = (tl1 - tl0) * K;
+    const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
+    for (int e = threadIdx.x; e < nent; e += kThreads) {
+        const int r = e / K, slot = e - r * K;
+        const int j = src[(size_t)r * H * K + slot];
+        const int i = (tl0 + r) / B;
+        if (j >= 0 && j < i) {
+            const int p = atomicAdd(&cur[j], 1);
+            ent[p] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx)
+{
+    const SegTable& st = L.st;
+    if (st.K <= 1 || st.total_chunks == 0) return hipSuccess;
+    int32_t* cmat = (int32_t*)(wsp + ws.cmat_off);
+    Item* items = (Item*)(wsp + ws.items_off);
+    uint32_t* ent = (uint32_t*)(wsp + ws.ent_off);
+    int maxn = 0;
+    for (int s = 0; s < st.nseq; ++s) maxn = maxn > seq_nblk(st, s) ? maxn : seq_nblk(st, s);
+    dim3 gc(st.total_chunks, st.H);
+    hipLaunchKernelGGL(inv_count_kernel, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx, cmat);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(inv_scan_kernel, dim3(st.nseq, st.H), dim3(kScanThreads), (size_t)maxn * 8,
+                       L.stream, st, cmat, items);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(inv_scatter_kernel, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx,
+                       cmat, ent);
+    return hipGetLastError();
+}
+
+}  // namespace moba

@@ -1,0 +1,262 @@
+// moba_api.hip -- the C ABI of include/moba.h: argument validation,
+// sequence/block tables, workspace carving and kernel launches.  No
+// allocation, no synchronisation, no printing.
+#include <math.h>
+#include <string.h>
+
+#include "moba_internal.h"
+
+using namespace moba;
+
+namespace {
+
+constexpr int64_t kMaxRows = (int64_t)1 << 27;   // tokens * heads (entry encoding)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Validate the shape and fill the launch description.
+moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
+{
+    if (!sh) return MOBA_ERR_INVALID_ARG;
+    if (sh->heads < 1 || sh->seq < 0 || sh->batch < 1) return MOBA_ERR_INVALID_ARG;
+    if (sh->dtype != MOBA_F32 && sh->dtype != MOBA_BF16) return MOBA_ERR_INVALID_ARG;
+    if (sh->head_dim != 64 && sh->head_dim != 128) return MOBA_ERR_UNSUPPORTED;
+    if (sh->block_size != 64 && sh->block_size != 128) return MOBA_ERR_UNSUPPORTED;
+    if (sh->top_k < 1) return MOBA_ERR_INVALID_ARG;
+    if (sh->top_k > 32) return MOBA_ERR_UNSUPPORTED;
+    // fp32 keeps a whole key block of K and V in LDS: B * d <= 8192
+    if (sh->dtype == MOBA_F32 && sh->head_dim * sh->block_size > 8192) return MOBA_ERR_UNSUPPORTED;
+
+    memset(L, 0, sizeof(*L));
+    SegTable& st = L->st;
+    st.H = sh->heads;
+    st.B = sh->block_size;
+    st.K = sh->top_k;
+    int64_t tokens;
+    if (sh->cu_seqlens) {
+        if (sh->batch != 1) return MOBA_ERR_INVALID_ARG;
+        if (sh->num_seqs < 1) return MOBA_ERR_INVALID_ARG;
+        if (sh->num_seqs > kMaxSeqs) return MOBA_ERR_UNSUPPORTED;
+        const int32_t* cu = sh->cu_seqlens;
+        if (cu[0] != 0 || cu[sh->num_seqs] != sh->seq) return MOBA_ERR_INVALID_ARG;
+        for (int s = 0; s < sh->num_seqs; ++s)
+            if (cu[s + 1] < cu[s]) return MOBA_ERR_INVALID_ARG;
+        st.nseq = sh->num_seqs;
+        for (int s = 0; s <= st.nseq; ++s) st.cu[s] = cu[s];
+        tokens = sh->seq;
+    } else {
+        if (sh->batch > kMaxSeqs) return MOBA_ERR_UNSUPPORTED;
+        st.nseq = sh->batch;
+        tokens = (int64_t)sh->batch * sh->seq;
+        if (tokens * sh->heads >= kMaxRows) return MOBA_ERR_UNSUPPORTED;
+        for (int s = 0; s <= st.nseq; ++s) st.cu[s] = s * sh->seq;
+    }
+    if (tokens * sh->heads >= kMaxRows) return MOBA_ERR_UNSUPPORTED;
+
+    const int K1 = st.K - 1;
+    st.boff[0] = 0;
+    st.cbase[0] = 0;
+    st.cmbase[0] = 0;
+    st.ebase[0] = 0;
+    st.ibase[0] = 0;
+    for (int s = 0; s < st.nseq; ++s) {
+        const int Ls = st.cu[s + 1] - st.cu[s];
+        const int n = ceil_div(Ls, st.B);
+        if (n > kMaxBlocksPerSeq) return MOBA_ERR_UNSUPPORTED;
+        const int nch = ceil_div(n, kInvChunkBlocks);
+        st.boff[s + 1] = st.boff[s] + n;
+        st.cbase[s + 1] = st.cbase[s] + nch;
+        st.cmbase[s + 1] = st.cmbase[s] + (int64_t)st.H * nch * n;
+        // lists are sized for K entries per row so that any idx row (even one
+        // that omits its own block) stays in bounds
+        st.ebase[s + 1] = st.ebase[s] + (int64_t)st.H * Ls * st.K;
+        const int64_t cap = (int64_t)Ls * st.K / kItemRows + n;
+        st.ibase[s + 1] = st.ibase[s] + (int64_t)st.H * cap;
+    }
+    st.total_blocks = st.boff[st.nseq];
+    st.total_chunks = st.cbase[st.nseq];
+    st.total_items = K1 > 0 ? st.ibase[st.nseq] : 0;
+    L->D = sh->head_dim;
+    L->dtype = sh->dtype;
+    L->tokens = (int)tokens;
+    L->stream = stream;
+    return MOBA_OK;
+}
+
+WsLayout layout(const Launch& L)
+{
+    WsLayout w;
+    memset(&w, 0, sizeof(w));
+    const SegTable& st = L.st;
+    const size_t esz = L.dtype == MOBA_BF16 ? 2 : 4;
+    const size_t rows = (size_t)L.tokens * st.H;
+    if (st.K > 1) {
+        w.cmat_bytes = (size_t)st.cmbase[st.nseq] * 4;
+        w.items_bytes = (size_t)st.total_items * sizeof(Item);
+        w.ent_bytes = (size_t)st.ebase[st.nseq] * 4;
+        w.po_bytes = rows * st.K * L.D * esz;
+        w.pl_bytes = rows * st.K * 4;
+    }
+    size_t off = 0;
+    w.cmat_off = off;  off += align256(w.cmat_bytes);
+    w.items_off = off; off += align256(w.items_bytes);
+    w.ent_off = off;   off += align256(w.ent_bytes);
+    w.po_off = off;    off += align256(w.po_bytes);
+    w.pl_off = off;    off += align256(w.pl_bytes);
+    w.total = off;
+    return w;
+}
+
+moba_status hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
+
+bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out)
+{
+    *out = layout(L);
+    if (out->total > 0) {
+        if (!ws || ((uintptr_t)ws & 255u) != 0) return MOBA_ERR_INVALID_ARG;
+        if (bytes < out->total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    return MOBA_OK;
+}
+
+float resolve_scale(float scale, int D)
+{
+    return scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char* moba_status_string(moba_status s)
+{
+    switch (s) {
+        case MOBA_OK: return "ok";
+        case MOBA_ERR_INVALID_ARG: return "invalid argument";
+        case MOBA_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+        case MOBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOBA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+int64_t moba_total_blocks(const moba_shape* shape)
+{
+    Launch L;
+    if (make_launch(shape, &L, nullptr) != MOBA_OK) return -1;
+    return L.st.total_blocks;
+}
+
+size_t moba_attn_fwd_workspace_bytes(const moba_shape* shape)
+{
+    Launch L;
+    if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
+    return layout(L).total;
+}
+
+moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w, int32_t width,
+                          int32_t mode, void* k_out, float* cent, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (mode != MOBA_CONV_PLAIN && mode != MOBA_CONV_SILU_RESIDUAL) return MOBA_ERR_INVALID_ARG;
+    if (width < 1) return MOBA_ERR_INVALID_ARG;
+    if (width > 8) return MOBA_ERR_UNSUPPORTED;
+    if (!ptr_ok(k) || !ptr_ok(w) || !ptr_ok(k_out)) return MOBA_ERR_INVALID_ARG;
+    if (cent && !aligned16(cent)) return MOBA_ERR_INVALID_ARG;
+    if (k == k_out) return MOBA_ERR_INVALID_ARG;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_conv_pool(L, k, w, width, mode, k_out, cent));
+}
+
+moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(k) || !ptr_ok(cent)) return MOBA_ERR_INVALID_ARG;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_conv_pool(L, k, nullptr, 0, 0, nullptr, cent));
+}
+
+moba_status moba_route_topk(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
+                            hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(q) || !ptr_ok(cent) || !ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_route(L, q, cent, idx));
+}
+
+moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    WsLayout ws;
+    st = check_ws(L, workspace, workspace_bytes, &ws);
+    if (st != MOBA_OK) return st;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_inv(L, ws, (char*)workspace, idx));
+}
+
+moba_status moba_attn_routed(const moba_shape* shape, const void* q, const void* k, const void* v,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v)) return MOBA_ERR_INVALID_ARG;
+    WsLayout ws;
+    st = check_ws(L, workspace, workspace_bytes, &ws);
+    if (st != MOBA_OK) return st;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_routed_attn(L, ws, (char*)workspace, q, k, v,
+                                         resolve_scale(softmax_scale, L.D)));
+}
+
+moba_status moba_attn_combine(const moba_shape* shape, const void* q, const void* k, const void* v,
+                              const int32_t* idx, float softmax_scale, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o))
+        return MOBA_ERR_INVALID_ARG;
+    if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
+    WsLayout ws;
+    st = check_ws(L, workspace, workspace_bytes, &ws);
+    if (st != MOBA_OK) return st;
+    if (L.tokens == 0) return MOBA_OK;
+    return hip_status(launch_diag_combine(L, ws, (char*)workspace, q, k, v, idx,
+                                          resolve_scale(softmax_scale, L.D), o, lse));
+}
+
+moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+                          const int32_t* idx, float softmax_scale, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    moba_status st = moba_attn_index(shape, idx, workspace, workspace_bytes, stream);
+    if (st != MOBA_OK) return st;
+    st = moba_attn_routed(shape, q, k, v, softmax_scale, workspace, workspace_bytes, stream);
+    if (st != MOBA_OK) return st;
+    return moba_attn_combine(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
+                             workspace_bytes, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,140 @@
+// moba_internal.h -- shared definitions of the gfx950 MoBA forward kernels.
+//
+// Sequences, blocks and heads are addressed through a SegTable that the host
+// fills from the shape and passes to every kernel by value (no device
+// allocation, no host<->device copy).  Token rows are [tokens][heads][d].
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moba.h"
+
+namespace moba {
+
+constexpr int kMaxSeqs = MOBA_MAX_SEQS;
+// queries per routed-attention work item (4 waves x 32 gathered queries)
+constexpr int kItemRows = 128;
+// query blocks per inversion chunk (one workgroup of the count/scatter passes)
+constexpr int kInvChunkBlocks = 16;
+// largest number of blocks of one sequence (LDS histogram of the inversion)
+constexpr int kMaxBlocksPerSeq = 16384;
+
+struct SegTable {
+    int32_t nseq;       // number of independent sequences
+    int32_t H;          // heads
+    int32_t B;          // block size
+    int32_t K;          // top_k (own block included)
+    int32_t total_blocks;
+    int32_t total_chunks;   // inversion chunks over all sequences (per head)
+    int64_t total_items;    // routed-attention item capacity over all (seq, head)
+    int32_t cu[kMaxSeqs + 1];     // token start of sequence s
+    int32_t boff[kMaxSeqs + 1];   // first global block of sequence s
+    int32_t cbase[kMaxSeqs + 1];  // first inversion chunk of sequence s
+    int64_t cmbase[kMaxSeqs + 1]; // count-matrix base of (s, h=0); + h * nch * nblk
+    int64_t ebase[kMaxSeqs + 1];  // entries base of (s, h=0); + h * L * K
+    int64_t ibase[kMaxSeqs + 1];  // item base of (s, h=0); + h * cap(s)
+};
+
+__host__ __device__ inline int seq_len(const SegTable& st, int s) { return st.cu[s + 1] - st.cu[s]; }
+__host__ __device__ inline int seq_nblk(const SegTable& st, int s) { return st.boff[s + 1] - st.boff[s]; }
+__host__ __device__ inline int seq_nchunk(const SegTable& st, int s) { return st.cbase[s + 1] - st.cbase[s]; }
+__host__ __device__ inline int64_t seq_item_cap(const SegTable& st, int s) {
+    // a row lists at most K blocks (K-1 when it holds its own block, as it should)
+    return (int64_t)seq_len(st, s) * st.K / kItemRows + seq_nblk(st, s);
+}
+
+// sequence holding global block g (boff is non-decreasing; empty sequences
+// have boff[s] == boff[s+1] and are skipped)
+__device__ inline int seq_of_block(const SegTable& st, int g) {
+    int lo = 0, hi = st.nseq - 1;
+    while (lo < hi) {               // last s with boff[s] <= g and nonempty
+        int mid = (lo + hi + 1) >> 1;
+        if (st.boff[mid] <= g) lo = mid; else hi = mid - 1;
+    }
+    while (lo > 0 && st.boff[lo] > g) --lo;
+    return lo;
+}
+__device__ inline int seq_of_chunk(const SegTable& st, int c) {
+    int lo = 0, hi = st.nseq - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (st.cbase[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ bf16 ------
+// bf16 is carried as its 16-bit pattern.  Rounding is IEEE round to nearest,
+// ties to even.
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(((uint32_t)b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u) {
+        if (u & 0x007fffffu) u |= 0x00400000u;
+        return (uint16_t)(u >> 16);
+    }
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct IO;
+template <> struct IO<float> {
+    static __device__ __forceinline__ float load(const float* p) { return *p; }
+    static __device__ __forceinline__ float round(float x) { return x; }
+    static __device__ __forceinline__ void store(float* p, float x) { *p = x; }
+};
+template <> struct IO<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p) { return bf16_to_f32(*p); }
+    static __device__ __forceinline__ float round(float x) { return bf16_to_f32(f32_to_bf16(x)); }
+    static __device__ __forceinline__ void store(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+};
+
+// ------------------------------------------------------------ MFMA ------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8_t __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// routed-attention work item: a run of <= kItemRows entries of one list
+struct Item {
+    int32_t begin;   // first entry, relative to the (seq, head) entries base
+    int32_t count;   // 0 = empty slot
+    int32_t g;       // global key block
+    int32_t h;       // head
+};
+
+// ----------------------------------------------------- workspace layout --
+struct WsLayout {
+    size_t cmat_off, cmat_bytes;     // int32 count / position matrix
+    size_t items_off, items_bytes;   // Item[total_items]
+    size_t ent_off, ent_bytes;       // uint32 entries (t << 5 | slot)
+    size_t po_off, po_bytes;         // partial o [tokens][H][K][D] (I/O dtype)
+    size_t pl_off, pl_bytes;         // partial lse [tokens][H][K] fp32 (log2 units)
+    size_t total;
+};
+
+// ----------------------------------------------------------- launchers --
+struct Launch {
+    SegTable st;
+    int D;
+    int dtype;          // moba_dtype
+    int tokens;         // total tokens over all sequences
+    hipStream_t stream;
+};
+
+hipError_t launch_conv_pool(const Launch& L, const void* k, const float* w, int W,
+                            int mode, void* k_out, float* cent);
+hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx);
+hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx);
+hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
+                              const void* q, const void* k, const void* v, float scale);
+hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp,
+                               const void* q, const void* k, const void* v,
+                               const int32_t* idx, float scale, void* o, float* lse);
+
+}  // namespace moba

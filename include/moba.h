@@ -1,0 +1,183 @@
+/*
+ * moba.h -- C ABI of the MI355X (gfx950) Mixture of Block Attention forward.
+ *
+ * The method is the one of "Optimizing Mixture of Block Attention" (Xiao,
+ * Guo, Mazaheri, Han), as summarised on its summary pages:
+ *   - task definition ("Definizione del Compito"): N keys split into
+ *     n = N/B blocks; each query attends, with O = softmax(QK^T/sqrt(d))V,
+ *     to its top-k blocks only;
+ *   - router score ("Architettura del Modello Statistico", router-score
+ *     equation): s_j = q . kbar_j with kbar_j the mean key of block j;
+ *   - key convolution ("Appendice B", formal-form equation): a depthwise,
+ *     causal, left-padded conv over the sequence, one filter per channel.
+ * Causal rules (not spelled out on the pages, plainest decoder reading): the
+ * query's own block is always kept and attended token-causally (u <= t), and
+ * does not compete for the other k-1 places; future blocks are never
+ * selected; equal scores go to the lower block index.  k counts the own
+ * block (k = 8 of n = 64 blocks is the pages' "7/8 sparsity").
+ *
+ * Conventions shared by every call
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates, frees or synchronises; every call only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = default stream)
+ *     and returns.  Inputs are never modified; outputs are fully written.
+ *   - q, k, v, k_out, o: [batch][seq][heads][head_dim], contiguous,
+ *     head_dim fastest, dtype `shape->dtype`.  Varlen: batch == 1, seq ==
+ *     total tokens, and `cu_seqlens` (HOST array of num_seqs+1 int32,
+ *     cu[0] = 0, non-decreasing, cu[num_seqs] = seq) splits the token axis
+ *     into independent sequences.  A uniform batch is the same as num_seqs =
+ *     batch sequences of length seq.
+ *   - Blocks restart at every sequence start; block j of a sequence holds
+ *     its tokens [jB, min((j+1)B, L)).  Block ids in `idx` are local to the
+ *     sequence.  "total blocks" = sum over sequences of ceil(L/B); centroid
+ *     rows are ordered sequence-major, then block.
+ *   - Errors: arguments are validated on the host before any launch:
+ *     MOBA_ERR_INVALID_ARG (null pointer, misaligned pointer -- 16 bytes
+ *     required --, inconsistent shape), MOBA_ERR_UNSUPPORTED (outside the
+ *     support matrix below), MOBA_ERR_WORKSPACE_TOO_SMALL.  A failed launch
+ *     returns MOBA_ERR_HIP.  Device faults surface at the caller's next sync.
+ *     Nothing is printed, nothing throws.
+ *   - Calls are stateless and may be issued from several host threads.
+ *
+ * Support matrix: head_dim 64 or 128; block_size 64 or 128; top_k 1..32;
+ * conv width 1..8; dtype bf16 (fast path) or fp32 (correctness path);
+ * num_seqs <= MOBA_MAX_SEQS (varlen); tokens * heads < 2^27 per call.
+ */
+#ifndef MOBA_H_
+#define MOBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOBA_ABI_VERSION 1
+#define MOBA_MAX_SEQS 64
+
+typedef enum {
+    MOBA_OK = 0,
+    MOBA_ERR_INVALID_ARG = 1,
+    MOBA_ERR_UNSUPPORTED = 2,
+    MOBA_ERR_WORKSPACE_TOO_SMALL = 3,
+    MOBA_ERR_HIP = 4
+} moba_status;
+
+typedef enum { MOBA_F32 = 0, MOBA_BF16 = 1 } moba_dtype;
+
+typedef enum {
+    MOBA_CONV_PLAIN = 0,          /* k'_t = sum_l w_l * k_{t-l}                 */
+    MOBA_CONV_SILU_RESIDUAL = 1   /* k'_t = k_t + SiLU(sum_l w_l * k_{t-l})     */
+} moba_conv_mode;
+
+typedef struct {
+    int32_t batch;                /* uniform batches; 1 when cu_seqlens is set    */
+    int32_t seq;                  /* tokens per batch row (varlen: total tokens)  */
+    int32_t heads;
+    int32_t head_dim;
+    const int32_t *cu_seqlens;    /* HOST pointer or NULL; read during the call   */
+    int32_t num_seqs;             /* entries of cu_seqlens minus one (varlen)     */
+    int32_t block_size;           /* B                                            */
+    int32_t top_k;                /* k, counting the query's own block            */
+    int32_t dtype;                /* moba_dtype of q, k, v, k', o                 */
+} moba_shape;
+
+/*
+ * moba_key_conv -- key convolution (Appendice B, formal form).
+ *   w: fp32 [heads][head_dim][width]; w[h][c][l] multiplies k_{t-l} of
+ *      channel (h, c) (l = 0 is the current token).  Zero before each
+ *      sequence start.
+ *   The tap sum is fp32 fmaf from the oldest tap to the newest, started at
+ *   +0; MOBA_CONV_SILU_RESIDUAL then adds k_t + conv/(1+exp(-conv)) in fp32.
+ *   k_out (same layout and dtype as k) is rounded to the dtype (bf16:
+ *   round-to-nearest-even).  k_out must not alias k.
+ *   If `cent` is not NULL, the block centroids of k_out are also written to
+ *   it (same contract as moba_centroids), in the same pass.
+ */
+moba_status moba_key_conv(const moba_shape *shape, const void *k,
+                          const float *w, int32_t width, int32_t mode,
+                          void *k_out, float *cent, hipStream_t stream);
+
+/*
+ * moba_centroids -- block means kbar_j (router-score equation).
+ *   cent: fp32 [total_blocks][heads][head_dim].  Each mean is the exact
+ *   fp64 sum of the block's keys, divided by the block's key count and
+ *   rounded once to fp32; a final partial block is averaged over the keys
+ *   it holds.
+ */
+moba_status moba_centroids(const moba_shape *shape, const void *k,
+                           float *cent, hipStream_t stream);
+
+/*
+ * moba_route_topk -- router scores and causal top-k selection.
+ *   For query t in block i of its sequence: scores s_j = q_t . cent_j for the
+ *   past blocks j < i; keep the first min(k-1, i) in the order (score
+ *   descending, block id ascending), add the own block i.
+ *   idx: int32 [batch][seq][heads][top_k]; each row ascending, own block
+ *   included, padded with -1 at the end.
+ *   The selection is exact with respect to scores computed in fp64: the
+ *   kernel scores in fp32 with a rigorous error bound and re-scores in fp64
+ *   any query whose k-1-th and k-th scores are closer than that bound.
+ */
+moba_status moba_route_topk(const moba_shape *shape, const void *q,
+                            const float *cent, int32_t *idx,
+                            hipStream_t stream);
+
+/*
+ * moba_attn_fwd -- attention over the selected blocks (task definition).
+ *   For query t in block i: keys = all keys of each listed past block
+ *   (0 <= idx < i) plus the keys u <= t of block i.  -1 entries are padding;
+ *   listed entries >= i are ignored (the own block is always attended).
+ *   Listed past blocks must be distinct.
+ *   z_u = scale * q_t . k_u; O_t = softmax(z) V; LSE_t = max z + ln sum
+ *   exp(z - max z) (natural log).
+ *   softmax_scale <= 0 selects 1/sqrt(head_dim).
+ *   o: same layout/dtype as q.  lse: NULL or fp32 [batch][seq][heads].
+ *   workspace: device memory of at least moba_attn_fwd_workspace_bytes(),
+ *   256-byte aligned; its contents on entry are ignored and on exit are
+ *   scratch.  Calls that share a workspace must be stream-ordered.
+ *   Internally: build, for every (sequence, head, block j), the list of
+ *   (query, slot) pairs that routed to j; attend each list's gathered
+ *   queries against block j densely (bf16 MFMA, fp32 softmax), keeping one
+ *   (o, lse) partial per pair; then the own block causally and the merge of
+ *   the partials per query.
+ */
+moba_status moba_attn_fwd(const moba_shape *shape, const void *q,
+                          const void *k, const void *v, const int32_t *idx,
+                          float softmax_scale, void *o, float *lse,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* The three stages of moba_attn_fwd, in order, for stage timing: the
+ * index inversion, the routed (past-block) attention, and the own-block
+ * attention plus merge.  Running them in order on one stream with one
+ * workspace is exactly moba_attn_fwd.  Same arguments and errors. */
+moba_status moba_attn_index(const moba_shape *shape, const int32_t *idx,
+                            void *workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+moba_status moba_attn_routed(const moba_shape *shape, const void *q,
+                             const void *k, const void *v, float softmax_scale,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+moba_status moba_attn_combine(const moba_shape *shape, const void *q,
+                              const void *k, const void *v,
+                              const int32_t *idx, float softmax_scale,
+                              void *o, float *lse, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace moba_attn_fwd needs for `shape` (0 on invalid shape). */
+size_t moba_attn_fwd_workspace_bytes(const moba_shape *shape);
+
+/* Total number of blocks (centroid rows) of `shape`; -1 on invalid shape. */
+int64_t moba_total_blocks(const moba_shape *shape);
+
+const char *moba_status_string(moba_status status);
+int32_t moba_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H_ */

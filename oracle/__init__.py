@@ -54,6 +54,10 @@ def _load():
         lib.moba_oracle_route.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _P, _P, _I]
         lib.moba_oracle_attend.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _P, _I]
         lib.moba_oracle_total_blocks.argtypes = [_P, _I, _I]
+        lib.moba_oracle_route_rows.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P]
+        lib.moba_oracle_attend_rows.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _I, _P, _P]
+        lib.moba_oracle_route_rows.restype = _I
+        lib.moba_oracle_attend_rows.restype = _I
         for f in (lib.moba_oracle_key_conv, lib.moba_oracle_centroids,
                   lib.moba_oracle_route, lib.moba_oracle_attend,
                   lib.moba_oracle_total_blocks):
@@ -176,3 +180,43 @@ def forward(q, k, v, B: int, K: int, cu, conv_w=None, conv_mode: int = 0,
     o, lse = attend(q, kk, v, idx, B, K, cu, scale, nthreads)
     return {"k_conv": kk, "cent": cent, "idx": idx, "gap_a": ga, "gap_b": gb,
             "exempt": ex, "o": o, "lse": lse}
+
+
+def route_rows(q, cent, B: int, K: int, cu, rows):
+    """Routing for the listed rows only (row = token * H + head).
+
+    Returns (idx [nrows, K], gap_a, gap_b, exempt) for those rows.
+    """
+    q = _f32(q)
+    cent = np.ascontiguousarray(cent, dtype=np.float32)
+    T, H, d = q.shape
+    c = _cu(cu)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    idx = np.full((T * H, K), -7, dtype=np.int32)
+    ga = np.zeros(T * H)
+    gb = np.zeros(T * H)
+    ex = np.zeros(T * H, dtype=np.uint8)
+    rc = _load().moba_oracle_route_rows(_ptr(q), _ptr(cent), H, d, B, K, _ptr(c),
+                                        len(c) - 1, _ptr(rows), len(rows), _ptr(idx),
+                                        _ptr(ga), _ptr(gb), _ptr(ex))
+    assert rc == 0
+    return idx[rows], ga[rows], gb[rows], ex[rows].astype(bool)
+
+
+def attend_rows(q, k, v, idx, B: int, K: int, cu, rows, scale: float = 0.0):
+    """Attention for the listed rows only; idx is the full [T, H, K] array.
+
+    Returns (o [nrows, d], lse [nrows]).
+    """
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    T, H, d = q.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, H, K)
+    c = _cu(cu)
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    o = np.zeros((T * H, d), dtype=np.float64)
+    lse = np.zeros(T * H, dtype=np.float64)
+    rc = _load().moba_oracle_attend_rows(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), H, d, B, K,
+                                         _ptr(c), len(c) - 1, float(scale), _ptr(rows),
+                                         len(rows), _ptr(o), _ptr(lse))
+    assert rc == 0
+    return o[rows], lse[rows]

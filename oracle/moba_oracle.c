@@ -260,58 +260,64 @@ static int cmp_int(const void *a, const void *b)
     return (x > y) - (x < y);
 }
 
+/* one query: token t_local `tl` of sequence s, head h; sc/order scratch of
+ * n doubles/ints, row scratch of K ints */
+static void route_one(route_ctx *c, int s, int h, int tl, double *sc, int *order, int *row)
+{
+    int t0 = c->cu[s];
+    size_t t = (size_t)(t0 + tl);
+    int i = tl / c->B;
+    const float *qv = c->q + (t * c->H + h) * c->d;
+    /* scores of the past blocks */
+    for (int j = 0; j < i; ++j) {
+        const float *cv = c->cent + ((size_t)(c->boff[s] + j) * c->H + h) * c->d;
+        double acc = 0.0;
+        for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)cv[ch];
+        sc[j] = acc;
+    }
+    /* selection sort of the first m+1 places in the total order */
+    int m = (c->K - 1) < i ? (c->K - 1) : i;
+    int need = (m + 1) < i ? (m + 1) : i;
+    for (int j = 0; j < i; ++j) order[j] = j;
+    for (int p = 0; p < need; ++p) {
+        int best = p;
+        for (int r = p + 1; r < i; ++r)
+            if (ranks_before(sc[order[r]], order[r], sc[order[best]], order[best])) best = r;
+        int tmp = order[p]; order[p] = order[best]; order[best] = tmp;
+    }
+    for (int p = 0; p < m; ++p) row[p] = order[p];
+    row[m] = i;
+    qsort(row, (size_t)(m + 1), sizeof(int), cmp_int);
+    for (int p = m + 1; p < c->K; ++p) row[p] = -1;
+    int *dst = c->idx + (t * c->H + h) * c->K;
+    for (int p = 0; p < c->K; ++p) dst[p] = row[p];
+    size_t r = t * c->H + h;
+    if (c->gap_a) {
+        if (i >= c->K && c->K >= 2) {
+            double a = sc[order[c->K - 2]], b = sc[order[c->K - 1]];
+            double mx = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
+            if (mx < 1e-30) mx = 1e-30;
+            c->gap_a[r] = a;
+            c->gap_b[r] = b;
+            c->exempt[r] = (fabs(a - b) <= 1e-5 * mx) ? 1 : 0;
+        } else {
+            c->gap_a[r] = NAN;
+            c->gap_b[r] = NAN;
+            c->exempt[r] = 0;
+        }
+    }
+}
+
 static void route_job(void *vctx, int job)
 {
     route_ctx *c = (route_ctx *)vctx;
     int s = job / c->H, h = job % c->H;
-    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    int L = c->cu[s + 1] - c->cu[s];
     int n = ceil_div(L, c->B);
     double *sc = (double *)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
     int *order = (int *)malloc(sizeof(int) * (size_t)(n > 0 ? n : 1));
     int *row = (int *)malloc(sizeof(int) * (size_t)c->K);
-    for (int tl = 0; tl < L; ++tl) {
-        size_t t = (size_t)(t0 + tl);
-        int i = tl / c->B;
-        const float *qv = c->q + (t * c->H + h) * c->d;
-        /* scores of the past blocks */
-        for (int j = 0; j < i; ++j) {
-            const float *cv = c->cent + ((size_t)(c->boff[s] + j) * c->H + h) * c->d;
-            double acc = 0.0;
-            for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)cv[ch];
-            sc[j] = acc;
-        }
-        /* selection sort of the first m+1 places in the total order */
-        int m = (c->K - 1) < i ? (c->K - 1) : i;
-        int need = (m + 1) < i ? (m + 1) : i;
-        for (int j = 0; j < i; ++j) order[j] = j;
-        for (int p = 0; p < need; ++p) {
-            int best = p;
-            for (int r = p + 1; r < i; ++r)
-                if (ranks_before(sc[order[r]], order[r], sc[order[best]], order[best])) best = r;
-            int tmp = order[p]; order[p] = order[best]; order[best] = tmp;
-        }
-        for (int p = 0; p < m; ++p) row[p] = order[p];
-        row[m] = i;
-        qsort(row, (size_t)(m + 1), sizeof(int), cmp_int);
-        for (int p = m + 1; p < c->K; ++p) row[p] = -1;
-        int *dst = c->idx + (t * c->H + h) * c->K;
-        for (int p = 0; p < c->K; ++p) dst[p] = row[p];
-        size_t r = t * c->H + h;
-        if (c->gap_a) {
-            if (i >= c->K && c->K >= 2) {
-                double a = sc[order[c->K - 2]], b = sc[order[c->K - 1]];
-                double mx = fabs(a) > fabs(b) ? fabs(a) : fabs(b);
-                if (mx < 1e-30) mx = 1e-30;
-                c->gap_a[r] = a;
-                c->gap_b[r] = b;
-                c->exempt[r] = (fabs(a - b) <= 1e-5 * mx) ? 1 : 0;
-            } else {
-                c->gap_a[r] = NAN;
-                c->gap_b[r] = NAN;
-                c->exempt[r] = 0;
-            }
-        }
-    }
+    for (int tl = 0; tl < L; ++tl) route_one(c, s, h, tl, sc, order, row);
     free(sc);
     free(order);
     free(row);
@@ -348,48 +354,52 @@ typedef struct {
     double scale;
 } attn_ctx;
 
+static void attend_one(attn_ctx *c, int s, int h, int tl, double *z, int *keys)
+{
+    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    size_t t = (size_t)(t0 + tl);
+    int i = tl / c->B;
+    const int *row = c->idx + (t * c->H + h) * c->K;
+    int nk = 0;
+    /* listed past blocks, in row order */
+    for (int p = 0; p < c->K; ++p) {
+        int j = row[p];
+        if (j < 0 || j >= i) continue;
+        for (int u = j * c->B; u < (j + 1) * c->B && u < L; ++u) keys[nk++] = u;
+    }
+    /* own block, causal */
+    for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
+    const float *qv = c->q + (t * c->H + h) * c->d;
+    double M = -INFINITY;
+    for (int e = 0; e < nk; ++e) {
+        const float *kv = c->k + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
+        double acc = 0.0;
+        for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)kv[ch];
+        z[e] = c->scale * acc;
+        if (z[e] > M) M = z[e];
+    }
+    double l = 0.0;
+    for (int e = 0; e < nk; ++e) l += exp(z[e] - M);
+    double *ov = c->o + (t * c->H + h) * c->d;
+    for (int ch = 0; ch < c->d; ++ch) ov[ch] = 0.0;
+    for (int e = 0; e < nk; ++e) {
+        double p = exp(z[e] - M);
+        const float *vv = c->v + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
+        for (int ch = 0; ch < c->d; ++ch) ov[ch] += p * (double)vv[ch];
+    }
+    for (int ch = 0; ch < c->d; ++ch) ov[ch] /= l;
+    if (c->lse) c->lse[t * c->H + h] = M + log(l);
+}
+
 static void attn_job(void *vctx, int job)
 {
     attn_ctx *c = (attn_ctx *)vctx;
     int s = job / c->H, h = job % c->H;
-    int t0 = c->cu[s], L = c->cu[s + 1] - c->cu[s];
+    int L = c->cu[s + 1] - c->cu[s];
     int maxkeys = c->K * c->B + c->B;
     double *z = (double *)malloc(sizeof(double) * (size_t)maxkeys);
     int *keys = (int *)malloc(sizeof(int) * (size_t)maxkeys);
-    for (int tl = 0; tl < L; ++tl) {
-        size_t t = (size_t)(t0 + tl);
-        int i = tl / c->B;
-        const int *row = c->idx + (t * c->H + h) * c->K;
-        int nk = 0;
-        /* listed past blocks, in row order */
-        for (int p = 0; p < c->K; ++p) {
-            int j = row[p];
-            if (j < 0 || j >= i) continue;
-            for (int u = j * c->B; u < (j + 1) * c->B && u < L; ++u) keys[nk++] = u;
-        }
-        /* own block, causal */
-        for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
-        const float *qv = c->q + (t * c->H + h) * c->d;
-        double M = -INFINITY;
-        for (int e = 0; e < nk; ++e) {
-            const float *kv = c->k + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
-            double acc = 0.0;
-            for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)kv[ch];
-            z[e] = c->scale * acc;
-            if (z[e] > M) M = z[e];
-        }
-        double l = 0.0;
-        for (int e = 0; e < nk; ++e) l += exp(z[e] - M);
-        double *ov = c->o + (t * c->H + h) * c->d;
-        for (int ch = 0; ch < c->d; ++ch) ov[ch] = 0.0;
-        for (int e = 0; e < nk; ++e) {
-            double p = exp(z[e] - M);
-            const float *vv = c->v + ((size_t)(t0 + keys[e]) * c->H + h) * c->d;
-            for (int ch = 0; ch < c->d; ++ch) ov[ch] += p * (double)vv[ch];
-        }
-        for (int ch = 0; ch < c->d; ++ch) ov[ch] /= l;
-        if (c->lse) c->lse[t * c->H + h] = M + log(l);
-    }
+    for (int tl = 0; tl < L; ++tl) attend_one(c, s, h, tl, z, keys);
     free(z);
     free(keys);
 }
@@ -403,5 +413,68 @@ int moba_oracle_attend(const float *q, const float *k, const float *v,
     if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
     attn_ctx c = {q, k, v, idx, o, lse, cu, H, d, B, K, scale};
     run_jobs(attn_job, &c, nseq * H, nthreads);
+    return 0;
+}
+
+/* =====================================================================
+ * Row subsets (for sampled checks at sizes where the full oracle is too
+ * slow): the same steps 3-4 / 5 for the listed (token, head) rows only.
+ * rows[r] = token * H + head (global token index).  Outputs are written at
+ * the rows' usual places in idx / o / lse; other rows are untouched.
+ * ===================================================================== */
+static int seq_of_token(const int *cu, int nseq, int t)
+{
+    int s = 0;
+    while (s + 1 < nseq && cu[s + 1] <= t) ++s;
+    return s;
+}
+
+int moba_oracle_route_rows(const float *q, const float *cent, int H, int d, int B,
+                           int K, const int *cu, int nseq, const long long *rows,
+                           int nrows, int *idx, double *gap_a, double *gap_b,
+                           unsigned char *exempt)
+{
+    if (B < 1 || K < 1) return 1;
+    int *boff = block_offsets(cu, nseq, B);
+    route_ctx c = {q, cent, idx, gap_a, gap_b, exempt, cu, boff, H, d, B, K};
+    int nmax = 1;
+    for (int s = 0; s < nseq; ++s) {
+        int n = ceil_div(cu[s + 1] - cu[s], B);
+        if (n > nmax) nmax = n;
+    }
+    double *sc = (double *)malloc(sizeof(double) * (size_t)nmax);
+    int *order = (int *)malloc(sizeof(int) * (size_t)nmax);
+    int *row = (int *)malloc(sizeof(int) * (size_t)K);
+    for (int r = 0; r < nrows; ++r) {
+        int t = (int)(rows[r] / H), h = (int)(rows[r] % H);
+        int s = seq_of_token(cu, nseq, t);
+        route_one(&c, s, h, t - cu[s], sc, order, row);
+    }
+    free(sc);
+    free(order);
+    free(row);
+    free(boff);
+    return 0;
+}
+
+int moba_oracle_attend_rows(const float *q, const float *k, const float *v,
+                            const int *idx, int H, int d, int B, int K,
+                            const int *cu, int nseq, double scale,
+                            const long long *rows, int nrows, double *o,
+                            double *lse)
+{
+    if (B < 1 || K < 1) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    attn_ctx c = {q, k, v, idx, o, lse, cu, H, d, B, K, scale};
+    int maxkeys = K * B + B;
+    double *z = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int *keys = (int *)malloc(sizeof(int) * (size_t)maxkeys);
+    for (int r = 0; r < nrows; ++r) {
+        int t = (int)(rows[r] / H), h = (int)(rows[r] % H);
+        int s = seq_of_token(cu, nseq, t);
+        attend_one(&c, s, h, t - cu[s], z, keys);
+    }
+    free(z);
+    free(keys);
     return 0;
 }

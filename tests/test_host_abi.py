@@ -1,0 +1,111 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/moba.h declares, and
+reject bad arguments on the host before any launch.  Only host-only entry
+points and validation paths are called here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_long_key_amd as moba
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moba.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moba.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return moba._load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moba_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert "moba_attn_fwd" in names and "moba_route_topk" in names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported"
+    assert lib.moba_abi_version() == 1
+    assert lib.moba_status_string(0) == b"ok"
+    assert lib.moba_status_string(WS_SMALL) == b"workspace too small"
+
+
+def _shape(batch=1, seq=1024, heads=2, d=64, B=64, K=4, dtype=1, cu=None):
+    if cu is not None:
+        arr = (ctypes.c_int32 * len(cu))(*cu)
+        sh = moba._Shape(1, cu[-1], heads, d, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                         len(cu) - 1, B, K, dtype)
+        sh._keep = arr
+        return sh
+    return moba._Shape(batch, seq, heads, d, None, 0, B, K, dtype)
+
+
+def test_total_blocks_and_workspace(lib):
+    assert lib.moba_total_blocks(ctypes.byref(_shape(batch=2, seq=1000, B=64))) == 2 * 16
+    sh = _shape(cu=[0, 100, 100, 300], B=64)
+    assert lib.moba_total_blocks(ctypes.byref(sh)) == 2 + 0 + 4
+    assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(_shape(K=1))) == 0
+    ws = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(_shape()))
+    # at least the partial outputs: tokens * heads * k * (d * 2 + 4)
+    assert ws >= 1024 * 2 * 4 * (64 * 2 + 4)
+    s = workloads.spec("H")
+    big = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(_shape(2, 65536, 16, 64, 128, 8)))
+    assert big >= s.batch * s.seq * s.heads * s.top_k * (s.head_dim * 2 + 4)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=96), UNSUPPORTED), (dict(B=32), UNSUPPORTED), (dict(B=256), UNSUPPORTED),
+    (dict(K=0), INVALID), (dict(K=33), UNSUPPORTED), (dict(dtype=7), INVALID),
+    (dict(heads=0), INVALID), (dict(batch=65), UNSUPPORTED),
+    (dict(dtype=0, d=128, B=128), UNSUPPORTED),
+    (dict(cu=[0, 10, 5]), INVALID), (dict(cu=[1, 10]), INVALID),
+])
+def test_bad_shapes_rejected_on_host(lib, kw, code):
+    sh = _shape(**kw)
+    p = ctypes.c_void_p(16 * 1024)          # never dereferenced: validation fails first
+    rc = lib.moba_route_topk(ctypes.byref(sh), p, p, p, None)
+    assert rc == code
+    assert lib.moba_total_blocks(ctypes.byref(sh)) == -1
+    assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def test_null_misaligned_and_small_workspace_rejected(lib):
+    sh = _shape()
+    good = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 4)
+    assert lib.moba_centroids(ctypes.byref(sh), None, good, None) == INVALID
+    assert lib.moba_centroids(ctypes.byref(sh), odd, good, None) == INVALID
+    assert lib.moba_route_topk(None, good, good, good, None) == INVALID
+    need = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh))
+    rc = lib.moba_attn_fwd(ctypes.byref(sh), good, good, good, good, 0.0, good, None, good,
+                           need - 1, None)
+    assert rc == WS_SMALL
+    rc = lib.moba_attn_fwd(ctypes.byref(sh), good, good, good, good, 0.0, good, None,
+                           ctypes.c_void_p((1 << 20) + 16), need, None)
+    assert rc == INVALID                    # workspace must be 256-byte aligned
+    # conv: width and mode checks, aliasing
+    assert lib.moba_key_conv(ctypes.byref(sh), good, good, 9, 0, ctypes.c_void_p(2 << 20),
+                             None, None) == UNSUPPORTED
+    assert lib.moba_key_conv(ctypes.byref(sh), good, good, 3, 5, ctypes.c_void_p(2 << 20),
+                             None, None) == INVALID
+    assert lib.moba_key_conv(ctypes.byref(sh), good, good, 3, 0, good, None, None) == INVALID
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
+    with pytest.raises(moba.MobaError):
+        moba.moba_centroids(q, 64)

@@ -380,3 +380,20 @@ def test_effective_flops_match_counts_from_oracle_idx():
     assert workloads.eff_flops(s)["total"] == 4 * s.head_dim * keys
     pairs = int(np.sum((idx >= 0) & (idx < (np.arange(s.seq) // s.block_size)[None, :, None, None].repeat(2, 0).reshape(-1, 1, 1))))
     assert workloads.routed_pairs(s) == pairs
+
+
+def test_row_subsets_equal_full_runs():
+    H, d, B, K = 2, 8, 4, 3
+    lens = [37, 0, 20]
+    cu = list(np.cumsum([0] + lens))
+    q, k, v = (_bf16(_rand((cu[-1], H, d), s)) for s in (34, 35, 36))
+    cent = oracle.centroids(k, B, cu)
+    idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    o, lse = oracle.attend(q, k, v, idx, B, K, cu)
+    rows = np.array([0, 5, 17, 2 * 36 + 1, 2 * 37, 2 * 56 + 1])
+    ri, rga, rgb, rex = oracle.route_rows(q, cent, B, K, cu, rows)
+    assert np.array_equal(ri, idx.reshape(-1, K)[rows])
+    assert np.array_equal(rex, ex.reshape(-1)[rows])
+    ro, rl = oracle.attend_rows(q, k, v, idx, B, K, cu, rows)
+    assert np.array_equal(ro, o.reshape(-1, d)[rows])
+    assert np.array_equal(rl, lse.reshape(-1)[rows])
