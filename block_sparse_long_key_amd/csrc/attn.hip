@@ -109,27 +109,28 @@ __device__ __forceinline__ void load_kv(Smem<T, D, BLK>& sm, const T* __restrict
     }
 }
 
-// Per-wave tile state for NSB sub-tiles of 16 queries against BLK keys.
+// Per-wave tile state: two sub-tiles of 16 queries each against BLK keys.
+// Both sub-tiles share every K / V operand fragment read from LDS.
 template <typename T, int D, int BLK>
-struct WaveTile {
+struct Wave2 {
     static constexpr bool BF = sizeof(T) == 2;
     static constexpr int NKT = BLK / 16;          // key tiles
     static constexpr int NDT = D / 16;            // dim tiles
     static constexpr int QREG = BF ? D / 32 : D / 4;
-    // query fragments: bf16 -> QREG x 8 bf16; fp32 -> QREG floats
-    u16x8_t qb[BF ? QREG : 1];
-    float qf[BF ? 1 : QREG];
-    f32x4_t s[NKT];
-    f32x4_t o[NDT];
+    u16x8_t qb[2][BF ? QREG : 1];                 // bf16: B operand per k-step
+    float qf[2][BF ? 1 : QREG];                   // fp32: one k-slot per k-step
+    f32x4_t s[2][NKT];
+    f32x4_t o[2][NDT];
+    uint32_t pk[2][BF ? NKT * 2 : 1];             // bf16: P packed in pairs (PV B operand)
 
-    // B-operand fragment of query row `qrow` (null -> zero)
-    __device__ __forceinline__ void load_q(const T* qrow, int g4)
+    // B-operand fragments of query row `qrow` for sub-tile sb (null -> zero)
+    __device__ __forceinline__ void load_q(int sb, const T* qrow, int g4)
     {
         if constexpr (BF) {
 #pragma unroll
             for (int ks = 0; ks < QREG; ++ks) {
                 u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
-                qb[ks] = qrow ? *(const u16x8_t*)(qrow + 32 * ks + 8 * g4) : z;
+                qb[sb][ks] = qrow ? *(const u16x8_t*)(qrow + 32 * ks + 8 * g4) : z;
             }
         } else {
             // k-slot g4 of k-step ks <-> dim g4*(D/4) + ks (contiguous per lane)
@@ -137,48 +138,82 @@ struct WaveTile {
             for (int ks = 0; ks < QREG; ks += 4) {
                 float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
                 float4 x = qrow ? *(const float4*)((const float*)qrow + g4 * (D / 4) + ks) : z;
-                qf[ks] = x.x; qf[ks + 1] = x.y; qf[ks + 2] = x.z; qf[ks + 3] = x.w;
+                qf[sb][ks] = x.x; qf[sb][ks + 1] = x.y; qf[sb][ks + 2] = x.z; qf[sb][ks + 3] = x.w;
             }
         }
     }
 
-    // S^T tiles kt <= ktmax (others left at zero)
-    __device__ __forceinline__ void scores(const Smem<T, D, BLK>& sm, int l16, int g4, int ktmax)
+    // S^T tiles: sub-tile sb computes key tiles kt <= km[sb] (others zero).
+    // The K fragments of tile kt+1 are read from LDS while tile kt's MFMAs
+    // run; the scheduling fences keep the compiler from hoisting every
+    // fragment load (which would double the register footprint).
+    __device__ __forceinline__ void scores(const Smem<T, D, BLK>& sm, int l16, int g4, int km0, int km1)
     {
         using S = Smem<T, D, BLK>;
+        const int km = km0 > km1 ? km0 : km1;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
-            s[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if (kt > ktmax) continue;
-            if constexpr (BF) {
+            s[0][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            s[1][kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        if constexpr (BF) {
+            u16x8_t a[QREG], an[QREG];
+#pragma unroll
+            for (int ks = 0; ks < QREG; ++ks)
+                a[ks] = *(const u16x8_t*)(sm.k + l16 * S::KS + 32 * ks + 8 * g4);
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                if (kt > km) break;
+                if (kt + 1 < NKT) {
+#pragma unroll
+                    for (int ks = 0; ks < QREG; ++ks)
+                        an[ks] = *(const u16x8_t*)(sm.k + (16 * (kt + 1) + l16) * S::KS + 32 * ks + 8 * g4);
+                }
 #pragma unroll
                 for (int ks = 0; ks < QREG; ++ks) {
-                    const u16x8_t a = *(const u16x8_t*)(sm.k + (16 * kt + l16) * S::KS + 32 * ks + 8 * g4);
-                    s[kt] = mfma_bf16(a, qb[ks], s[kt]);
+                    if (kt <= km0) s[0][kt] = mfma_bf16(a[ks], qb[0][ks], s[0][kt]);
+                    if (kt <= km1) s[1][kt] = mfma_bf16(a[ks], qb[1][ks], s[1][kt]);
                 }
-            } else {
+#pragma unroll
+                for (int ks = 0; ks < QREG; ++ks) a[ks] = an[ks];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt) {
+                if (kt > km) break;
                 const float* kr = (const float*)sm.k + (16 * kt + l16) * S::KS + g4 * (D / 4);
 #pragma unroll
-                for (int ks = 0; ks < QREG; ++ks) s[kt] = mfma_f32(kr[ks], qf[ks], s[kt]);
+                for (int ks = 0; ks < QREG; ++ks) {
+                    const float a = kr[ks];
+                    if (kt <= km0) s[0][kt] = mfma_f32(a, qf[0][ks], s[0][kt]);
+                    if (kt <= km1) s[1][kt] = mfma_f32(a, qf[1][ks], s[1][kt]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     }
 
-    // O^T += V^T P^T over key tiles kt <= ktmax; s[] holds P
-    __device__ __forceinline__ void pv(const Smem<T, D, BLK>& sm, int l16, int g4, int ktmax)
+    // O^T = V^T P^T over key tiles kt <= km[sb]; s[] holds P.  One key step
+    // (32 keys) at a time, fenced like scores().
+    __device__ __forceinline__ void pv(const Smem<T, D, BLK>& sm, int l16, int g4, int km0, int km1)
     {
         using S = Smem<T, D, BLK>;
+        const int km = km0 > km1 ? km0 : km1;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt < NDT; ++dt) {
+            o[0][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            o[1][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
         if constexpr (BF) {
 #pragma unroll
             for (int ks2 = 0; ks2 < NKT / 2; ++ks2) {
-                if (2 * ks2 > ktmax) continue;
-                u16x8_t pb;
+                if (2 * ks2 > km) break;
+                u16x8_t pb[2];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    pb[r] = f32_to_bf16(s[2 * ks2][r]);
-                    pb[4 + r] = f32_to_bf16(s[2 * ks2 + 1][r]);
+                for (int sb = 0; sb < 2; ++sb) {
+                    u32x4_t w = {pk[sb][4 * ks2], pk[sb][4 * ks2 + 1], pk[sb][4 * ks2 + 2], pk[sb][4 * ks2 + 3]};
+                    pb[sb] = __builtin_bit_cast(u16x8_t, w);
                 }
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
@@ -186,53 +221,137 @@ struct WaveTile {
                     const u16x4_t lo = *(const u16x4_t*)vp;
                     const u16x4_t hi = *(const u16x4_t*)(vp + 16);
                     const u16x8_t a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    o[dt] = mfma_bf16(a, pb, o[dt]);
+                    if (2 * ks2 <= km0) o[0][dt] = mfma_bf16(a, pb[0], o[0][dt]);
+                    if (2 * ks2 <= km1) o[1][dt] = mfma_bf16(a, pb[1], o[1][dt]);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt) {
-                if (kt > ktmax) continue;
+                if (kt > km) break;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const float* vp = (const float*)sm.vt + (16 * dt + l16) * S::VS + 16 * kt + 4 * g4;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) o[dt] = mfma_f32(vp[r], s[kt][r], o[dt]);
+                    for (int r = 0; r < 4; ++r) {
+                        const float a = vp[r];
+                        if (kt <= km0) o[0][dt] = mfma_f32(a, s[0][kt][r], o[0][dt]);
+                        if (kt <= km1) o[1][dt] = mfma_f32(a, s[1][kt][r], o[1][dt]);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
+        }
+    }
+
+    // softmax of sub-tile sb in log2 units; key u > ulim masked when MASK.
+    // Returns (m2, sum of exact weights, sum of the weights used by PV).
+    template <bool MASK>
+    __device__ __forceinline__ void softmax(int sb, float sl2, int g4, int km, int ulim,
+                                            float& m2, float& sum, float& sumr)
+    {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                if constexpr (MASK) {
+                    const int u = 16 * kt + 4 * g4 + r4;
+                    if (kt > km || u > ulim) s[sb][kt][r4] = -INFINITY;
+                }
+                mx = fmaxf(mx, s[sb][kt][r4]);
+            }
+        m2 = wave_max16(mx) * sl2;
+        float a = 0.f, ar = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][kt][r4], sl2, -m2));
+                s[sb][kt][r4] = p;
+                a += p;
+            }
+        if constexpr (BF) {
+            // key tiles 2c and 2c+1 form the 8-key group of PV step c
+#pragma unroll
+            for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const uint32_t w = pack_bf16x2(s[sb][kt][2 * h2], s[sb][kt][2 * h2 + 1]);
+                    pk[sb][4 * (kt / 2) + 2 * (kt % 2) + h2] = w;
+                    ar += bf16_lo(w) + bf16_hi(w);
+                }
+        } else {
+            ar = a;
+        }
+        sum = wave_sum16(a);
+        sumr = wave_sum16(ar);
+    }
+};
+
+// A partial-output row is stored permuted so that each lane's values are
+// contiguous: dim 16*dt + 4*g + r (the O^T accumulator layout) lives at
+// g*(D/4) + 4*dt + r.  Lane g reads / writes D/4 consecutive elements.
+template <typename T, int NDT>
+__device__ __forceinline__ void store_lane_row(T* p, const float (&x)[NDT][4])
+{
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c = 0; c < NDT / 2; ++c) {
+            u32x4_t w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dt = 2 * c + e / 2, r = 2 * (e % 2);
+                w[e] = pack_bf16x2(x[dt][r], x[dt][r + 1]);
+            }
+            *(u32x4_t*)(p + 8 * c) = w;
+        }
+    } else {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            *(float4*)(p + 4 * dt) = make_float4(x[dt][0], x[dt][1], x[dt][2], x[dt][3]);
+    }
+}
+
+template <typename T, int NDT>
+struct LaneRow {
+    // packed copy of one lane's D/4 elements of a partial row
+    u32x4_t w[sizeof(T) == 2 ? NDT / 2 : NDT];
+    __device__ __forceinline__ void load(const T* p)
+    {
+#pragma unroll
+        for (int c = 0; c < (sizeof(T) == 2 ? NDT / 2 : NDT); ++c) w[c] = *(const u32x4_t*)(p + (16 / sizeof(T)) * c);
+    }
+    __device__ __forceinline__ float get(int dt, int r) const
+    {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t word = w[dt / 2][2 * (dt % 2) + r / 2];
+            return __uint_as_float((r & 1) ? (word & 0xffff0000u) : (word << 16));
+        } else {
+            return __uint_as_float(w[dt][r]);
         }
     }
 };
 
+// O (row-contiguous dims) store of one lane's O^T values
 template <typename T>
 __device__ __forceinline__ void store4(T* p, const float (&x)[4])
 {
     if constexpr (sizeof(T) == 2) {
         u32x2_t w;
-        w[0] = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
-        w[1] = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+        w[0] = pack_bf16x2(x[0], x[1]);
+        w[1] = pack_bf16x2(x[2], x[3]);
         *(u32x2_t*)p = w;
     } else {
         *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
     }
 }
-template <typename T>
-__device__ __forceinline__ void load4(const T* p, float (&x)[4])
-{
-    if constexpr (sizeof(T) == 2) {
-        const u32x2_t w = *(const u32x2_t*)p;
-        x[0] = __uint_as_float(w[0] << 16);
-        x[1] = __uint_as_float(w[0] & 0xffff0000u);
-        x[2] = __uint_as_float(w[1] << 16);
-        x[3] = __uint_as_float(w[1] & 0xffff0000u);
-    } else {
-        const float4 v = *(const float4*)p;
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    }
-}
 
 // ------------------------------------------------------------------------
-// routed attention: one item = (key block j, <= 128 gathered queries)
+// routed attention: one item = (key block j, <= kItemRows gathered queries),
+// processed in tiles of 128 queries (4 waves x 2 sub-tiles x 16) while K_j
+// and V_j stay in LDS
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(256) void routed_attn_kernel(
     SegTable st, const Item* __restrict__ items, const uint32_t* __restrict__ entries,
@@ -240,6 +359,7 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
+    constexpr int NDT = D / 16;
     // the hardware deals workgroups round-robin over the 8 XCDs; give each
     // XCD a contiguous run of items so one (sequence, head) stays in one L2
     const int64_t w = blockIdx.x;
@@ -258,52 +378,39 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
-    if (32 * wave >= it.count) return;
     const uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K + it.begin;
 
+    for (int base = 32 * wave; base < it.count; base += 128) {
+        Wave2<T, D, BLK> wt;
+        int tq[2], slot[2];
+        bool ok[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        const int r = 32 * wave + 16 * sb + l16;
-        const bool ok = r < it.count;
-        uint32_t e = ok ? ent[r] : 0u;
-        const int tq = (int)(e >> 5), slot = (int)(e & 31u);
-        WaveTile<T, D, BLK> wt;
-        wt.load_q(ok ? q + ((size_t)tq * H + h) * D : nullptr, g4);
-        wt.scores(sm, l16, g4, BLK / 16 - 1);
-        float mx = -INFINITY;
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = base + 16 * sb + l16;
+            ok[sb] = r < it.count;
+            const uint32_t e = ok[sb] ? ent[r] : 0u;
+            tq[sb] = (int)(e >> 5);
+            slot[sb] = (int)(e & 31u);
+            wt.load_q(sb, ok[sb] ? q + ((size_t)tq[sb] * H + h) * D : nullptr, g4);
+        }
+        wt.scores(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
+        float m2[2], sum[2], sumr[2];
 #pragma unroll
-        for (int kt = 0; kt < BLK / 16; ++kt)
+        for (int sb = 0; sb < 2; ++sb)
+            wt.template softmax<false>(sb, sl2, g4, BLK / 16 - 1, BLK, m2[sb], sum[sb], sumr[sb]);
+        wt.pv(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) mx = fmaxf(mx, wt.s[kt][r4]);
-        const float m2 = wave_max16(mx) * sl2;
-        // sum: exact fp32 weights (for the log-sum-exp); sumr: the weights
-        // actually used by the PV product (bf16-rounded), for normalising
-        float sum = 0.f, sumr = 0.f;
+        for (int sb = 0; sb < 2; ++sb) {
+            if (!ok[sb]) continue;
+            const float inv = 1.0f / sumr[sb];
+            const size_t prow = ((size_t)tq[sb] * H + h) * K + slot[sb];
+            float x[NDT][4];
 #pragma unroll
-        for (int kt = 0; kt < BLK / 16; ++kt)
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float p = exp2f(__builtin_fmaf(wt.s[kt][r4], sl2, -m2));
-                const float pr = (sizeof(T) == 2) ? bf16_to_f32(f32_to_bf16(p)) : p;
-                wt.s[kt][r4] = pr;
-                sum += p;
-                sumr += pr;
-            }
-        sum = wave_sum16(sum);
-        sumr = wave_sum16(sumr);
-        wt.pv(sm, l16, g4, BLK / 16 - 1);
-        if (ok) {
-            const float inv = 1.0f / sumr;
-            const size_t prow = ((size_t)tq * H + h) * K + slot;
-            T* dst = po + prow * D + 4 * g4;
-#pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                float x[4];
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) x[r4] = wt.o[dt][r4] * inv;
-                store4<T>(dst + 16 * dt, x);
-            }
-            if (g4 == 0) pl[prow] = m2 + __log2f(sum);
+                for (int r4 = 0; r4 < 4; ++r4) x[dt][r4] = wt.o[sb][dt][r4] * inv;
+            store_lane_row<T, NDT>(po + prow * D + g4 * (D / 4), x);
+            if (g4 == 0) pl[prow] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
         }
     }
 }
@@ -317,6 +424,8 @@ __global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
     float sl2, T* __restrict__ o, float* __restrict__ lse)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
+    constexpr int NDT = D / 16;
+    constexpr int PF = 4;                 // partial rows prefetched together
     const int g = blockIdx.x, h = blockIdx.y;
     const int H = st.H, K = st.K;
     const int s = seq_of_block(st, g);
@@ -332,88 +441,86 @@ __global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
     const int l16 = lane & 15, g4 = lane >> 4;
     if (32 * wave >= nq) return;
 
+    Wave2<T, D, BLK> wt;
+    bool ok[2];
+    size_t qrow[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        const int r = 32 * wave + 16 * sb + l16;        // query row in the block
-        const bool ok = r < nq;
-        const int ktmax = 2 * wave + sb;                // last key tile touching rows of this sub-tile
-        const size_t qrow = row0 + (size_t)r * H;
-        WaveTile<T, D, BLK> wt;
-        wt.load_q(ok ? q + qrow * D : nullptr, g4);
-        wt.scores(sm, l16, g4, ktmax);
-        float mx = -INFINITY;
+        const int r = 32 * wave + 16 * sb + l16;   // query row in the block
+        ok[sb] = r < nq;
+        qrow[sb] = row0 + (size_t)r * H;
+        wt.load_q(sb, ok[sb] ? q + qrow[sb] * D : nullptr, g4);
+    }
+    // last key tile touching the rows of each sub-tile
+    const int km0 = 2 * wave, km1 = 2 * wave + 1;
+    wt.scores(sm, l16, g4, km0, km1);
+    float m2[2], sum[2], sumr[2];
 #pragma unroll
-        for (int kt = 0; kt < BLK / 16; ++kt)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int u = 16 * kt + 4 * g4 + r4;
-                if (kt > ktmax || u > r) wt.s[kt][r4] = -INFINITY;
-                mx = fmaxf(mx, wt.s[kt][r4]);
-            }
-        const float m2 = wave_max16(mx) * sl2;
-        // sum: exact fp32 weights (for the log-sum-exp); sumr: the weights
-        // actually used by the PV product (bf16-rounded), for normalising
-        float sum = 0.f, sumr = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < BLK / 16; ++kt)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const float p = exp2f(__builtin_fmaf(wt.s[kt][r4], sl2, -m2));
-                const float pr = (sizeof(T) == 2) ? bf16_to_f32(f32_to_bf16(p)) : p;
-                wt.s[kt][r4] = pr;
-                sum += p;
-                sumr += pr;
-            }
-        sum = wave_sum16(sum);
-        sumr = wave_sum16(sumr);
-        wt.pv(sm, l16, g4, ktmax);
-        if (!ok) continue;
+    for (int sb = 0; sb < 2; ++sb)
+        wt.template softmax<true>(sb, sl2, g4, sb ? km1 : km0, 32 * wave + 16 * sb + l16,
+                                  m2[sb], sum[sb], sumr[sb]);
+    wt.pv(sm, l16, g4, km0, km1);
 
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        if (!ok[sb]) continue;
         // merge: running (M, wsum, acc) in log2 units, own block first
-        float acc[D / 16][4];
-        const float inv = 1.0f / sumr;
+        float acc[NDT][4];
+        const float inv = 1.0f / sumr[sb];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt)
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] = wt.o[dt][r4] * inv;
-        float M = m2 + __log2f(sum);
+            for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] = wt.o[sb][dt][r4] * inv;
+        float M = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
         float wsum = 1.0f;
-        const int32_t* irow = idx + qrow * K;
-        for (int p = 0; p < K; ++p) {
-            const int jj = irow[p];
-            if (jj < 0 || jj >= i) continue;
-            const size_t prow = qrow * K + p;
-            const float lp = pl[prow];
-            if (lp > M) {
-                const float f = exp2f(M - lp);
+        const int32_t* irow = idx + qrow[sb] * K;
+        for (int p0 = 0; p0 < K; p0 += PF) {
+            bool val[PF];
+            float lp[PF];
+            LaneRow<T, NDT> xr[PF];
 #pragma unroll
-                for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] *= f;
-                wsum *= f;
-                M = lp;
+            for (int u = 0; u < PF; ++u) {
+                const int p = p0 + u;
+                const int jj = p < K ? irow[p] : -1;
+                val[u] = jj >= 0 && jj < i;
+                lp[u] = -INFINITY;
+                if (val[u]) {
+                    const size_t prow = qrow[sb] * K + p;
+                    lp[u] = pl[prow];
+                    xr[u].load(po + prow * D + g4 * (D / 4));
+                }
             }
-            const float wgt = exp2f(lp - M);
-            wsum += wgt;
-            const T* src = po + prow * D + 4 * g4;
 #pragma unroll
-            for (int dt = 0; dt < D / 16; ++dt) {
-                float x[4];
-                load4<T>(src + 16 * dt, x);
+            for (int u = 0; u < PF; ++u) {
+                if (!val[u]) continue;
+                if (lp[u] > M) {
+                    const float f = __builtin_amdgcn_exp2f(M - lp[u]);
 #pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] = __builtin_fmaf(wgt, x[r4], acc[dt][r4]);
+                    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                        for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] *= f;
+                    wsum *= f;
+                    M = lp[u];
+                }
+                const float wgt = __builtin_amdgcn_exp2f(lp[u] - M);
+                wsum += wgt;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        acc[dt][r4] = __builtin_fmaf(wgt, xr[u].get(dt, r4), acc[dt][r4]);
             }
         }
         const float winv = 1.0f / wsum;
-        T* dst = o + qrow * D + 4 * g4;
+        T* dst = o + qrow[sb] * D + 4 * g4;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
+        for (int dt = 0; dt < NDT; ++dt) {
             float x[4];
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) x[r4] = acc[dt][r4] * winv;
             store4<T>(dst + 16 * dt, x);
         }
-        if (lse && g4 == 0) lse[qrow] = (M + __log2f(wsum)) * 0.69314718055994531f;
+        if (lse && g4 == 0) lse[qrow[sb]] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994531f;
     }
 }
 

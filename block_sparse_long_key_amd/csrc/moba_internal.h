@@ -13,8 +13,8 @@
 namespace moba {
 
 constexpr int kMaxSeqs = MOBA_MAX_SEQS;
-// queries per routed-attention work item (4 waves x 32 gathered queries)
-constexpr int kItemRows = 128;
+// most queries per routed-attention work item (looped in tiles of 128)
+constexpr int kItemRows = 512;
 // query blocks per inversion chunk (one workgroup of the count/scatter passes)
 constexpr int kInvChunkBlocks = 16;
 // largest number of blocks of one sequence (LDS histogram of the inversion)
@@ -66,19 +66,22 @@ __device__ inline int seq_of_chunk(const SegTable& st, int c) {
 
 // ------------------------------------------------------------ bf16 ------
 // bf16 is carried as its 16-bit pattern.  Rounding is IEEE round to nearest,
-// ties to even.
+// ties to even, done by the hardware conversion (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(((uint32_t)b) << 16);
 }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7f800000u) == 0x7f800000u) {
-        if (u & 0x007fffffu) u |= 0x00400000u;
-        return (uint16_t)(u >> 16);
-    }
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// two floats -> packed bf16 pair (a in the low half)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2_t x = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 template <typename T> struct IO;
 template <> struct IO<float> {
