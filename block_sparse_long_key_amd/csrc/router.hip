@@ -18,9 +18,10 @@
 // correctly-ordered sums -- and selected again.  That happens for a small
 // fraction of queries (near-ties).
 //
-// Layout: one workgroup = one query block (B threads, one query each) of one
-// head; the centroids of the past blocks stream through LDS in tiles of 32
-// and are read by all threads as broadcasts.
+// fp32 queries (VALU kernel): one workgroup = one query block (B threads,
+// one query each) of one head; the centroids of the past blocks stream
+// through LDS in tiles of 32 and are read by all threads as broadcasts.
+// bf16 queries use the MFMA kernel below.
 #include "moba_internal.h"
 
 namespace moba {
@@ -200,6 +201,321 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
     out[K - 1] = i;
 }
 
+// ------------------------------------------------------------------------
+// bf16 queries: MFMA scoring.  Each centroid c (fp32) is split into two bf16
+// terms, hi = rne(c), lo = rne(c - hi), so c = hi + lo + r with
+// |r| <= 2^-16 |c|; q is exact in bf16, every product q*hi, q*lo is exact in
+// fp32 and v_mfma_f32_16x16x32_bf16 accumulates in fp32.  Bounding each of
+// the (2d + 16) accumulation steps by one fp32 ulp gives
+//   |s_mfma - s| <= (2^-16 + (2d + 16) 2^-23) * sum_c |q_c c_c|
+//                <= (2^-16 + (2d + 16) 2^-23) * |q| * max_j |c_j|  =: E,
+// and the separation test / fp64 re-scoring work as in the VALU kernel.
+//
+// Workgroup = one query block of one head, B/32 waves of 32 queries (two
+// 16-query sub-tiles); centroid tiles of 64 blocks are staged in LDS as
+// hi / lo rows.  S^T = C Q^T puts 4 blocks x 1 query in each lane.
+//
+// Selection without branches: a score s of block j becomes a float key whose
+// low LB mantissa bits hold the lane-local block number (inverted for s >= 0
+// so that the lower block wins ties), |key - s| <= 2^(LB-23) |s|.  A lane
+// keeps its k best keys in a descending list, and inserting a key x is one
+// v_med3_f32 per slot, a[p] = med3(a[p-1], a[p], x); slots above the live k
+// hold +inf, so every register index is a compile-time constant.  The key
+// error is added to E in the separation test.  The 4 lanes of a query merge
+// their lists through LDS.
+__device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
+{
+    return sa > sb || (sa == sb && ja < jb);
+}
+__device__ __forceinline__ bool ranks_before64(double sa, int ja, double sb, int jb)
+{
+    return sa > sb || (sa == sb && ja < jb);
+}
+
+// insert (sv, j) into a descending list; j exceeds every listed index, so it
+// goes after equal scores; the last slot falls off
+template <int KMAX, typename F>
+__device__ __forceinline__ void insert_tail(F (&sc)[KMAX], int (&ix)[KMAX], F sv, int j)
+{
+#pragma unroll
+    for (int p = KMAX - 1; p >= 1; --p) {
+        if (sc[p - 1] < sv) { sc[p] = sc[p - 1]; ix[p] = ix[p - 1]; }
+        else if (sc[p] < sv) { sc[p] = sv; ix[p] = j; }
+    }
+    if (sc[0] < sv) { sc[0] = sv; ix[0] = j; }
+}
+
+template <int D, int BLK, int KMAX>
+__global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ cent,
+                                                             int32_t* __restrict__ idx)
+{
+    constexpr int TB = 64;                 // centroid rows per LDS tile
+    constexpr int CS = D + 8;              // LDS row stride (bf16 elements)
+    constexpr int NKS = D / 32;            // MFMA k-steps
+    constexpr int NT = 2 * BLK;
+    constexpr int NW = NT / 64;
+    __shared__ __align__(16) uint16_t chi[TB * CS];
+    __shared__ __align__(16) uint16_t clo[TB * CS];
+    __shared__ float red[NW];
+    __shared__ float qstage[NW][D];
+    // merge buffers: per wave, 64 lanes x KMAX entries (fp32 lists for the
+    // 4-lane merge; fp64 lists for the re-scoring merge)
+    __shared__ double mscore[NW][KMAX][64];
+    __shared__ int mj[NW][KMAX][64];
+
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int H = st.H, K = st.K;
+    const int s = seq_of_block(st, g);
+    const int i = g - st.boff[s];
+    const int L = seq_len(st, s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
+    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
+
+    int tl[2];
+    bool valid[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        tl[sb] = i * BLK + 32 * wave + 16 * sb + l16;
+        valid[sb] = tl[sb] < L;
+    }
+    if (K == 1 || i <= K - 1) {
+        // only the own block, or every past block: no scoring
+        if (g4 == 0) {
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                if (!valid[sb]) continue;
+                int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+                if (K == 1) out[0] = i;
+                else for (int p = 0; p < K; ++p) out[p] = p <= i ? p : -1;
+            }
+        }
+        return;
+    }
+
+    // query fragments (B operand) and |q|^2
+    u16x8_t qb[2][NKS];
+    float qn2[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        float acc = 0.f;
+        const uint16_t* qp = q + ((size_t)(st.cu[s] + tl[sb]) * H + h) * D;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+            qb[sb][ks] = valid[sb] ? *(const u16x8_t*)(qp + 32 * ks + 8 * g4) : z;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = bf16_to_f32(qb[sb][ks][e]);
+                acc = __builtin_fmaf(x, x, acc);
+            }
+        }
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        qn2[sb] = acc;
+    }
+
+    // per-lane key lists: live entries are slots [KMAX-K, KMAX)
+    float key[2][KMAX];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) key[sb][p] = p < KMAX - K ? INFINITY : -INFINITY;
+    // lane-local block numbers (j / 16) * 4 + r stay below 4 * ceil(i / 16)
+    const int nloc = 4 * ((i + 15) / 16);
+    const int LB = 32 - __builtin_clz((unsigned)(nloc - 1) | 1u);
+    const uint32_t lmask = (1u << LB) - 1u;
+    const float kdel = ldexpf(1.0f, LB - 23) * 1.01f;
+    float cmax2 = 0.f;                      // max |c|^2 over the past blocks
+
+    for (int j0 = 0; j0 < i; j0 += TB) {
+        __syncthreads();
+        // stage the tile: hi / lo bf16 rows, and the row norms
+        for (int e = threadIdx.x; e < TB * (D / 4); e += NT) {
+            const int r = e / (D / 4), c4 = e % (D / 4);
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + r < i) x = *(const float4*)(cbase + (size_t)(j0 + r) * H * D + 4 * c4);
+            const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
+            const uint32_t l01 = pack_bf16x2(x.x - bf16_lo(h01), x.y - bf16_hi(h01));
+            const uint32_t l23 = pack_bf16x2(x.z - bf16_lo(h23), x.w - bf16_hi(h23));
+            *(u32x2_t*)(chi + r * CS + 4 * c4) = u32x2_t{h01, h23};
+            *(u32x2_t*)(clo + r * CS + 4 * c4) = u32x2_t{l01, l23};
+            float n2 = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+            // the D/4 consecutive threads of a row reduce its norm
+#pragma unroll
+            for (int m = 1; m < D / 4; m <<= 1) n2 += __shfl_xor(n2, m);
+            cmax2 = fmaxf(cmax2, n2);
+        }
+        __syncthreads();
+        for (int bt = 0; bt < TB / 16; ++bt) {
+            const int jb = j0 + 16 * bt;
+            if (jb >= i) break;
+            u16x8_t ah[NKS], al[NKS];
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                ah[ks] = *(const u16x8_t*)(chi + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
+                al[ks] = *(const u16x8_t*)(clo + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
+            }
+#pragma unroll
+            for (int sb = 0; sb < 2; ++sb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah[ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
+                                                                  acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[ks]),
+                                                                  __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
+                                                                  acc, 0, 0, 0);
+                }
+                // lane holds blocks jb + 4*g4 + r for query l16 of sub-tile sb
+                const float thr = key[sb][KMAX - 1];
+                float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+                if (jb + 16 > i) mx = INFINITY;               // partial tile: mask below
+                // a key exceeds its score by at most 2^(LB-23)|s|: skip the tile
+                // only when no key can reach the list
+                if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t jl = (uint32_t)(jb / 16 * 4 + r);
+                        const uint32_t bits = __float_as_uint(acc[r]);
+                        const uint32_t low = (bits >> 31) ? jl : (lmask - jl);
+                        float x = __uint_as_float((bits & ~lmask) | low);
+                        if (jb + 4 * g4 + r >= i) x = -INFINITY;
+#pragma unroll
+                        for (int p = KMAX - 1; p >= 1; --p)
+                            key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
+                        key[sb][0] = fmaxf(key[sb][0], x);
+                    }
+                }
+            }
+        }
+    }
+    // max centroid norm over the workgroup
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) cmax2 = fmaxf(cmax2, __shfl_xor(cmax2, m));
+    if (lane == 0) red[wave] = cmax2;
+    __syncthreads();
+    float cm2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) cm2 = fmaxf(cm2, red[w]);
+    const float cmax = sqrtf(cm2);
+    const float E0 = (1.52587890625e-05f + (float)(2 * D + 16) * 1.1920929e-07f) * 1.02f;
+
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+        // 4-lane merge through LDS: each lane decodes its block ids, then lane
+        // g4 == 0 of each query reads the four lists (live slots KMAX-K ..
+        // KMAX-1) and keeps the best K
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) {
+            const uint32_t bits = __float_as_uint(key[sb][p]);
+            const uint32_t low = bits & lmask;
+            const uint32_t jl = (bits >> 31) ? low : (lmask - low);
+            mscore[wave][p][lane] = key[sb][p];
+            mj[wave][p][lane] = (int)(16 * (jl / 4) + 4 * g4 + (jl % 4));
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        bool flag = false;
+        int sel[KMAX];
+        if (g4 == 0) {
+            int ptr[4] = {KMAX - K, KMAX - K, KMAX - K, KMAX - K};
+            float a = 0.f, b = 0.f;
+#pragma unroll
+            for (int rd = 0; rd < KMAX; ++rd) {
+                sel[rd] = 0x7fffffff;
+                if (rd >= K) continue;
+                float bs = -INFINITY;
+                int bj = 0x7fffffff, bl = 0;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float vs = ptr[u] < KMAX ? (float)mscore[wave][ptr[u]][l16 + 16 * u] : -INFINITY;
+                    const int vj = ptr[u] < KMAX ? mj[wave][ptr[u]][l16 + 16 * u] : 0x7fffffff;
+                    if (ranks_before(vs, vj, bs, bj)) { bs = vs; bj = vj; bl = u; }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) ptr[u] += (u == bl);
+                if (rd < K - 1) sel[rd] = bj;
+                if (rd == K - 2) a = bs;
+                if (rd == K - 1) b = bs;
+            }
+            // keys are within 2^(LB-23)|s| of the MFMA scores
+            const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
+            const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
+            flag = !(a - b > 2.0f * E);
+            if (valid[sb] && !flag) {
+                sort_asc<KMAX>(sel);
+                int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if (p < K - 1) out[p] = sel[p];
+                out[K - 1] = i;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // near-ties: the whole wave re-scores each flagged query in fp64
+        uint64_t fm = __ballot(valid[sb] && g4 == 0 && flag);
+        while (fm) {
+            const int src = __builtin_ctzll(fm);
+            fm &= fm - 1;
+            const int tq = __shfl(tl[sb], src);
+            const uint16_t* qp = q + ((size_t)(st.cu[s] + tq) * H + h) * D;
+            for (int c = lane; c < D; c += 64) qstage[wave][c] = bf16_to_f32(qp[c]);
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            const int K1 = K - 1;
+            double s64[KMAX];
+            int j64[KMAX];
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p) { s64[p] = p < KMAX - K1 ? INFINITY : -INFINITY; j64[p] = -1; }
+            for (int j = lane; j < i; j += 64) {
+                const float* cp = cbase + (size_t)j * H * D;
+                double acc = 0.0;
+                for (int c = 0; c < D; ++c) acc = __builtin_fma((double)qstage[wave][c], (double)cp[c], acc);
+                if (acc > s64[KMAX - 1]) insert_tail<KMAX>(s64, j64, acc, j);
+            }
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p) {
+                mscore[wave][p][lane] = s64[p];
+                mj[wave][p][lane] = j64[p];
+            }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            // K-1 rounds of a 64-lane argmax over the list heads
+            int ptr = KMAX - K1;
+            int rsel[KMAX];
+#pragma unroll
+            for (int rd = 0; rd < KMAX; ++rd) {
+                rsel[rd] = 0x7fffffff;
+                if (rd >= K1) continue;
+                double bs = ptr < KMAX ? mscore[wave][ptr][lane] : -INFINITY;
+                int bj = ptr < KMAX ? mj[wave][ptr][lane] : 0x7fffffff;
+                if (bj < 0) bj = 0x7fffffff;
+                const int myj = bj;
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) {
+                    const double os = __shfl_xor(bs, m);
+                    const int oj = __shfl_xor(bj, m);
+                    if (ranks_before64(os, oj, bs, bj)) { bs = os; bj = oj; }
+                }
+                rsel[rd] = bj;
+                ptr += (myj == bj);
+            }
+            sort_asc<KMAX>(rsel);
+            if (lane == 0) {
+                int32_t* out = idx + ((size_t)(st.cu[s] + tq) * H + h) * K;
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if (p < K - 1) out[p] = rsel[p];
+                out[K - 1] = i;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_d(const Launch& L, const void* q, const float* cent, int32_t* idx)
 {
@@ -220,12 +536,31 @@ hipError_t launch_d(const Launch& L, const void* q, const float* cent, int32_t* 
 
 }  // namespace
 
+template <int D, int BLK>
+hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_t* idx)
+{
+    dim3 grid(L.st.total_blocks, L.st.H);
+    dim3 block(2 * BLK);
+    const int K = L.st.K;
+    const uint16_t* qq = (const uint16_t*)q;
+    if (K <= 8)
+        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+    else if (K <= 16)
+        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+    else
+        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
-    if (L.dtype == MOBA_BF16)
-        return L.D == 64 ? launch_d<uint16_t, 64>(L, q, cent, idx)
-                         : launch_d<uint16_t, 128>(L, q, cent, idx);
+    if (L.dtype == MOBA_BF16) {
+        if (L.D == 64) return L.st.B == 64 ? launch_mfma<64, 64>(L, q, cent, idx)
+                                           : launch_mfma<64, 128>(L, q, cent, idx);
+        return L.st.B == 64 ? launch_mfma<128, 64>(L, q, cent, idx)
+                            : launch_mfma<128, 128>(L, q, cent, idx);
+    }
     return L.D == 64 ? launch_d<float, 64>(L, q, cent, idx)
                      : launch_d<float, 128>(L, q, cent, idx);
 }
