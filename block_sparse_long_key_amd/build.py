@@ -2,8 +2,9 @@
 
 Every ``csrc/*.hip`` file is compiled to an object in ``_build/`` (in
 parallel) and linked into ``block_sparse_long_key_amd/libmoba_amd.so``.
-Flags: gfx950 only, -O3, and packed-fp32 instructions disabled (hipcc's host
-pass warns that it does not know that feature; the warning is harmless).
+Flags: gfx950 only, -O3, packed-fp32 instructions disabled (hipcc's host
+pass warns that it does not know that feature; the warning is harmless), and
+MFMA accumulators kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -21,6 +22,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs (no AGPR round trips)
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=true",
     "-Wall", "-Wno-unused-function",
 ]
 

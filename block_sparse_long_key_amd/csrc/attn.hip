@@ -19,7 +19,9 @@
 //   is exactly the B-operand layout of the second product once keys are
 //   paired as {4g..4g+3, 16+4g..16+4g+3}, so P never leaves registers.
 //   Output: one normalised partial o (I/O dtype) and its log2-sum-exp per
-//   (query, slot).
+//   (query, slot), stored in list order so each tile's writes are one
+//   contiguous run of full rows (scattered partial-line writes cost far
+//   more than the MFMA work).
 // own-block kernel -- one workgroup per (query block i, head): the causal
 //   tile Q_i K_i^T (u <= t), same MFMA scheme, skipping key tiles that are
 //   fully masked, then the merge of that result with the query's routed
@@ -122,6 +124,7 @@ struct Wave2 {
     f32x4_t s[2][NKT];
     f32x4_t o[2][NDT];
     uint32_t pk[2][BF ? NKT * 2 : 1];             // bf16: P packed in pairs (PV B operand)
+    f32x4_t osum[2];                              // bf16: row sums of the rounded P (MFMA)
 
     // B-operand fragments of query row `qrow` for sub-tile sb (null -> zero)
     __device__ __forceinline__ void load_q(int sb, const T* qrow, int g4)
@@ -206,6 +209,11 @@ struct Wave2 {
             o[1][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
         if constexpr (BF) {
+            // an all-ones A operand turns one more MFMA per key step into the
+            // row sums of the bf16 weights, accumulated exactly like O
+            osum[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            osum[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            const u16x8_t ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80, 0x3f80};
 #pragma unroll
             for (int ks2 = 0; ks2 < NKT / 2; ++ks2) {
                 if (2 * ks2 > km) break;
@@ -224,6 +232,8 @@ struct Wave2 {
                     if (2 * ks2 <= km0) o[0][dt] = mfma_bf16(a, pb[0], o[0][dt]);
                     if (2 * ks2 <= km1) o[1][dt] = mfma_bf16(a, pb[1], o[1][dt]);
                 }
+                if (2 * ks2 <= km0) osum[0] = mfma_bf16(ones, pb[0], osum[0]);
+                if (2 * ks2 <= km1) osum[1] = mfma_bf16(ones, pb[1], osum[1]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         } else {
@@ -246,10 +256,11 @@ struct Wave2 {
     }
 
     // softmax of sub-tile sb in log2 units; key u > ulim masked when MASK.
-    // Returns (m2, sum of exact weights, sum of the weights used by PV).
+    // Returns m2 and the sum of the exact fp32 weights (for the log-sum-exp);
+    // bf16 packs P for the PV product.
     template <bool MASK>
     __device__ __forceinline__ void softmax(int sb, float sl2, int g4, int km, int ulim,
-                                            float& m2, float& sum, float& sumr)
+                                            float& m2, float& sum)
     {
         float mx = -INFINITY;
 #pragma unroll
@@ -263,30 +274,32 @@ struct Wave2 {
                 mx = fmaxf(mx, s[sb][kt][r4]);
             }
         m2 = wave_max16(mx) * sl2;
-        float a = 0.f, ar = 0.f;
+        float a0 = 0.f, a1 = 0.f;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][kt][r4], sl2, -m2));
                 s[sb][kt][r4] = p;
-                a += p;
+                if (r4 & 1) a1 += p; else a0 += p;
             }
         if constexpr (BF) {
             // key tiles 2c and 2c+1 form the 8-key group of PV step c
 #pragma unroll
             for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const uint32_t w = pack_bf16x2(s[sb][kt][2 * h2], s[sb][kt][2 * h2 + 1]);
-                    pk[sb][4 * (kt / 2) + 2 * (kt % 2) + h2] = w;
-                    ar += bf16_lo(w) + bf16_hi(w);
-                }
-        } else {
-            ar = a;
+                for (int h2 = 0; h2 < 2; ++h2)
+                    pk[sb][4 * (kt / 2) + 2 * (kt % 2) + h2] =
+                        pack_bf16x2(s[sb][kt][2 * h2], s[sb][kt][2 * h2 + 1]);
         }
-        sum = wave_sum16(a);
-        sumr = wave_sum16(ar);
+        sum = wave_sum16(a0 + a1);
+    }
+
+    // sum of the weights the PV product used (call after pv)
+    __device__ __forceinline__ float used_sum(int sb, float sum) const
+    {
+        if constexpr (BF) return osum[sb][0];
+        else return sum;
     }
 };
 
@@ -359,7 +372,9 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
+    __shared__ uint32_t sent[kItemRows];
     constexpr int NDT = D / 16;
+    using W = Wave2<T, D, BLK>;
     // the hardware deals workgroups round-robin over the 8 XCDs; give each
     // XCD a contiguous run of items so one (sequence, head) stays in one L2
     const int64_t w = blockIdx.x;
@@ -373,37 +388,78 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     const int j = it.g - st.boff[s];
     const int t0 = st.cu[s];
     const int L = seq_len(st, s);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
+
+    // the item's (query, slot) entries go to LDS once; its partials are
+    // written at the same (list-order) positions, so every tile writes one
+    // contiguous run of full rows
+    const int64_t e0 = st.ebase[s] + (int64_t)h * L * K + it.begin;
+    const uint32_t* ent = entries + e0;
+    for (int r = threadIdx.x; r < it.count; r += 256) sent[r] = ent[r];
+
+    // gathered query fragments of the first tile are requested before the
+    // K / V staging so the two overlap
+    W wt;
+    u16x8_t qn[2][W::BF ? W::QREG : 1];
+    float qfn[2][W::BF ? 1 : W::QREG];
+    int base = 32 * wave;
+    auto fetch_q = [&](int b0, u16x8_t (&qb)[2][W::BF ? W::QREG : 1], float (&qf)[2][W::BF ? 1 : W::QREG],
+                       const uint32_t* src) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = b0 + 16 * sb + l16;
+            const bool ok = r < it.count;
+            const uint32_t e = ok ? src[r] : 0u;
+            const T* qrow = ok ? q + ((size_t)(e >> 5) * H + h) * D : nullptr;
+            if constexpr (W::BF) {
+#pragma unroll
+                for (int ks = 0; ks < W::QREG; ++ks) {
+                    u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
+                    qb[sb][ks] = qrow ? *(const u16x8_t*)(qrow + 32 * ks + 8 * g4) : z;
+                }
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < W::QREG; ks += 4) {
+                    float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+                    float4 x = qrow ? *(const float4*)((const float*)qrow + g4 * (D / 4) + ks) : z;
+                    qf[sb][ks] = x.x; qf[sb][ks + 1] = x.y; qf[sb][ks + 2] = x.z; qf[sb][ks + 3] = x.w;
+                }
+            }
+        }
+    };
+    if (base < it.count) fetch_q(base, qn, qfn, ent);
     load_kv<T, D, BLK, 256>(sm, k, v, (size_t)(t0 + j * BLK) * H + h, H, BLK);
     __syncthreads();
 
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int l16 = lane & 15, g4 = lane >> 4;
-    const uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K + it.begin;
-
-    for (int base = 32 * wave; base < it.count; base += 128) {
-        Wave2<T, D, BLK> wt;
-        int tq[2], slot[2];
+    for (; base < it.count; base += 128) {
+        // current tile's fragments; the next tile's are requested now and
+        // arrive while this one computes
         bool ok[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int r = base + 16 * sb + l16;
             ok[sb] = r < it.count;
-            const uint32_t e = ok[sb] ? ent[r] : 0u;
-            tq[sb] = (int)(e >> 5);
-            slot[sb] = (int)(e & 31u);
-            wt.load_q(sb, ok[sb] ? q + ((size_t)tq[sb] * H + h) * D : nullptr, g4);
+            if constexpr (W::BF) {
+#pragma unroll
+                for (int ks = 0; ks < W::QREG; ++ks) wt.qb[sb][ks] = qn[sb][ks];
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < W::QREG; ++ks) wt.qf[sb][ks] = qfn[sb][ks];
+            }
         }
+        if (base + 128 < it.count) fetch_q(base + 128, qn, qfn, sent);
         wt.scores(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
-        float m2[2], sum[2], sumr[2];
+        float m2[2], sum[2];
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb)
-            wt.template softmax<false>(sb, sl2, g4, BLK / 16 - 1, BLK, m2[sb], sum[sb], sumr[sb]);
+            wt.template softmax<false>(sb, sl2, g4, BLK / 16 - 1, BLK, m2[sb], sum[sb]);
         wt.pv(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             if (!ok[sb]) continue;
-            const float inv = 1.0f / sumr[sb];
-            const size_t prow = ((size_t)tq[sb] * H + h) * K + slot[sb];
+            const float inv = 1.0f / wt.used_sum(sb, sum[sb]);
+            const size_t prow = (size_t)(e0 + base + 16 * sb + l16);
             float x[NDT][4];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
@@ -416,16 +472,29 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
 }
 
 // ------------------------------------------------------------------------
-// own block (causal) + merge of the routed partials
+// own block (causal) + merge of the routed partials.
+// Phase A: the causal tile on MFMA, as in the routed kernel.  Phase B: the
+// own-block result goes to LDS (over the K rows, no longer needed) in the
+// partials' lane-permuted layout.  Phase C: lanes are re-mapped to
+// (query, 16-byte chunk); the query's list positions come from the reverse
+// map built by the index pass, its partial rows are gathered as coalesced
+// 16-byte chunks and merged with a running (max, sum) in log2 units.
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
     SegTable st, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ idx, const T* __restrict__ po, const float* __restrict__ pl,
+    const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
     float sl2, T* __restrict__ o, float* __restrict__ lse)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
+    __shared__ float own_lse[BLK];
     constexpr int NDT = D / 16;
-    constexpr int PF = 4;                 // partial rows prefetched together
+    constexpr int CH = 16 / sizeof(T);        // elements per 16-byte chunk
+    constexpr int NCH = D / CH;               // chunks per row
+    constexpr int QPP = 64 / NCH;             // queries per wave pass
+    constexpr int PF = 8;                     // slots loaded together
+    static_assert(BLK * D <= BLK * Smem<T, D, BLK>::KS, "own rows fit over K");
+    T* own = sm.k;                            // [BLK][D], lane-permuted rows
+
     const int g = blockIdx.x, h = blockIdx.y;
     const int H = st.H, K = st.K;
     const int s = seq_of_block(st, g);
@@ -439,88 +508,117 @@ __global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
-    if (32 * wave >= nq) return;
+    const bool active = 32 * wave < nq;
 
+    // ---- phase A
     Wave2<T, D, BLK> wt;
-    bool ok[2];
-    size_t qrow[2];
+    float m2[2], sum[2];
+    if (active) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        const int r = 32 * wave + 16 * sb + l16;   // query row in the block
-        ok[sb] = r < nq;
-        qrow[sb] = row0 + (size_t)r * H;
-        wt.load_q(sb, ok[sb] ? q + qrow[sb] * D : nullptr, g4);
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = 32 * wave + 16 * sb + l16;
+            wt.load_q(sb, r < nq ? q + (row0 + (size_t)r * H) * D : nullptr, g4);
+        }
+        const int km0 = 2 * wave, km1 = 2 * wave + 1;   // last key tile of each sub-tile
+        wt.scores(sm, l16, g4, km0, km1);
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+            wt.template softmax<true>(sb, sl2, g4, sb ? km1 : km0, 32 * wave + 16 * sb + l16,
+                                      m2[sb], sum[sb]);
+        wt.pv(sm, l16, g4, km0, km1);
     }
-    // last key tile touching the rows of each sub-tile
-    const int km0 = 2 * wave, km1 = 2 * wave + 1;
-    wt.scores(sm, l16, g4, km0, km1);
-    float m2[2], sum[2], sumr[2];
+    __syncthreads();
+    // ---- phase B
+    if (active) {
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-        wt.template softmax<true>(sb, sl2, g4, sb ? km1 : km0, 32 * wave + 16 * sb + l16,
-                                  m2[sb], sum[sb], sumr[sb]);
-    wt.pv(sm, l16, g4, km0, km1);
-
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = 32 * wave + 16 * sb + l16;
+            const float inv = 1.0f / wt.used_sum(sb, sum[sb]);
+            float x[NDT][4];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        if (!ok[sb]) continue;
-        // merge: running (M, wsum, acc) in log2 units, own block first
-        float acc[NDT][4];
-        const float inv = 1.0f / sumr[sb];
+            for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+                for (int r4 = 0; r4 < 4; ++r4) x[dt][r4] = wt.o[sb][dt][r4] * inv;
+            store_lane_row<T, NDT>(own + r * D + g4 * (D / 4), x);
+            if (g4 == 0) own_lse[r] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+    // ---- phase C
+    const int c = lane % NCH, ql = lane / NCH;
+    for (int pass = 0; pass < 32 / QPP; ++pass) {
+        const int r = 32 * wave + pass * QPP + ql;
+        if (r >= nq) break;
+        const size_t qrow = row0 + (size_t)r * H;
+        float acc[CH];
+        {
+            const u32x4_t w = *(const u32x4_t*)(own + r * D + c * CH);
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] = wt.o[sb][dt][r4] * inv;
-        float M = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+                for (int e = 0; e < 4; ++e) { acc[2 * e] = bf16_lo(w[e]); acc[2 * e + 1] = bf16_hi(w[e]); }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(w[e]);
+            }
+        }
+        float M = own_lse[r];
         float wsum = 1.0f;
-        const int32_t* irow = idx + qrow[sb] * K;
-        for (int p0 = 0; p0 < K; p0 += PF) {
-            bool val[PF];
+        // the query's K list positions (-1: nothing routed in that slot)
+        const int32_t* rrow = rev + qrow * K;
+        const int64_t eb = st.ebase[s] + (int64_t)h * L * K;
+        const int kmerge = K > 1 ? K : 0;      // K == 1: no routed partials exist
+        for (int p0 = 0; p0 < kmerge; p0 += PF) {
+            int pos[PF];
+#pragma unroll
+            for (int u = 0; u < PF; ++u) pos[u] = (p0 + u < kmerge) ? rrow[p0 + u] : -1;
             float lp[PF];
-            LaneRow<T, NDT> xr[PF];
+            u32x4_t xv[PF];
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
-                const int p = p0 + u;
-                const int jj = p < K ? irow[p] : -1;
-                val[u] = jj >= 0 && jj < i;
-                lp[u] = -INFINITY;
-                if (val[u]) {
-                    const size_t prow = qrow[sb] * K + p;
+                if (pos[u] >= 0) {
+                    const int64_t prow = eb + pos[u];
                     lp[u] = pl[prow];
-                    xr[u].load(po + prow * D + g4 * (D / 4));
+                    xv[u] = *(const u32x4_t*)(po + prow * D + c * CH);
                 }
             }
 #pragma unroll
             for (int u = 0; u < PF; ++u) {
-                if (!val[u]) continue;
+                if (pos[u] < 0) continue;
                 if (lp[u] > M) {
                     const float f = __builtin_amdgcn_exp2f(M - lp[u]);
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                        for (int r4 = 0; r4 < 4; ++r4) acc[dt][r4] *= f;
+                    for (int e = 0; e < CH; ++e) acc[e] *= f;
                     wsum *= f;
                     M = lp[u];
                 }
                 const float wgt = __builtin_amdgcn_exp2f(lp[u] - M);
                 wsum += wgt;
+                if constexpr (sizeof(T) == 2) {
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
+                    for (int e = 0; e < 4; ++e) {
+                        acc[2 * e] = __builtin_fmaf(wgt, bf16_lo(xv[u][e]), acc[2 * e]);
+                        acc[2 * e + 1] = __builtin_fmaf(wgt, bf16_hi(xv[u][e]), acc[2 * e + 1]);
+                    }
+                } else {
 #pragma unroll
-                    for (int r4 = 0; r4 < 4; ++r4)
-                        acc[dt][r4] = __builtin_fmaf(wgt, xr[u].get(dt, r4), acc[dt][r4]);
+                    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(wgt, __uint_as_float(xv[u][e]), acc[e]);
+                }
             }
         }
+        // stored position c*CH + e holds dim 16*dt + 4*gg + r4 with
+        // gg = pos / (D/4), dt = (pos % (D/4)) / 4: runs of 4 consecutive dims
         const float winv = 1.0f / wsum;
-        T* dst = o + qrow[sb] * D + 4 * g4;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
+        for (int e4 = 0; e4 < CH / 4; ++e4) {
+            const int pos = c * CH + 4 * e4;
+            const int dim = 16 * ((pos % (D / 4)) / 4) + 4 * (pos / (D / 4));
             float x[4];
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) x[r4] = acc[dt][r4] * winv;
-            store4<T>(dst + 16 * dt, x);
+            for (int r4 = 0; r4 < 4; ++r4) x[r4] = acc[4 * e4 + r4] * winv;
+            store4<T>(o + qrow * D + dim, x);
         }
-        if (lse && g4 == 0) lse[qrow[sb]] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994531f;
+        if (lse && c == 0) lse[qrow] = (M + __builtin_amdgcn_logf(wsum)) * 0.69314718055994531f;
     }
 }
 
@@ -544,9 +642,11 @@ hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                   const void* v, const int32_t* idx, float sl2, void* o, float* lse)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
+    (void)idx;   // the index pass turned idx into the reverse map
     hipLaunchKernelGGL((diag_combine_kernel<T, D, BLK>), dim3(L.st.total_blocks, L.st.H),
-                       dim3(2 * BLK), 0, L.stream, L.st, (const T*)q, (const T*)k, (const T*)v, idx,
-                       (const T*)(wsp + ws.po_off), (const float*)(wsp + ws.pl_off), sl2, (T*)o, lse);
+                       dim3(2 * BLK), 0, L.stream, L.st, (const T*)q, (const T*)k, (const T*)v,
+                       (const int32_t*)(wsp + ws.rev_off), (const T*)(wsp + ws.po_off),
+                       (const float*)(wsp + ws.pl_off), sl2, (T*)o, lse);
     return hipGetLastError();
 }
 

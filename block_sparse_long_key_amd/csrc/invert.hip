@@ -12,7 +12,8 @@
 //              per-chunk positions (in place), and the work items (runs of
 //              <= 128 entries of one list) for the routed attention;
 //   scatter -- same grid as count: entries (token << 5 | slot) written at the
-//              chunk's positions with LDS cursors.
+//              chunk's positions with LDS cursors, and the reverse map
+//              (query, slot) -> list position (-1 where nothing is routed).
 // The own block is not listed (the own-block kernel handles it); -1 and
 // out-of-range ids are skipped.  Order inside a list is not deterministic,
 // which the routed attention does not depend on (each row of a tile is
@@ -135,7 +136,8 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
 
 __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ cmat,
-                                                              uint32_t* __restrict__ entries)
+                                                              uint32_t* __restrict__ entries,
+                                                              int32_t* __restrict__ rev)
 {
     extern __shared__ int32_t cur[];
     const int c = blockIdx.x, h = blockIdx.y;
@@ -151,14 +153,19 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
     const int nent = (tl1 - tl0) * K;
     const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
+    int32_t* rv = rev + ((size_t)(t0 + tl0) * H + h) * K;
     for (int e = threadIdx.x; e < nent; e += kThreads) {
         const int r = e / K, slot = e - r * K;
         const int j = src[(size_t)r * H * K + slot];
         const int i = (tl0 + r) / B;
+        int p = -1;
         if (j >= 0 && j < i) {
-            const int p = atomicAdd(&cur[j], 1);
+            p = atomicAdd(&cur[j], 1);
             ent[p] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
         }
+        // every slot is written, so each query's K positions form one
+        // contiguous, fully written record
+        rv[(size_t)r * H * K + slot] = p;
     }
 }
 
@@ -171,6 +178,7 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
     int32_t* cmat = (int32_t*)(wsp + ws.cmat_off);
     Item* items = (Item*)(wsp + ws.items_off);
     uint32_t* ent = (uint32_t*)(wsp + ws.ent_off);
+    int32_t* rev = (int32_t*)(wsp + ws.rev_off);
     int maxn = 0;
     for (int s = 0; s < st.nseq; ++s) maxn = maxn > seq_nblk(st, s) ? maxn : seq_nblk(st, s);
     dim3 gc(st.total_chunks, st.H);
@@ -182,7 +190,7 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(inv_scatter_kernel, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx,
-                       cmat, ent);
+                       cmat, ent, rev);
     return hipGetLastError();
 }
 

@@ -98,13 +98,16 @@ WsLayout layout(const Launch& L)
         w.cmat_bytes = (size_t)st.cmbase[st.nseq] * 4;
         w.items_bytes = (size_t)st.total_items * sizeof(Item);
         w.ent_bytes = (size_t)st.ebase[st.nseq] * 4;
-        w.po_bytes = rows * st.K * L.D * esz;
-        w.pl_bytes = rows * st.K * 4;
+        w.rev_bytes = rows * st.K * 4;
+        // partials are indexed like the entries (list order)
+        w.po_bytes = (size_t)st.ebase[st.nseq] * L.D * esz;
+        w.pl_bytes = (size_t)st.ebase[st.nseq] * 4;
     }
     size_t off = 0;
     w.cmat_off = off;  off += align256(w.cmat_bytes);
     w.items_off = off; off += align256(w.items_bytes);
     w.ent_off = off;   off += align256(w.ent_bytes);
+    w.rev_off = off;   off += align256(w.rev_bytes);
     w.po_off = off;    off += align256(w.po_bytes);
     w.pl_off = off;    off += align256(w.pl_bytes);
     w.total = off;

@@ -216,13 +216,11 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 // hi / lo rows.  S^T = C Q^T puts 4 blocks x 1 query in each lane.
 //
 // Selection without branches: a score s of block j becomes a float key whose
-// low LB mantissa bits hold the lane-local block number (inverted for s >= 0
-// so that the lower block wins ties), |key - s| <= 2^(LB-23) |s|.  A lane
-// keeps its k best keys in a descending list, and inserting a key x is one
-// v_med3_f32 per slot, a[p] = med3(a[p-1], a[p], x); slots above the live k
-// hold +inf, so every register index is a compile-time constant.  The key
-// error is added to E in the separation test.  The 4 lanes of a query merge
-// their lists through LDS.
+// low LB mantissa bits hold j (inverted for s >= 0 so that the lower block
+// wins ties), |key - s| <= 2^(LB-23) |s|.  A lane keeps its KMAX best keys
+// in a descending list, and inserting a key x is one v_med3_f32 per slot,
+// a[p] = med3(a[p-1], a[p], x).  The key error is added to E in the
+// separation test.  The 4 lanes of a query merge their lists by shuffles.
 __device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
 {
     return sa > sb || (sa == sb && ja < jb);
@@ -316,15 +314,14 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
         qn2[sb] = acc;
     }
 
-    // per-lane key lists: live entries are slots [KMAX-K, KMAX)
+    // per-lane key lists (descending, all KMAX slots live); the low LB
+    // mantissa bits of a key carry the block id j < i
     float key[2][KMAX];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int p = 0; p < KMAX; ++p) key[sb][p] = p < KMAX - K ? INFINITY : -INFINITY;
-    // lane-local block numbers (j / 16) * 4 + r stay below 4 * ceil(i / 16)
-    const int nloc = 4 * ((i + 15) / 16);
-    const int LB = 32 - __builtin_clz((unsigned)(nloc - 1) | 1u);
+        for (int p = 0; p < KMAX; ++p) key[sb][p] = -INFINITY;
+    const int LB = 32 - __builtin_clz((unsigned)(i - 1) | 1u);
     const uint32_t lmask = (1u << LB) - 1u;
     const float kdel = ldexpf(1.0f, LB - 23) * 1.01f;
     float cmax2 = 0.f;                      // max |c|^2 over the past blocks
@@ -371,22 +368,26 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
                 }
                 // lane holds blocks jb + 4*g4 + r for query l16 of sub-tile sb
                 const float thr = key[sb][KMAX - 1];
-                float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-                if (jb + 16 > i) mx = INFINITY;               // partial tile: mask below
-                // a key exceeds its score by at most 2^(LB-23)|s|: skip the tile
-                // only when no key can reach the list
+                const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+                // a key exceeds its score by at most 2^(LB-23)|s|: skip the
+                // group only when no key can reach the list
                 if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
+                    const bool full = jb + 16 <= i;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const uint32_t jl = (uint32_t)(jb / 16 * 4 + r);
+                        // key: score with its low LB bits replaced by j (s < 0)
+                        // or lmask - j (s >= 0), so equal scores rank the lower j
+                        // first and every key decodes back to its block
+                        const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
                         const uint32_t bits = __float_as_uint(acc[r]);
-                        const uint32_t low = (bits >> 31) ? jl : (lmask - jl);
-                        float x = __uint_as_float((bits & ~lmask) | low);
-                        if (jb + 4 * g4 + r >= i) x = -INFINITY;
+                        const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
+                        const uint32_t low = j ^ (lmask & ~neg);
+                        float x = __uint_as_float((bits & ~lmask) | (low & lmask));
+                        if (!full && (int)j >= i) x = -INFINITY;
 #pragma unroll
                         for (int p = KMAX - 1; p >= 1; --p)
                             key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
-                        key[sb][0] = fmaxf(key[sb][0], x);
+                        key[sb][0] = __builtin_amdgcn_fmed3f(key[sb][0], x, INFINITY);
                     }
                 }
             }
@@ -405,47 +406,49 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
 
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        // 4-lane merge through LDS: each lane decodes its block ids, then lane
-        // g4 == 0 of each query reads the four lists (live slots KMAX-K ..
-        // KMAX-1) and keeps the best K
+        // merge the 4 lanes of a query (lanes l16 + 16*g4): two rounds of
+        // "top KMAX of two sorted lists" -- c[p] = max(a[p], b[KMAX-1-p]) is
+        // bitonic and holds the top KMAX, a bitonic clean sorts it -- after
+        // which all 4 lanes hold the query's sorted top KMAX keys
 #pragma unroll
-        for (int p = 0; p < KMAX; ++p) {
-            const uint32_t bits = __float_as_uint(key[sb][p]);
-            const uint32_t low = bits & lmask;
-            const uint32_t jl = (bits >> 31) ? low : (lmask - low);
-            mscore[wave][p][lane] = key[sb][p];
-            mj[wave][p][lane] = (int)(16 * (jl / 4) + 4 * g4 + (jl % 4));
+        for (int m = 16; m <= 32; m <<= 1) {
+            float b[KMAX];
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p) b[p] = __shfl_xor(key[sb][p], m);
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p) key[sb][p] = fmaxf(key[sb][p], b[KMAX - 1 - p]);
+#pragma unroll
+            for (int st2 = KMAX / 2; st2 >= 1; st2 >>= 1)
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if ((p & st2) == 0) {
+                        const float hi = fmaxf(key[sb][p], key[sb][p + st2]);
+                        const float lo = fminf(key[sb][p], key[sb][p + st2]);
+                        key[sb][p] = hi;
+                        key[sb][p + st2] = lo;
+                    }
         }
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         bool flag = false;
-        int sel[KMAX];
-        if (g4 == 0) {
-            int ptr[4] = {KMAX - K, KMAX - K, KMAX - K, KMAX - K};
-            float a = 0.f, b = 0.f;
+        {
+            float a = key[sb][0], b = key[sb][0];
 #pragma unroll
-            for (int rd = 0; rd < KMAX; ++rd) {
-                sel[rd] = 0x7fffffff;
-                if (rd >= K) continue;
-                float bs = -INFINITY;
-                int bj = 0x7fffffff, bl = 0;
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float vs = ptr[u] < KMAX ? (float)mscore[wave][ptr[u]][l16 + 16 * u] : -INFINITY;
-                    const int vj = ptr[u] < KMAX ? mj[wave][ptr[u]][l16 + 16 * u] : 0x7fffffff;
-                    if (ranks_before(vs, vj, bs, bj)) { bs = vs; bj = vj; bl = u; }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) ptr[u] += (u == bl);
-                if (rd < K - 1) sel[rd] = bj;
-                if (rd == K - 2) a = bs;
-                if (rd == K - 1) b = bs;
+            for (int p = 1; p < KMAX; ++p) {
+                a = (p == K - 2) ? key[sb][p] : a;
+                b = (p == K - 1) ? key[sb][p] : b;
             }
             // keys are within 2^(LB-23)|s| of the MFMA scores
             const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
             const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
             flag = !(a - b > 2.0f * E);
-            if (valid[sb] && !flag) {
+            if (g4 == 0 && valid[sb] && !flag) {
+                int sel[KMAX];
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p) {
+                    const uint32_t bits = __float_as_uint(key[sb][p]);
+                    const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
+                    const int jj = (int)((bits ^ (lmask & ~neg)) & lmask);
+                    sel[p] = p < K - 1 ? jj : 0x7fffffff;
+                }
                 sort_asc<KMAX>(sel);
                 int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
 #pragma unroll

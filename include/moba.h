@@ -130,7 +130,8 @@ moba_status moba_route_topk(const moba_shape *shape, const void *q,
  *   For query t in block i: keys = all keys of each listed past block
  *   (0 <= idx < i) plus the keys u <= t of block i.  -1 entries are padding;
  *   listed entries >= i are ignored (the own block is always attended).
- *   Listed past blocks must be distinct.
+ *   Listed past blocks must be distinct.  With top_k == 1 only the own
+ *   block is attended (a row has no room for a routed block).
  *   z_u = scale * q_t . k_u; O_t = softmax(z) V; LSE_t = max z + ln sum
  *   exp(z - max z) (natural log).
  *   softmax_scale <= 0 selects 1/sqrt(head_dim).
