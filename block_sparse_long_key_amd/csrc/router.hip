@@ -28,6 +28,8 @@ namespace moba {
 namespace {
 
 constexpr int kTile = 32;
+// idx slot-0 marker: row awaiting the exact fp64 re-selection
+constexpr int32_t kPending = (int32_t)0x80000000;
 
 template <int KMAX>
 __device__ __forceinline__ void insert_desc(float (&sc)[KMAX], int (&ix)[KMAX], int K,
@@ -243,6 +245,14 @@ __device__ __forceinline__ void insert_tail(F (&sc)[KMAX], int (&ix)[KMAX], F sv
     if (sc[0] < sv) { sc[0] = sv; ix[0] = j; }
 }
 
+// block id carried in the low bits of a selection key
+__device__ __forceinline__ int key_block(float k, uint32_t lmask)
+{
+    const uint32_t bits = __float_as_uint(k);
+    const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
+    return (int)((bits ^ (lmask & ~neg)) & lmask);
+}
+
 template <int D, int BLK, int KMAX>
 __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
                                                              const float* __restrict__ cent,
@@ -256,11 +266,6 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
     __shared__ __align__(16) uint16_t chi[TB * CS];
     __shared__ __align__(16) uint16_t clo[TB * CS];
     __shared__ float red[NW];
-    __shared__ float qstage[NW][D];
-    // merge buffers: per wave, 64 lanes x KMAX entries (fp32 lists for the
-    // 4-lane merge; fp64 lists for the re-scoring merge)
-    __shared__ double mscore[NW][KMAX][64];
-    __shared__ int mj[NW][KMAX][64];
 
     const int g = blockIdx.x, h = blockIdx.y;
     const int H = st.H, K = st.K;
@@ -406,106 +411,229 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
 
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        // merge the 4 lanes of a query (lanes l16 + 16*g4): two rounds of
-        // "top KMAX of two sorted lists" -- c[p] = max(a[p], b[KMAX-1-p]) is
-        // bitonic and holds the top KMAX, a bitonic clean sorts it -- after
-        // which all 4 lanes hold the query's sorted top KMAX keys
+        // merge the 4 lanes of a query (lanes l16 + 16*g4) into the top
+        // MW keys (2*KMAX for the short lists, else KMAX): two rounds of
+        // "top MW of two sorted lists" -- c[p] = max(a[p], b[MW-1-p]) is
+        // bitonic and holds the top MW, a bitonic clean sorts it; afterwards
+        // all 4 lanes hold the query's sorted top MW keys
+        constexpr int MW = KMAX <= 8 ? 2 * KMAX : KMAX;
+        float mk[MW];
+        const float mylast = key[sb][KMAX - 1];
+#pragma unroll
+        for (int p = 0; p < MW; ++p) mk[p] = p < KMAX ? key[sb][p] : -INFINITY;
 #pragma unroll
         for (int m = 16; m <= 32; m <<= 1) {
-            float b[KMAX];
+            float bb[MW];
 #pragma unroll
-            for (int p = 0; p < KMAX; ++p) b[p] = __shfl_xor(key[sb][p], m);
+            for (int p = 0; p < MW; ++p) bb[p] = (m == 16 && p >= KMAX) ? -INFINITY : __shfl_xor(mk[p], m);
+            // (with MW == KMAX the first round keeps the top KMAX of 2 KMAX)
 #pragma unroll
-            for (int p = 0; p < KMAX; ++p) key[sb][p] = fmaxf(key[sb][p], b[KMAX - 1 - p]);
+            for (int p = 0; p < MW; ++p) mk[p] = fmaxf(mk[p], bb[MW - 1 - p]);
 #pragma unroll
-            for (int st2 = KMAX / 2; st2 >= 1; st2 >>= 1)
+            for (int st2 = MW / 2; st2 >= 1; st2 >>= 1)
 #pragma unroll
-                for (int p = 0; p < KMAX; ++p)
+                for (int p = 0; p < MW; ++p)
                     if ((p & st2) == 0) {
-                        const float hi = fmaxf(key[sb][p], key[sb][p + st2]);
-                        const float lo = fminf(key[sb][p], key[sb][p + st2]);
-                        key[sb][p] = hi;
-                        key[sb][p + st2] = lo;
+                        const float hi = fmaxf(mk[p], mk[p + st2]);
+                        const float lo = fminf(mk[p], mk[p + st2]);
+                        mk[p] = hi;
+                        mk[p + st2] = lo;
                     }
         }
-        bool flag = false;
-        {
-            float a = key[sb][0], b = key[sb][0];
+        // highest key any lane dropped is below its own last kept key
+        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
+        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
+        float a = mk[0], b = mk[0];
 #pragma unroll
-            for (int p = 1; p < KMAX; ++p) {
-                a = (p == K - 2) ? key[sb][p] : a;
-                b = (p == K - 1) ? key[sb][p] : b;
-            }
-            // keys are within 2^(LB-23)|s| of the MFMA scores
-            const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
-            const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
-            flag = !(a - b > 2.0f * E);
-            if (g4 == 0 && valid[sb] && !flag) {
-                int sel[KMAX];
+        for (int p = 1; p < KMAX; ++p) {
+            a = (p == K - 2) ? mk[p] : a;
+            b = (p == K - 1) ? mk[p] : b;
+        }
+        // keys are within 2^(LB-23)|s| of the MFMA scores
+        const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
+        const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
+        const bool flag = !(a - b > 2.0f * E);
+        int sel[KMAX];
 #pragma unroll
-                for (int p = 0; p < KMAX; ++p) {
-                    const uint32_t bits = __float_as_uint(key[sb][p]);
-                    const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
-                    const int jj = (int)((bits ^ (lmask & ~neg)) & lmask);
-                    sel[p] = p < K - 1 ? jj : 0x7fffffff;
+        for (int p = 0; p < KMAX; ++p)
+            sel[p] = (!flag && p < K - 1) ? key_block(mk[p], lmask) : 0x7fffffff;
+        // near-tie: every block that can still be selected has a key >= a - 2E
+        // (its exact score is >= a - E).  If no such key can have been dropped,
+        // re-score just those in fp64 and select among them.
+        const float tlow = a - 2.0f * E;
+        const bool local = flag && mk[MW - 1] < tlow && lastmax < tlow;
+        if (__ballot(valid[sb] && local)) {
+            double ex[MW / 4];
+            int jx[MW / 4];
+            const uint16_t* qp = q + ((size_t)(st.cu[s] + tl[sb]) * H + h) * D;
+#pragma unroll
+            for (int u = 0; u < MW / 4; ++u) {
+                const int p = 4 * u + g4;
+                bool inU = false;
+#pragma unroll
+                for (int e = 0; e < MW; ++e) if (e == p) inU = mk[e] >= tlow;
+                float kp = mk[0];
+#pragma unroll
+                for (int e = 0; e < MW; ++e) if (e == p) kp = mk[e];
+                jx[u] = 0x7fffffff;
+                ex[u] = -INFINITY;
+                if (valid[sb] && local && inU) {
+                    const int j = key_block(kp, lmask);
+                    const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
+                    double acc = 0.0;
+#pragma unroll
+                    for (int c8 = 0; c8 < D / 8; ++c8) {
+                        const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
+                        const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
+                        acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
+                    }
+                    ex[u] = acc;
+                    jx[u] = j;
                 }
-                sort_asc<KMAX>(sel);
-                int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+            }
+            // every lane of the query gathers the MW (score, block) pairs and
+            // ranks its own; the K-1 best by (score desc, block asc) win
+            double as[MW];
+            int aj[MW];
 #pragma unroll
-                for (int p = 0; p < KMAX; ++p)
-                    if (p < K - 1) out[p] = sel[p];
-                out[K - 1] = i;
+            for (int u = 0; u < MW / 4; ++u)
+#pragma unroll
+                for (int src = 0; src < 4; ++src) {
+                    as[4 * u + src] = __shfl(ex[u], l16 + 16 * src);
+                    aj[4 * u + src] = __shfl(jx[u], l16 + 16 * src);
+                }
+            if (valid[sb] && local) {
+#pragma unroll
+                for (int p = 0; p < MW; ++p) {
+                    int rank = 0;
+#pragma unroll
+                    for (int e = 0; e < MW; ++e) rank += ranks_before64(as[e], aj[e], as[p], aj[p]) ? 1 : 0;
+                    // the selection holds K-1 blocks; slot order is fixed by the sort below
+#pragma unroll
+                    for (int r = 0; r < KMAX; ++r)
+                        if (r == rank && r < K - 1) sel[r] = aj[p];
+                }
             }
         }
-        __builtin_amdgcn_wave_barrier();
-        // near-ties: the whole wave re-scores each flagged query in fp64
-        uint64_t fm = __ballot(valid[sb] && g4 == 0 && flag);
+        if (g4 == 0 && valid[sb] && (!flag || local)) {
+            sort_asc<KMAX>(sel);
+            int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p)
+                if (p < K - 1) out[p] = sel[p];
+            out[K - 1] = i;
+        }
+        // near-ties that could not be settled here: mark the row;
+        // route_refine_kernel re-selects it in fp64
+        if (g4 == 0 && valid[sb] && flag && !local)
+            idx[((size_t)(st.cu[s] + tl[sb]) * H + h) * K] = kPending;
+    }
+}
+
+// ------------------------------------------------------------------------
+// Exact re-selection of the rows the MFMA kernel marked (near-ties): one
+// wave per query block.  Lanes score past blocks j = lane, lane + 64, ...
+// in fp64 (products of bf16 by fp32 are exact in fp64), two rows at a time
+// so two FMA chains overlap, and keep their best KMAX by (score desc, index
+// asc); a 6-level bitonic merge over the lanes ("top KMAX of two sorted
+// lists", c[p] = better(a[p], b[KMAX-1-p]) then a bitonic clean) leaves the
+// sorted global best KMAX in every lane.  Blocks without a marked row exit
+// after one look at their rows.
+__device__ __forceinline__ void cas_desc(double& s0, int& j0, double& s1, int& j1)
+{
+    // afterwards (s0, j0) ranks before (s1, j1)
+    if (ranks_before64(s1, j1, s0, j0)) {
+        const double ts = s0; s0 = s1; s1 = ts;
+        const int tj = j0; j0 = j1; j1 = tj;
+    }
+}
+
+template <int D, int BLK, int KMAX>
+__global__ __launch_bounds__(64) void route_refine_kernel(SegTable st, const uint16_t* __restrict__ q,
+                                                          const float* __restrict__ cent,
+                                                          int32_t* __restrict__ idx)
+{
+    __shared__ __align__(16) float qstage[D];
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int H = st.H, K = st.K;
+    const int s = seq_of_block(st, g);
+    const int i = g - st.boff[s];
+    if (K == 1 || i <= K - 1) return;                  // no scoring happened here
+    const int L = seq_len(st, s);
+    const int lane = threadIdx.x;
+    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
+    for (int r0 = 0; r0 < BLK; r0 += 64) {
+        const int tl = i * BLK + r0 + lane;
+        const bool mine = r0 + lane < BLK && tl < L &&
+                          idx[((size_t)(st.cu[s] + tl) * H + h) * K] == kPending;
+        uint64_t fm = __ballot(mine);
         while (fm) {
             const int src = __builtin_ctzll(fm);
             fm &= fm - 1;
-            const int tq = __shfl(tl[sb], src);
+            const int tq = i * BLK + r0 + src;
             const uint16_t* qp = q + ((size_t)(st.cu[s] + tq) * H + h) * D;
-            for (int c = lane; c < D; c += 64) qstage[wave][c] = bf16_to_f32(qp[c]);
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            const int K1 = K - 1;
-            double s64[KMAX];
-            int j64[KMAX];
+            for (int c = lane; c < D; c += 64) qstage[c] = bf16_to_f32(qp[c]);
+            __syncthreads();
+            double sc[KMAX];
+            int jx[KMAX];
 #pragma unroll
-            for (int p = 0; p < KMAX; ++p) { s64[p] = p < KMAX - K1 ? INFINITY : -INFINITY; j64[p] = -1; }
-            for (int j = lane; j < i; j += 64) {
-                const float* cp = cbase + (size_t)j * H * D;
-                double acc = 0.0;
-                for (int c = 0; c < D; ++c) acc = __builtin_fma((double)qstage[wave][c], (double)cp[c], acc);
-                if (acc > s64[KMAX - 1]) insert_tail<KMAX>(s64, j64, acc, j);
+            for (int p = 0; p < KMAX; ++p) { sc[p] = -INFINITY; jx[p] = 0x7fffffff; }
+            const float4* qs = (const float4*)qstage;
+            for (int j = lane; j < i; j += 128) {
+                const int j2 = j + 64;
+                const bool two = j2 < i;
+                const float4* cp0 = (const float4*)(cbase + (size_t)j * H * D);
+                const float4* cp1 = (const float4*)(cbase + (size_t)(two ? j2 : j) * H * D);
+                double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+                for (int c8 = 0; c8 < D / 4; c8 += 4) {
+                    float4 u0[4], u1[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) { u0[u] = cp0[c8 + u]; u1[u] = cp1[c8 + u]; }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float4 qv = qs[c8 + u];
+                        a0 = __builtin_fma((double)qv.x, (double)u0[u].x, a0);
+                        a1 = __builtin_fma((double)qv.x, (double)u1[u].x, a1);
+                        a0 = __builtin_fma((double)qv.y, (double)u0[u].y, a0);
+                        a1 = __builtin_fma((double)qv.y, (double)u1[u].y, a1);
+                        a0 = __builtin_fma((double)qv.z, (double)u0[u].z, a0);
+                        a1 = __builtin_fma((double)qv.z, (double)u1[u].z, a1);
+                        a0 = __builtin_fma((double)qv.w, (double)u0[u].w, a0);
+                        a1 = __builtin_fma((double)qv.w, (double)u1[u].w, a1);
+                    }
+                }
+                if (a0 > sc[KMAX - 1]) insert_tail<KMAX>(sc, jx, a0, j);
+                if (two && a1 > sc[KMAX - 1]) insert_tail<KMAX>(sc, jx, a1, j2);
             }
 #pragma unroll
-            for (int p = 0; p < KMAX; ++p) {
-                mscore[wave][p][lane] = s64[p];
-                mj[wave][p][lane] = j64[p];
+            for (int m = 1; m < 64; m <<= 1) {
+                double os[KMAX];
+                int oj[KMAX];
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p) { os[p] = __shfl_xor(sc[p], m); oj[p] = __shfl_xor(jx[p], m); }
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if (ranks_before64(os[KMAX - 1 - p], oj[KMAX - 1 - p], sc[p], jx[p])) {
+                        sc[p] = os[KMAX - 1 - p];
+                        jx[p] = oj[KMAX - 1 - p];
+                    }
+#pragma unroll
+                for (int st2 = KMAX / 2; st2 >= 1; st2 >>= 1)
+#pragma unroll
+                    for (int p = 0; p < KMAX; ++p)
+                        if ((p & st2) == 0) cas_desc(sc[p], jx[p], sc[p + st2], jx[p + st2]);
             }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-            // K-1 rounds of a 64-lane argmax over the list heads
-            int ptr = KMAX - K1;
             int rsel[KMAX];
 #pragma unroll
-            for (int rd = 0; rd < KMAX; ++rd) {
-                rsel[rd] = 0x7fffffff;
-                if (rd >= K1) continue;
-                double bs = ptr < KMAX ? mscore[wave][ptr][lane] : -INFINITY;
-                int bj = ptr < KMAX ? mj[wave][ptr][lane] : 0x7fffffff;
-                if (bj < 0) bj = 0x7fffffff;
-                const int myj = bj;
-#pragma unroll
-                for (int m = 1; m < 64; m <<= 1) {
-                    const double os = __shfl_xor(bs, m);
-                    const int oj = __shfl_xor(bj, m);
-                    if (ranks_before64(os, oj, bs, bj)) { bs = os; bj = oj; }
-                }
-                rsel[rd] = bj;
-                ptr += (myj == bj);
-            }
+            for (int p = 0; p < KMAX; ++p) rsel[p] = p < K - 1 ? jx[p] : 0x7fffffff;
             sort_asc<KMAX>(rsel);
             if (lane == 0) {
                 int32_t* out = idx + ((size_t)(st.cu[s] + tq) * H + h) * K;
@@ -514,7 +642,7 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
                     if (p < K - 1) out[p] = rsel[p];
                 out[K - 1] = i;
             }
-            __builtin_amdgcn_wave_barrier();
+            __syncthreads();
         }
     }
 }
@@ -546,12 +674,16 @@ hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_
     dim3 block(2 * BLK);
     const int K = L.st.K;
     const uint16_t* qq = (const uint16_t*)q;
-    if (K <= 8)
+    if (K <= 8) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-    else if (K <= 16)
+        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+    } else if (K <= 16) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-    else
+        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+    } else {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+    }
     return hipGetLastError();
 }
 

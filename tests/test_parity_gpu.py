@@ -197,6 +197,32 @@ def _run_case(seqlens, H, d, B, K, dtype, seed, conv_w_width=0, scale=None, v_on
     return o, lse, idx, ref
 
 
+@pytest.mark.parametrize("period,seq,B,K", [(3, 4096, 64, 8), (5, 8192, 64, 16), (40, 8192, 64, 8)])
+def test_route_exact_ties(period, seq, B, K):
+    """Keys that repeat block by block with a period give bit-identical
+    centroids, so each query sees classes of exactly tied scores and the
+    lower block index must win.  Period 3 makes tie classes of up to ~n/3
+    blocks: more than fit the router's candidate window, so both the in-kernel
+    fp64 re-selection and the separate re-selection kernel are exercised."""
+    H, d = 2, 64
+    print(f"[ties period {period} seq {seq} B{B} K{K}]", flush=True)
+    g = torch.Generator().manual_seed(1000 + period)
+    q = torch.randn((seq, H, d), generator=g).to(torch.bfloat16)
+    base = torch.randn((period * B, H, d), generator=g).to(torch.bfloat16)
+    nblk = seq // B
+    k = torch.cat([base[(j % period) * B:(j % period + 1) * B] for j in range(nblk)])
+    cu = [0, seq]
+    cent = oracle.centroids(k, B, cu)
+    ref_idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    idx = moba().moba_route_topk(q.to(DEV), torch.from_numpy(cent).to(DEV), B, K, cu)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().reshape(ref_idx.shape)
+    ndiff = int(np.any(got != ref_idx, axis=-1).sum())
+    print(f"[ties period {period}] rows differing: {ndiff}; near-tie rows: {int(ex.sum())}")
+    assert ex.sum() > 0
+    assert ndiff == 0
+
+
 @pytest.mark.parametrize("seqlens,H,d,B,K,dtype", [
     ([1000], 2, 64, 64, 4, "bf16"),           # ragged tail (1000 = 15*64 + 40)
     ([130, 1, 64, 300], 3, 64, 128, 8, "bf16"),  # short / single-token sequences
