@@ -253,8 +253,34 @@ __device__ __forceinline__ int key_block(float k, uint32_t lmask)
     return (int)((bits ^ (lmask & ~neg)) & lmask);
 }
 
+// Sorted (descending) top-N merge of the lists of lanes l, l^16, l^32, l^48.
+// The first NIN entries of x are the lane's own sorted list (the rest -INF).
+template <int N, int NIN>
+__device__ __forceinline__ void merge_lanes(float (&x)[N])
+{
+#pragma unroll
+    for (int m = 16; m <= 32; m <<= 1) {
+        float y[N];
+#pragma unroll
+        for (int p = 0; p < N; ++p) y[p] = (m == 16 && p >= NIN) ? -INFINITY : __shfl_xor(x[p], m);
+#pragma unroll
+        for (int p = 0; p < N; ++p) x[p] = fmaxf(x[p], y[N - 1 - p]);
+#pragma unroll
+        for (int st2 = N / 2; st2 >= 1; st2 >>= 1)
+#pragma unroll
+            for (int p = 0; p < N; ++p)
+                if ((p & st2) == 0) {
+                    const float hi = fmaxf(x[p], x[p + st2]);
+                    const float lo = fminf(x[p], x[p + st2]);
+                    x[p] = hi;
+                    x[p + st2] = lo;
+                }
+    }
+}
+
 template <int D, int BLK, int KMAX>
-__global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
+// (d = 64 with short lists fits 96 VGPRs: ask for 5 waves per SIMD)
+__global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
                                                              const float* __restrict__ cent,
                                                              int32_t* __restrict__ idx)
 {
@@ -411,38 +437,14 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
 
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        // merge the 4 lanes of a query (lanes l16 + 16*g4) into the top
-        // MW keys (2*KMAX for the short lists, else KMAX): two rounds of
-        // "top MW of two sorted lists" -- c[p] = max(a[p], b[MW-1-p]) is
-        // bitonic and holds the top MW, a bitonic clean sorts it; afterwards
-        // all 4 lanes hold the query's sorted top MW keys
-        constexpr int MW = KMAX <= 8 ? 2 * KMAX : KMAX;
-        float mk[MW];
-        const float mylast = key[sb][KMAX - 1];
+        // merge the 4 lanes of a query (lanes l16 + 16*g4): two rounds of
+        // "top N of two sorted lists" -- c[p] = max(x[p], y[N-1-p]) is
+        // bitonic and holds the top N of both, a bitonic clean sorts it;
+        // afterwards all 4 lanes hold the query's sorted top N keys
+        float mk[KMAX];
 #pragma unroll
-        for (int p = 0; p < MW; ++p) mk[p] = p < KMAX ? key[sb][p] : -INFINITY;
-#pragma unroll
-        for (int m = 16; m <= 32; m <<= 1) {
-            float bb[MW];
-#pragma unroll
-            for (int p = 0; p < MW; ++p) bb[p] = (m == 16 && p >= KMAX) ? -INFINITY : __shfl_xor(mk[p], m);
-            // (with MW == KMAX the first round keeps the top KMAX of 2 KMAX)
-#pragma unroll
-            for (int p = 0; p < MW; ++p) mk[p] = fmaxf(mk[p], bb[MW - 1 - p]);
-#pragma unroll
-            for (int st2 = MW / 2; st2 >= 1; st2 >>= 1)
-#pragma unroll
-                for (int p = 0; p < MW; ++p)
-                    if ((p & st2) == 0) {
-                        const float hi = fmaxf(mk[p], mk[p + st2]);
-                        const float lo = fminf(mk[p], mk[p + st2]);
-                        mk[p] = hi;
-                        mk[p + st2] = lo;
-                    }
-        }
-        // highest key any lane dropped is below its own last kept key
-        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
-        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
+        for (int p = 0; p < KMAX; ++p) mk[p] = key[sb][p];
+        merge_lanes<KMAX, KMAX>(mk);
         float a = mk[0], b = mk[0];
 #pragma unroll
         for (int p = 1; p < KMAX; ++p) {
@@ -453,31 +455,46 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
         const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
         const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
         const bool flag = !(a - b > 2.0f * E);
-        int sel[KMAX];
+        if (g4 == 0 && valid[sb] && !flag) {
+            int sel[KMAX];
 #pragma unroll
-        for (int p = 0; p < KMAX; ++p)
-            sel[p] = (!flag && p < K - 1) ? key_block(mk[p], lmask) : 0x7fffffff;
+            for (int p = 0; p < KMAX; ++p) sel[p] = p < K - 1 ? key_block(mk[p], lmask) : 0x7fffffff;
+            sort_asc<KMAX>(sel);
+            int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p)
+                if (p < K - 1) out[p] = sel[p];
+            out[K - 1] = i;
+        }
+        if (!__ballot(valid[sb] && flag)) continue;
+
         // near-tie: every block that can still be selected has a key >= a - 2E
-        // (its exact score is >= a - E).  If no such key can have been dropped,
-        // re-score just those in fp64 and select among them.
+        // (its exact score is >= a - E).  Merge again keeping the top MW; if
+        // no key that high can have been dropped (by the merge or by a lane's
+        // own list), re-score those blocks in fp64 and select among them.
+        constexpr int MW = KMAX <= 8 ? 2 * KMAX : KMAX;
+        float wk[MW];
+#pragma unroll
+        for (int p = 0; p < MW; ++p) wk[p] = p < KMAX ? key[sb][p] : -INFINITY;
+        merge_lanes<MW, KMAX>(wk);
+        const float mylast = key[sb][KMAX - 1];
+        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
+        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
         const float tlow = a - 2.0f * E;
-        const bool local = flag && mk[MW - 1] < tlow && lastmax < tlow;
+        const bool local = flag && wk[MW - 1] < tlow && lastmax < tlow;
         if (__ballot(valid[sb] && local)) {
+            // lane g4 re-scores merged positions p = 4u + g4 that reach tlow
             double ex[MW / 4];
             int jx[MW / 4];
             const uint16_t* qp = q + ((size_t)(st.cu[s] + tl[sb]) * H + h) * D;
 #pragma unroll
             for (int u = 0; u < MW / 4; ++u) {
-                const int p = 4 * u + g4;
-                bool inU = false;
+                float kp = wk[4 * u];
 #pragma unroll
-                for (int e = 0; e < MW; ++e) if (e == p) inU = mk[e] >= tlow;
-                float kp = mk[0];
-#pragma unroll
-                for (int e = 0; e < MW; ++e) if (e == p) kp = mk[e];
+                for (int e = 1; e < 4; ++e) kp = g4 == e ? wk[4 * u + e] : kp;
                 jx[u] = 0x7fffffff;
                 ex[u] = -INFINITY;
-                if (valid[sb] && local && inU) {
+                if (valid[sb] && local && kp >= tlow) {
                     const int j = key_block(kp, lmask);
                     const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
                     double acc = 0.0;
@@ -498,37 +515,41 @@ __global__ __launch_bounds__(2 * BLK) void route_mfma_kernel(SegTable st, const 
                     jx[u] = j;
                 }
             }
-            // every lane of the query gathers the MW (score, block) pairs and
-            // ranks its own; the K-1 best by (score desc, block asc) win
-            double as[MW];
-            int aj[MW];
+            // rank each own candidate against all MW of the query (score
+            // desc, block asc); the K-1 first are selected.  Candidates that
+            // were not re-scored rank after every re-scored one.
+            int rk[MW / 4];
 #pragma unroll
-            for (int u = 0; u < MW / 4; ++u)
+            for (int u = 0; u < MW / 4; ++u) rk[u] = 0;
 #pragma unroll
-                for (int src = 0; src < 4; ++src) {
-                    as[4 * u + src] = __shfl(ex[u], l16 + 16 * src);
-                    aj[4 * u + src] = __shfl(jx[u], l16 + 16 * src);
+            for (int src = 0; src < 4; ++src)
+#pragma unroll
+                for (int u2 = 0; u2 < MW / 4; ++u2) {
+                    const double os = __shfl(ex[u2], l16 + 16 * src);
+                    const int oj = __shfl(jx[u2], l16 + 16 * src);
+#pragma unroll
+                    for (int u = 0; u < MW / 4; ++u) rk[u] += ranks_before64(os, oj, ex[u], jx[u]) ? 1 : 0;
+                }
+            // output slot of a selected block: selected blocks with a lower id
+            int pos[MW / 4];
+#pragma unroll
+            for (int u = 0; u < MW / 4; ++u) pos[u] = 0;
+#pragma unroll
+            for (int src = 0; src < 4; ++src)
+#pragma unroll
+                for (int u2 = 0; u2 < MW / 4; ++u2) {
+                    const int oj = __shfl(jx[u2], l16 + 16 * src);
+                    const int orank = __shfl(rk[u2], l16 + 16 * src);
+#pragma unroll
+                    for (int u = 0; u < MW / 4; ++u) pos[u] += (orank < K - 1 && oj < jx[u]) ? 1 : 0;
                 }
             if (valid[sb] && local) {
+                int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
 #pragma unroll
-                for (int p = 0; p < MW; ++p) {
-                    int rank = 0;
-#pragma unroll
-                    for (int e = 0; e < MW; ++e) rank += ranks_before64(as[e], aj[e], as[p], aj[p]) ? 1 : 0;
-                    // the selection holds K-1 blocks; slot order is fixed by the sort below
-#pragma unroll
-                    for (int r = 0; r < KMAX; ++r)
-                        if (r == rank && r < K - 1) sel[r] = aj[p];
-                }
+                for (int u = 0; u < MW / 4; ++u)
+                    if (rk[u] < K - 1) out[pos[u]] = jx[u];
+                if (g4 == 0) out[K - 1] = i;
             }
-        }
-        if (g4 == 0 && valid[sb] && (!flag || local)) {
-            sort_asc<KMAX>(sel);
-            int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
-#pragma unroll
-            for (int p = 0; p < KMAX; ++p)
-                if (p < K - 1) out[p] = sel[p];
-            out[K - 1] = i;
         }
         // near-ties that could not be settled here: mark the row;
         // route_refine_kernel re-selects it in fp64
