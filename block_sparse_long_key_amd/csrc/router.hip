@@ -223,6 +223,12 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 // in a descending list, and inserting a key x is one v_med3_f32 per slot,
 // a[p] = med3(a[p-1], a[p], x).  The key error is added to E in the
 // separation test.  The 4 lanes of a query merge their lists by shuffles.
+//
+// Near-ties (the separation test fails) are finished by two small kernels
+// that run right after: when the query's K best keys are provably the only
+// blocks that can still be selected, the row carries them to
+// route_cand_kernel (K fp64 re-scorings); otherwise the row is marked for
+// route_refine_kernel (fp64 re-scoring of every past block).
 __device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
 {
     return sa > sb || (sa == sb && ja < jb);
@@ -469,10 +475,13 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
         if (!__ballot(valid[sb] && flag)) continue;
 
         // near-tie: every block that can still be selected has a key >= a - 2E
-        // (its exact score is >= a - E).  Merge again keeping the top MW; if
-        // no key that high can have been dropped (by the merge or by a lane's
-        // own list), re-score those blocks in fp64 and select among them.
-        constexpr int MW = KMAX <= 8 ? 2 * KMAX : KMAX;
+        // (its exact score is >= a - E), and b is one of them.  If the
+        // (K+1)-th key of the query is below a - 2E and no lane dropped a key
+        // that high, the K best keys are exactly the candidates: hand them to
+        // route_refine_kernel in the row (slot p = -(j + 2)), which re-scores
+        // them in fp64 and drops the worst.  Otherwise mark the row for a
+        // full fp64 re-selection.
+        constexpr int MW = 2 * KMAX;
         float wk[MW];
 #pragma unroll
         for (int p = 0; p < MW; ++p) wk[p] = p < KMAX ? key[sb][p] : -INFINITY;
@@ -481,105 +490,113 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
         float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
         lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
         const float tlow = a - 2.0f * E;
-        const bool local = flag && wk[MW - 1] < tlow && lastmax < tlow;
-        if (__ballot(valid[sb] && local)) {
-            // lane g4 re-scores merged positions p = 4u + g4 that reach tlow
-            double ex[MW / 4];
-            int jx[MW / 4];
-            const uint16_t* qp = q + ((size_t)(st.cu[s] + tl[sb]) * H + h) * D;
+        float next = wk[0];
 #pragma unroll
-            for (int u = 0; u < MW / 4; ++u) {
-                float kp = wk[4 * u];
+        for (int p = 1; p < MW; ++p) next = (p == K) ? wk[p] : next;
+        const bool cands = next < tlow && lastmax < tlow;
+        if (g4 == 0 && valid[sb] && flag) {
+            int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
+            if (cands) {
 #pragma unroll
-                for (int e = 1; e < 4; ++e) kp = g4 == e ? wk[4 * u + e] : kp;
-                jx[u] = 0x7fffffff;
-                ex[u] = -INFINITY;
-                if (valid[sb] && local && kp >= tlow) {
-                    const int j = key_block(kp, lmask);
-                    const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
-                    double acc = 0.0;
-#pragma unroll
-                    for (int c8 = 0; c8 < D / 8; ++c8) {
-                        const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
-                        const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
-                        acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
-                    }
-                    ex[u] = acc;
-                    jx[u] = j;
-                }
-            }
-            // rank each own candidate against all MW of the query (score
-            // desc, block asc); the K-1 first are selected.  Candidates that
-            // were not re-scored rank after every re-scored one.
-            int rk[MW / 4];
-#pragma unroll
-            for (int u = 0; u < MW / 4; ++u) rk[u] = 0;
-#pragma unroll
-            for (int src = 0; src < 4; ++src)
-#pragma unroll
-                for (int u2 = 0; u2 < MW / 4; ++u2) {
-                    const double os = __shfl(ex[u2], l16 + 16 * src);
-                    const int oj = __shfl(jx[u2], l16 + 16 * src);
-#pragma unroll
-                    for (int u = 0; u < MW / 4; ++u) rk[u] += ranks_before64(os, oj, ex[u], jx[u]) ? 1 : 0;
-                }
-            // output slot of a selected block: selected blocks with a lower id
-            int pos[MW / 4];
-#pragma unroll
-            for (int u = 0; u < MW / 4; ++u) pos[u] = 0;
-#pragma unroll
-            for (int src = 0; src < 4; ++src)
-#pragma unroll
-                for (int u2 = 0; u2 < MW / 4; ++u2) {
-                    const int oj = __shfl(jx[u2], l16 + 16 * src);
-                    const int orank = __shfl(rk[u2], l16 + 16 * src);
-#pragma unroll
-                    for (int u = 0; u < MW / 4; ++u) pos[u] += (orank < K - 1 && oj < jx[u]) ? 1 : 0;
-                }
-            if (valid[sb] && local) {
-                int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
-#pragma unroll
-                for (int u = 0; u < MW / 4; ++u)
-                    if (rk[u] < K - 1) out[pos[u]] = jx[u];
-                if (g4 == 0) out[K - 1] = i;
+                for (int p = 0; p < KMAX; ++p)
+                    if (p < K) out[p] = -(key_block(wk[p], lmask) + 2);
+            } else {
+                out[0] = kPending;
             }
         }
-        // near-ties that could not be settled here: mark the row;
-        // route_refine_kernel re-selects it in fp64
-        if (g4 == 0 && valid[sb] && flag && !local)
-            idx[((size_t)(st.cu[s] + tl[sb]) * H + h) * K] = kPending;
     }
 }
 
 // ------------------------------------------------------------------------
-// Exact re-selection of the rows the MFMA kernel marked (near-ties): one
-// wave per query block.  Lanes score past blocks j = lane, lane + 64, ...
-// in fp64 (products of bf16 by fp32 are exact in fp64), two rows at a time
-// so two FMA chains overlap, and keep their best KMAX by (score desc, index
-// asc); a 6-level bitonic merge over the lanes ("top KMAX of two sorted
-// lists", c[p] = better(a[p], b[KMAX-1-p]) then a bitonic clean) leaves the
-// sorted global best KMAX in every lane.  Blocks without a marked row exit
-// after one look at their rows.
-__device__ __forceinline__ void cas_desc(double& s0, int& j0, double& s1, int& j1)
+// Exact re-selection of the near-tie rows the MFMA kernel left.  Scores are
+// fp64, summed sequentially over channels (products of bf16 by fp32 are
+// exact in fp64), ties to the lower block id.
+//
+// route_cand_kernel: rows holding their K candidates (slot p = -(j + 2)).
+// One wave per query block; the candidate rows of 64 consecutive rows are
+// taken 64/KMAX at a time, one lane per (row, candidate): the lane re-scores
+// its candidate, ranks it against the row's others by shuffles, and the
+// K-1 best are written in ascending block order, the own block last.
+template <int D, int BLK, int KMAX>
+__global__ __launch_bounds__(64, 5) void route_cand_kernel(SegTable st, const uint16_t* __restrict__ q,
+                                                        const float* __restrict__ cent,
+                                                        int32_t* __restrict__ idx)
 {
-    // afterwards (s0, j0) ranks before (s1, j1)
-    if (ranks_before64(s1, j1, s0, j0)) {
-        const double ts = s0; s0 = s1; s1 = ts;
-        const int tj = j0; j0 = j1; j1 = tj;
+    constexpr int RPW = 64 / KMAX;               // rows per pass
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int H = st.H, K = st.K;
+    const int s = seq_of_block(st, g);
+    const int i = g - st.boff[s];
+    if (K == 1 || i <= K - 1) return;            // no scoring happened here
+    const int L = seq_len(st, s);
+    const int lane = threadIdx.x;
+    const int grp = lane / KMAX, p = lane % KMAX;
+    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
+    for (int r0 = 0; r0 < BLK; r0 += 64) {
+        const int tl = i * BLK + r0 + lane;
+        int32_t s0 = 0;
+        if (r0 + lane < BLK && tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
+        uint64_t cm = __ballot(s0 != kPending && s0 <= -2);
+        while (cm) {
+            // this group's row: the grp-th set bit of cm
+            uint64_t m = cm;
+            for (int t = 0; t < grp; ++t) m &= m - 1;
+            const int src = m ? __builtin_ctzll(m) : -1;
+            for (int t = 0; t < RPW; ++t) cm &= cm - 1;
+            double sc = -INFINITY;
+            int j = 0x7fffffff;
+            int32_t* row = nullptr;
+            if (src >= 0) row = idx + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * K;
+            if (src >= 0 && p < K) {
+                j = -row[p] - 2;
+                const uint16_t* qp = q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D;
+                const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
+                double acc = 0.0;
+#pragma unroll
+                for (int c8 = 0; c8 < D / 8; ++c8) {
+                    const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
+                    const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
+                    acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
+                    acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
+                    acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
+                    acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
+                    acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
+                    acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
+                    acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
+                    acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
+                }
+                sc = acc;
+            }
+            // rank against the row's candidates; the last-ranked is dropped
+            int rank = 0, pos = 0;
+#pragma unroll
+            for (int e = 0; e < KMAX; ++e) {
+                const double os = __shfl(sc, grp * KMAX + e);
+                const int oj = __shfl(j, grp * KMAX + e);
+                rank += ranks_before64(os, oj, sc, j) ? 1 : 0;
+            }
+            const bool keep = src >= 0 && p < K && rank < K - 1;
+#pragma unroll
+            for (int e = 0; e < KMAX; ++e) {
+                const int oj = __shfl(j, grp * KMAX + e);
+                const int ok = __shfl(keep ? 1 : 0, grp * KMAX + e);
+                pos += (ok && oj < j) ? 1 : 0;
+            }
+            if (keep) row[pos] = j;
+            if (src >= 0 && p == 0) row[K - 1] = i;
+        }
     }
 }
 
+// route_refine_kernel: marked rows (slot 0 = kPending), rare.  One wave per
+// query block; for a marked row, lanes score past blocks j = lane,
+// lane + 64, ... and keep their best KMAX by (score desc, index asc) in a
+// sorted list; K-1 rounds of a wave-wide argmax over the list heads then
+// give the selection in rank order.
 template <int D, int BLK, int KMAX>
-__global__ __launch_bounds__(64) void route_refine_kernel(SegTable st, const uint16_t* __restrict__ q,
-                                                          const float* __restrict__ cent,
-                                                          int32_t* __restrict__ idx)
+__global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_refine_kernel(SegTable st, const uint16_t* __restrict__ q,
+                                                             const float* __restrict__ cent,
+                                                             int32_t* __restrict__ idx)
 {
     __shared__ __align__(16) float qstage[D];
     const int g = blockIdx.x, h = blockIdx.y;
@@ -607,54 +624,42 @@ __global__ __launch_bounds__(64) void route_refine_kernel(SegTable st, const uin
 #pragma unroll
             for (int p = 0; p < KMAX; ++p) { sc[p] = -INFINITY; jx[p] = 0x7fffffff; }
             const float4* qs = (const float4*)qstage;
-            for (int j = lane; j < i; j += 128) {
-                const int j2 = j + 64;
-                const bool two = j2 < i;
-                const float4* cp0 = (const float4*)(cbase + (size_t)j * H * D);
-                const float4* cp1 = (const float4*)(cbase + (size_t)(two ? j2 : j) * H * D);
-                double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-                for (int c8 = 0; c8 < D / 4; c8 += 4) {
-                    float4 u0[4], u1[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) { u0[u] = cp0[c8 + u]; u1[u] = cp1[c8 + u]; }
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const float4 qv = qs[c8 + u];
-                        a0 = __builtin_fma((double)qv.x, (double)u0[u].x, a0);
-                        a1 = __builtin_fma((double)qv.x, (double)u1[u].x, a1);
-                        a0 = __builtin_fma((double)qv.y, (double)u0[u].y, a0);
-                        a1 = __builtin_fma((double)qv.y, (double)u1[u].y, a1);
-                        a0 = __builtin_fma((double)qv.z, (double)u0[u].z, a0);
-                        a1 = __builtin_fma((double)qv.z, (double)u1[u].z, a1);
-                        a0 = __builtin_fma((double)qv.w, (double)u0[u].w, a0);
-                        a1 = __builtin_fma((double)qv.w, (double)u1[u].w, a1);
-                    }
+            for (int j = lane; j < i; j += 64) {
+                const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
+                double acc = 0.0;
+#pragma unroll 4
+                for (int c4 = 0; c4 < D / 4; ++c4) {
+                    const float4 cv = cp[c4], qv = qs[c4];
+                    acc = __builtin_fma((double)qv.x, (double)cv.x, acc);
+                    acc = __builtin_fma((double)qv.y, (double)cv.y, acc);
+                    acc = __builtin_fma((double)qv.z, (double)cv.z, acc);
+                    acc = __builtin_fma((double)qv.w, (double)cv.w, acc);
                 }
-                if (a0 > sc[KMAX - 1]) insert_tail<KMAX>(sc, jx, a0, j);
-                if (two && a1 > sc[KMAX - 1]) insert_tail<KMAX>(sc, jx, a1, j2);
+                // j grows, so an equal score stays behind the listed ones
+                if (acc > sc[KMAX - 1]) insert_tail<KMAX>(sc, jx, acc, j);
             }
-#pragma unroll
-            for (int m = 1; m < 64; m <<= 1) {
-                double os[KMAX];
-                int oj[KMAX];
-#pragma unroll
-                for (int p = 0; p < KMAX; ++p) { os[p] = __shfl_xor(sc[p], m); oj[p] = __shfl_xor(jx[p], m); }
-#pragma unroll
-                for (int p = 0; p < KMAX; ++p)
-                    if (ranks_before64(os[KMAX - 1 - p], oj[KMAX - 1 - p], sc[p], jx[p])) {
-                        sc[p] = os[KMAX - 1 - p];
-                        jx[p] = oj[KMAX - 1 - p];
-                    }
-#pragma unroll
-                for (int st2 = KMAX / 2; st2 >= 1; st2 >>= 1)
-#pragma unroll
-                    for (int p = 0; p < KMAX; ++p)
-                        if ((p & st2) == 0) cas_desc(sc[p], jx[p], sc[p + st2], jx[p + st2]);
-            }
+            int head = 0;
             int rsel[KMAX];
 #pragma unroll
-            for (int p = 0; p < KMAX; ++p) rsel[p] = p < K - 1 ? jx[p] : 0x7fffffff;
+            for (int p = 0; p < KMAX; ++p) rsel[p] = 0x7fffffff;
+            for (int r = 0; r < K - 1; ++r) {
+                double bs = -INFINITY;
+                int bj = 0x7fffffff;
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if (p == head) { bs = sc[p]; bj = jx[p]; }
+                const int myj = bj;
+#pragma unroll
+                for (int m = 1; m < 64; m <<= 1) {
+                    const double os = __shfl_xor(bs, m);
+                    const int oj = __shfl_xor(bj, m);
+                    if (ranks_before64(os, oj, bs, bj)) { bs = os; bj = oj; }
+                }
+                head += (myj == bj) ? 1 : 0;
+#pragma unroll
+                for (int p = 0; p < KMAX; ++p)
+                    if (p == r) rsel[p] = bj;
+            }
             sort_asc<KMAX>(rsel);
             if (lane == 0) {
                 int32_t* out = idx + ((size_t)(st.cu[s] + tq) * H + h) * K;
@@ -697,12 +702,15 @@ hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_
     const uint16_t* qq = (const uint16_t*)q;
     if (K <= 8) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
         hipLaunchKernelGGL((route_refine_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     } else if (K <= 16) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
         hipLaunchKernelGGL((route_refine_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     } else {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
         hipLaunchKernelGGL((route_refine_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     }
     return hipGetLastError();
