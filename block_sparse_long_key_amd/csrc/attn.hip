@@ -62,8 +62,11 @@ __device__ __forceinline__ float wave_sum16(float x)
 template <typename T, int D, int BLK>
 struct Smem {
     static constexpr bool BF = sizeof(T) == 2;
-    static constexpr int KS = BF ? D + 8 : D + 4;      // K row stride (elements)
-    static constexpr int VS = BF ? BLK + 8 : BLK + 4;  // V^T row stride
+    // row strides (elements): the MFMA fragment reads of 8 lanes (b128, K)
+    // or 16 lanes (b64, V^T) then hit distinct LDS banks -- K rows step 4
+    // banks, V^T rows 2 banks
+    static constexpr int KS = BF ? D + 8 : D + 4;      // K row stride
+    static constexpr int VS = BLK + 4;                 // V^T row stride
     T k[BLK * KS];
     T vt[D * VS];
 };

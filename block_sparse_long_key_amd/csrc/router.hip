@@ -22,6 +22,8 @@
 // one query each) of one head; the centroids of the past blocks stream
 // through LDS in tiles of 32 and are read by all threads as broadcasts.
 // bf16 queries use the MFMA kernel below.
+#include <type_traits>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -218,8 +220,11 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 // hi / lo rows.  S^T = C Q^T puts 4 blocks x 1 query in each lane.
 //
 // Selection without branches: a score s of block j becomes a float key whose
-// low LB mantissa bits hold j (inverted for s >= 0 so that the lower block
-// wins ties), |key - s| <= 2^(LB-23) |s|.  A lane keeps its KMAX best keys
+// low LB mantissa bits hold j, |key - s| <= 2^(LB-23) |s|.  Keys are unique
+// and decode back to their block; how they order equal scores does not
+// matter, since two keys within 2E of each other at the selection boundary
+// send the row to the exact fp64 path, and inside the selection order is
+// irrelevant (the output is sorted by block).  A lane keeps its KMAX best keys
 // in a descending list, and inserting a key x is one v_med3_f32 per slot,
 // a[p] = med3(a[p-1], a[p], x).  The key error is added to E in the
 // separation test.  The 4 lanes of a query merge their lists by shuffles.
@@ -254,9 +259,7 @@ __device__ __forceinline__ void insert_tail(F (&sc)[KMAX], int (&ix)[KMAX], F sv
 // block id carried in the low bits of a selection key
 __device__ __forceinline__ int key_block(float k, uint32_t lmask)
 {
-    const uint32_t bits = __float_as_uint(k);
-    const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
-    return (int)((bits ^ (lmask & ~neg)) & lmask);
+    return (int)(__float_as_uint(k) & lmask);
 }
 
 // Sorted (descending) top-N merge of the lists of lanes l, l^16, l^32, l^48.
@@ -363,6 +366,55 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
     const float kdel = ldexpf(1.0f, LB - 23) * 1.01f;
     float cmax2 = 0.f;                      // max |c|^2 over the past blocks
 
+    // score one group of 16 blocks (LDS rows 16*bt..) against both sub-tiles
+    // and insert the keys.  In the partial group, blocks j >= i get the
+    // lowest finite score, below every real key (-inf would turn into a NaN
+    // once j is written into its mantissa); that is a select, not a branch,
+    // so every MFMA result is first read in the block that produced it.
+    auto group = [&](int bt, int jb, auto partial) {
+        u16x8_t ah[NKS], al[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            ah[ks] = *(const u16x8_t*)(chi + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
+            al[ks] = *(const u16x8_t*)(clo + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
+        }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah[ks]),
+                                                              __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
+                                                              acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[ks]),
+                                                              __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
+                                                              acc, 0, 0, 0);
+            }
+            // lane holds blocks jb + 4*g4 + r for query l16 of sub-tile sb
+            if constexpr (decltype(partial)::value) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
+            }
+            const float thr = key[sb][KMAX - 1];
+            const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+            // a key exceeds its score by at most 2^(LB-23)|s|: skip the
+            // group only when no key can reach the list
+            if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    // key: the score with its low LB mantissa bits replaced by j
+                    const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
+                    const float x = __uint_as_float((__float_as_uint(acc[r]) & ~lmask) | j);
+#pragma unroll
+                    for (int p = KMAX - 1; p >= 1; --p)
+                        key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
+                    key[sb][0] = fmaxf(key[sb][0], x);
+                }
+            }
+        }
+    };
+
     for (int j0 = 0; j0 < i; j0 += TB) {
         __syncthreads();
         // stage the tile: hi / lo bf16 rows, and the row norms
@@ -384,51 +436,14 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
         __syncthreads();
         for (int bt = 0; bt < TB / 16; ++bt) {
             const int jb = j0 + 16 * bt;
-            if (jb >= i) break;
-            u16x8_t ah[NKS], al[NKS];
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) {
-                ah[ks] = *(const u16x8_t*)(chi + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
-                al[ks] = *(const u16x8_t*)(clo + (16 * bt + l16) * CS + 32 * ks + 8 * g4);
-            }
-#pragma unroll
-            for (int sb = 0; sb < 2; ++sb) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ah[ks]),
-                                                                  __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
-                                                                  acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, al[ks]),
-                                                                  __builtin_bit_cast(bf16x8_t, qb[sb][ks]),
-                                                                  acc, 0, 0, 0);
-                }
-                // lane holds blocks jb + 4*g4 + r for query l16 of sub-tile sb
-                const float thr = key[sb][KMAX - 1];
-                const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
-                // a key exceeds its score by at most 2^(LB-23)|s|: skip the
-                // group only when no key can reach the list
-                if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
-                    const bool full = jb + 16 <= i;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        // key: score with its low LB bits replaced by j (s < 0)
-                        // or lmask - j (s >= 0), so equal scores rank the lower j
-                        // first and every key decodes back to its block
-                        const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
-                        const uint32_t bits = __float_as_uint(acc[r]);
-                        const uint32_t neg = (uint32_t)((int32_t)bits >> 31);
-                        const uint32_t low = j ^ (lmask & ~neg);
-                        float x = __uint_as_float((bits & ~lmask) | (low & lmask));
-                        if (!full && (int)j >= i) x = -INFINITY;
-#pragma unroll
-                        for (int p = KMAX - 1; p >= 1; --p)
-                            key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
-                        key[sb][0] = __builtin_amdgcn_fmed3f(key[sb][0], x, INFINITY);
-                    }
-                }
-            }
+            if (jb + 16 > i) break;                 // full groups here
+            group(bt, jb, std::false_type{});
         }
+    }
+    // the last, partial group of 16 blocks is still in LDS
+    if (i & 15) {
+        const int jb = i & ~15;
+        group((jb % TB) / 16, jb, std::true_type{});
     }
     // max centroid norm over the workgroup
 #pragma unroll
