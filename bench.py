@@ -193,6 +193,7 @@ def main():
     routed_ms = stage_ms["routed_attn"]
     routed_tflops = fl["routed"] / (routed_ms * 1e-3) / 1e12
     pairs = workloads.routed_pairs(spec)
+    traffic = _traffic(pairs) if args.config == "H" else None
 
     out = {
         "metric": METRIC,
@@ -214,6 +215,9 @@ def main():
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()},
         "event_ms_per_step": round(sum(ms_steps) / len(ms_steps), 4),
+        "event_ms_median": round(sorted(ms_steps)[len(ms_steps) // 2], 4),
+        "event_ms_min": round(min(ms_steps), 4),
+        "event_ms_max": round(max(ms_steps), 4),
         "roofline": {
             "kernel": "routed_attn_kernel (moba_attn_routed)",
             "bound": "mfma",
@@ -221,9 +225,13 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(routed_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": _traffic(pairs),
+            "traffic": traffic,
             "algorithmic_flops_per_launch": fl["routed"],
             "avg_launch_ms": round(routed_ms, 4),
+            # the kernel is bound by its HBM traffic in practice: the same
+            # bytes over the same time
+            "traffic_GBps": (round(traffic / (routed_ms * 1e-3) / 1e9, 1)
+                             if traffic else None),
         },
     }
     if not args.no_cpu_baseline and spec.conv_width == 0:

@@ -256,6 +256,19 @@ __device__ __forceinline__ void insert_tail(F (&sc)[KMAX], int (&ix)[KMAX], F sv
     if (sc[0] < sv) { sc[0] = sv; ix[0] = j; }
 }
 
+// max / min of non-NaN floats as one v_med3_f32 each: med3(a, b, +inf) is
+// max(a, b).  The infinity comes from a register the compiler cannot see
+// through; with a literal it rewrites the med3 as fmaxf, which first
+// canonicalises both operands (two more instructions).
+__device__ __forceinline__ float opaque_inf()
+{
+    float r;
+    asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(r));
+    return r;
+}
+__device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
+__device__ __forceinline__ float fmin2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, -inf); }
+
 // block id carried in the low bits of a selection key
 __device__ __forceinline__ int key_block(float k, uint32_t lmask)
 {
@@ -267,20 +280,21 @@ __device__ __forceinline__ int key_block(float k, uint32_t lmask)
 template <int N, int NIN>
 __device__ __forceinline__ void merge_lanes(float (&x)[N])
 {
+    const float inf = opaque_inf();
 #pragma unroll
     for (int m = 16; m <= 32; m <<= 1) {
         float y[N];
 #pragma unroll
         for (int p = 0; p < N; ++p) y[p] = (m == 16 && p >= NIN) ? -INFINITY : __shfl_xor(x[p], m);
 #pragma unroll
-        for (int p = 0; p < N; ++p) x[p] = fmaxf(x[p], y[N - 1 - p]);
+        for (int p = 0; p < N; ++p) x[p] = fmax2(x[p], y[N - 1 - p], inf);
 #pragma unroll
         for (int st2 = N / 2; st2 >= 1; st2 >>= 1)
 #pragma unroll
             for (int p = 0; p < N; ++p)
                 if ((p & st2) == 0) {
-                    const float hi = fmaxf(x[p], x[p + st2]);
-                    const float lo = fminf(x[p], x[p + st2]);
+                    const float hi = fmax2(x[p], x[p + st2], inf);
+                    const float lo = fmin2(x[p], x[p + st2], inf);
                     x[p] = hi;
                     x[p + st2] = lo;
                 }
@@ -371,6 +385,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
     // lowest finite score, below every real key (-inf would turn into a NaN
     // once j is written into its mantissa); that is a select, not a branch,
     // so every MFMA result is first read in the block that produced it.
+    const float pinf = opaque_inf();
     auto group = [&](int bt, int jb, auto partial) {
         u16x8_t ah[NKS], al[NKS];
 #pragma unroll
@@ -397,7 +412,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
                     acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
             }
             const float thr = key[sb][KMAX - 1];
-            const float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+            const float mx = fmax2(fmax2(acc[0], acc[1], pinf), fmax2(acc[2], acc[3], pinf), pinf);
             // a key exceeds its score by at most 2^(LB-23)|s|: skip the
             // group only when no key can reach the list
             if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
 #pragma unroll
                     for (int p = KMAX - 1; p >= 1; --p)
                         key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
-                    key[sb][0] = fmaxf(key[sb][0], x);
+                    key[sb][0] = fmax2(key[sb][0], x, pinf);
                 }
             }
         }
