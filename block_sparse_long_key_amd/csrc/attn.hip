@@ -568,7 +568,7 @@ __global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
         float M = own_lse[r];
         float wsum = 1.0f;
         // the query's K list positions (-1: nothing routed in that slot)
-        const int32_t* rrow = rev + qrow * K;
+        const int32_t* rrow = rev + ((size_t)h * st.cu[st.nseq] + t0 + i * BLK + r) * K;
         const int64_t eb = st.ebase[s] + (int64_t)h * L * K;
         const int kmerge = K > 1 ? K : 0;      // K == 1: no routed partials exist
         for (int p0 = 0; p0 < kmerge; p0 += PF) {

@@ -13,7 +13,9 @@
 //              <= 128 entries of one list) for the routed attention;
 //   scatter -- same grid as count: entries (token << 5 | slot) written at the
 //              chunk's positions with LDS cursors, and the reverse map
-//              (query, slot) -> list position (-1 where nothing is routed).
+//              (query, slot) -> list position (-1 where nothing is routed),
+//              stored head-major [H][tokens][K] so both its writer and its
+//              reader (one query block of one head) touch contiguous runs.
 // The own block is not listed (the own-block kernel handles it); -1 and
 // out-of-range ids are skipped.  Order inside a list is not deterministic,
 // which the routed attention does not depend on (each row of a tile is
@@ -153,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
     const int nent = (tl1 - tl0) * K;
     const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
-    int32_t* rv = rev + ((size_t)(t0 + tl0) * H + h) * K;
+    // reverse map is head-major, [H][tokens][K]: this chunk's records are
+    // one contiguous run, written in order
+    int32_t* rv = rev + ((size_t)h * st.cu[st.nseq] + t0 + tl0) * K;
     for (int e = threadIdx.x; e < nent; e += kThreads) {
         const int r = e / K, slot = e - r * K;
         const int j = src[(size_t)r * H * K + slot];
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
         }
         // every slot is written, so each query's K positions form one
         // contiguous, fully written record
-        rv[(size_t)r * H * K + slot] = p;
+        rv[e] = p;
     }
 }
 

@@ -116,7 +116,7 @@ struct WsLayout {
     size_t cmat_off, cmat_bytes;     // int32 count / position matrix
     size_t items_off, items_bytes;   // Item[total_items]
     size_t ent_off, ent_bytes;       // uint32 entries (t << 5 | slot), list order
-    size_t rev_off, rev_bytes;       // int32 [tokens][H][K]: list position of (t, slot), -1 if none
+    size_t rev_off, rev_bytes;       // int32 [H][tokens][K]: list position of (t, slot), -1 if none
     size_t po_off, po_bytes;         // partial o rows, list order (I/O dtype, D per row)
     size_t pl_off, pl_bytes;         // partial lse, list order, fp32 (log2 units)
     size_t total;
