@@ -378,6 +378,14 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     __shared__ uint32_t sent[kItemRows];
     constexpr int NDT = D / 16;
     using W = Wave2<T, D, BLK>;
+    // bf16: each wave stages its 16 partial rows of a sub-tile in LDS and
+    // stores them as whole contiguous 16-byte chunks (64 lanes = 1 KB per
+    // instruction) instead of half rows; rows padded by 16 B so the 8-lane
+    // b128 writes hit distinct banks
+    constexpr bool STAGE = sizeof(T) == 2 && D == 64;      // (d = 128: LDS would halve occupancy)
+    constexpr int RB = D * (int)sizeof(T);            // partial row bytes
+    constexpr int RS = RB + 16;                       // staged row stride
+    __shared__ __align__(16) char ostage[STAGE ? 4 * 16 * RS : 16];
     // the hardware deals workgroups round-robin over the 8 XCDs; give each
     // XCD a contiguous run of items so one (sequence, head) stays in one L2
     const int64_t w = blockIdx.x;
@@ -460,16 +468,31 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
         wt.pv(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
-            if (!ok[sb]) continue;
+            const int row0 = base + 16 * sb;                  // first row of the sub-tile
+            if (row0 >= it.count) continue;                   // wave-uniform
             const float inv = 1.0f / wt.used_sum(sb, sum[sb]);
-            const size_t prow = (size_t)(e0 + base + 16 * sb + l16);
+            const size_t prow = (size_t)(e0 + row0 + l16);
             float x[NDT][4];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) x[dt][r4] = wt.o[sb][dt][r4] * inv;
-            store_lane_row<T, NDT>(po + prow * D + g4 * (D / 4), x);
-            if (g4 == 0) pl[prow] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+            if constexpr (STAGE) {
+                char* st_w = ostage + wave * 16 * RS;
+                store_lane_row<T, NDT>((T*)(st_w + l16 * RS) + g4 * (D / 4), x);
+                // (LDS accesses of one wave complete in order)
+                constexpr int CPR = RB / 16;                  // 16-byte chunks per row
+#pragma unroll
+                for (int n = 0; n < 16 * CPR / 64; ++n) {
+                    const int qc = 64 * n + lane, r = qc / CPR, c = qc % CPR;
+                    const u32x4_t w = *(const u32x4_t*)(st_w + r * RS + c * 16);
+                    if (row0 + r < it.count)
+                        *(u32x4_t*)((char*)po + (size_t)(e0 + row0 + r) * RB + c * 16) = w;
+                }
+            } else {
+                if (ok[sb]) store_lane_row<T, NDT>(po + prow * D + g4 * (D / 4), x);
+            }
+            if (ok[sb] && g4 == 0) pl[prow] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
         }
     }
 }
