@@ -230,10 +230,10 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 // separation test.  The 4 lanes of a query merge their lists by shuffles.
 //
 // Near-ties (the separation test fails) are finished by two small kernels
-// that run right after: when the query's K best keys are provably the only
-// blocks that can still be selected, the row carries them to
-// route_cand_kernel (K fp64 re-scorings); otherwise the row is marked for
-// route_refine_kernel (fp64 re-scoring of every past block).
+// that run right after (route_fix_kernel): when the query's K best keys are
+// provably the only blocks that can still be selected, the row carries them
+// (K fp64 re-scorings); otherwise the row is marked for an fp64 re-scoring
+// of every past block.
 __device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
 {
     return sa > sb || (sa == sb && ja < jb);
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
         // (its exact score is >= a - E), and b is one of them.  If the
         // (K+1)-th key of the query is below a - 2E and no lane dropped a key
         // that high, the K best keys are exactly the candidates: hand them to
-        // route_refine_kernel in the row (slot p = -(j + 2)), which re-scores
+        // route_fix_kernel in the row (slot p = -(j + 2)), which re-scores
         // them in fp64 and drops the worst.  Otherwise mark the row for a
         // full fp64 re-selection.
         constexpr int MW = 2 * KMAX;
@@ -542,30 +542,21 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
 // fp64, summed sequentially over channels (products of bf16 by fp32 are
 // exact in fp64), ties to the lower block id.
 //
-// route_cand_kernel: rows holding their K candidates (slot p = -(j + 2)).
-// One wave per query block; the candidate rows of 64 consecutive rows are
-// taken 64/KMAX at a time, one lane per (row, candidate): the lane re-scores
-// its candidate, ranks it against the row's others by shuffles, and the
-// K-1 best are written in ascending block order, the own block last.
+// Candidate rows (slot p = -(j + 2) for the K best keys): the candidate
+// rows of a 64-row chunk are taken 64/KMAX at a time, one lane per (row,
+// candidate): the lane re-scores its candidate, ranks it against the row's
+// others by shuffles, and the K-1 best are written in ascending block order,
+// the own block last.
 template <int D, int BLK, int KMAX>
-__global__ __launch_bounds__(64, 5) void route_cand_kernel(SegTable st, const uint16_t* __restrict__ q,
-                                                        const float* __restrict__ cent,
-                                                        int32_t* __restrict__ idx)
+__device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uint16_t* __restrict__ q,
+                                                   const float* cbase, int32_t* __restrict__ idx,
+                                                   int s, int i, int h, int r0, int32_t s0)
 {
     constexpr int RPW = 64 / KMAX;               // rows per pass
-    const int g = blockIdx.x, h = blockIdx.y;
     const int H = st.H, K = st.K;
-    const int s = seq_of_block(st, g);
-    const int i = g - st.boff[s];
-    if (K == 1 || i <= K - 1) return;            // no scoring happened here
-    const int L = seq_len(st, s);
     const int lane = threadIdx.x;
     const int grp = lane / KMAX, p = lane % KMAX;
-    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
-    for (int r0 = 0; r0 < BLK; r0 += 64) {
-        const int tl = i * BLK + r0 + lane;
-        int32_t s0 = 0;
-        if (r0 + lane < BLK && tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
+    {
         uint64_t cm = __ballot(s0 != kPending && s0 <= -2);
         while (cm) {
             // this group's row: the grp-th set bit of cm
@@ -618,29 +609,19 @@ __global__ __launch_bounds__(64, 5) void route_cand_kernel(SegTable st, const ui
     }
 }
 
-// route_refine_kernel: marked rows (slot 0 = kPending), rare.  One wave per
-// query block; for a marked row, lanes score past blocks j = lane,
+// Marked rows (slot 0 = kPending), rare: lanes score past blocks j = lane,
 // lane + 64, ... and keep their best KMAX by (score desc, index asc) in a
 // sorted list; K-1 rounds of a wave-wide argmax over the list heads then
 // give the selection in rank order.
 template <int D, int BLK, int KMAX>
-__global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_refine_kernel(SegTable st, const uint16_t* __restrict__ q,
-                                                             const float* __restrict__ cent,
-                                                             int32_t* __restrict__ idx)
+__device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16_t* __restrict__ q,
+                                                const float* cbase, int32_t* __restrict__ idx,
+                                                float* qstage, int s, int i, int h, int r0, int32_t s0)
 {
-    __shared__ __align__(16) float qstage[D];
-    const int g = blockIdx.x, h = blockIdx.y;
     const int H = st.H, K = st.K;
-    const int s = seq_of_block(st, g);
-    const int i = g - st.boff[s];
-    if (K == 1 || i <= K - 1) return;                  // no scoring happened here
-    const int L = seq_len(st, s);
     const int lane = threadIdx.x;
-    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
-    for (int r0 = 0; r0 < BLK; r0 += 64) {
-        const int tl = i * BLK + r0 + lane;
-        const bool mine = r0 + lane < BLK && tl < L &&
-                          idx[((size_t)(st.cu[s] + tl) * H + h) * K] == kPending;
+    {
+        const bool mine = s0 == kPending;
         uint64_t fm = __ballot(mine);
         while (fm) {
             const int src = __builtin_ctzll(fm);
@@ -703,6 +684,31 @@ __global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_refine_kernel(S
     }
 }
 
+// One wave per query block: one look at its rows, then the candidate rows
+// and the (rare) marked rows of each 64-row chunk.
+template <int D, int BLK, int KMAX>
+__global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_fix_kernel(SegTable st, const uint16_t* __restrict__ q,
+                                                                      const float* __restrict__ cent,
+                                                                      int32_t* __restrict__ idx)
+{
+    __shared__ __align__(16) float qstage[D];
+    const int g = blockIdx.x, h = blockIdx.y;
+    const int H = st.H, K = st.K;
+    const int s = seq_of_block(st, g);
+    const int i = g - st.boff[s];
+    if (K == 1 || i <= K - 1) return;                  // no scoring happened here
+    const int L = seq_len(st, s);
+    const int lane = threadIdx.x;
+    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
+    for (int r0 = 0; r0 < BLK; r0 += 64) {
+        const int tl = i * BLK + r0 + lane;
+        int32_t s0 = 0;
+        if (r0 + lane < BLK && tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
+        fix_candidate_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
+        fix_marked_rows<D, BLK, KMAX>(st, q, cbase, idx, qstage, s, i, h, r0, s0);
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_d(const Launch& L, const void* q, const float* cent, int32_t* idx)
 {
@@ -732,16 +738,13 @@ hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_
     const uint16_t* qq = (const uint16_t*)q;
     if (K <= 8) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     } else if (K <= 16) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     } else {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_cand_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_refine_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
     }
     return hipGetLastError();
 }
