@@ -27,6 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
+constexpr int kBatch = 16;        // idx words loaded ahead per thread
 
 __device__ __forceinline__ int32_t* cm_base(const SegTable& st, int32_t* cmat, int s, int h)
 {
@@ -49,11 +50,21 @@ __global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const 
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
     const int nent = (tl1 - tl0) * K;
     const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
-    for (int e = threadIdx.x; e < nent; e += kThreads) {
-        const int r = e / K, slot = e - r * K;
-        const int j = src[(size_t)r * H * K + slot];
-        const int i = (tl0 + r) / B;
-        if (j >= 0 && j < i) atomicAdd(&hist[j], 1);
+    // kBatch loads in flight per thread before their LDS updates
+    for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
+        int jv[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + u * kThreads;
+            const int r = e / K, slot = e - r * K;
+            jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + u * kThreads;
+            const int i = (tl0 + e / K) / B;
+            if (jv[u] >= 0 && jv[u] < i) atomicAdd(&hist[jv[u]], 1);
+        }
     }
     __syncthreads();
     int32_t* dst = cm_base(st, cmat, s, h) + (int64_t)cl * n;
@@ -158,18 +169,29 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     // reverse map is head-major, [H][tokens][K]: this chunk's records are
     // one contiguous run, written in order
     int32_t* rv = rev + ((size_t)h * st.cu[st.nseq] + t0 + tl0) * K;
-    for (int e = threadIdx.x; e < nent; e += kThreads) {
-        const int r = e / K, slot = e - r * K;
-        const int j = src[(size_t)r * H * K + slot];
-        const int i = (tl0 + r) / B;
-        int p = -1;
-        if (j >= 0 && j < i) {
-            p = atomicAdd(&cur[j], 1);
-            ent[p] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
+    for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
+        int jv[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + u * kThreads;
+            const int r = e / K, slot = e - r * K;
+            jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
         }
-        // every slot is written, so each query's K positions form one
-        // contiguous, fully written record
-        rv[e] = p;
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + u * kThreads;
+            if (e >= nent) break;
+            const int r = e / K, slot = e - r * K;
+            const int i = (tl0 + r) / B;
+            int p = -1;
+            if (jv[u] >= 0 && jv[u] < i) {
+                p = atomicAdd(&cur[jv[u]], 1);
+                ent[p] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
+            }
+            // every slot is written, so each query's K positions form one
+            // contiguous, fully written record
+            rv[e] = p;
+        }
     }
 }
 
