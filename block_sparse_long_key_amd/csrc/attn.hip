@@ -506,7 +506,7 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
 // map built by the index pass, its partial rows are gathered as coalesced
 // 16-byte chunks and merged with a running (max, sum) in log2 units.
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(2 * BLK) void diag_combine_kernel(
+__global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void diag_combine_kernel(
     SegTable st, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
     float sl2, T* __restrict__ o, float* __restrict__ lse)
