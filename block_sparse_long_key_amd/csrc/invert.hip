@@ -29,6 +29,19 @@ constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kBatch = 16;        // idx words loaded ahead per thread
 
+// entry e -> token row e / K by a multiply-high with ceil(2^32 / K), exact
+// while e * (ceil(2^32 / K) - 2^32 / K) < 2^32 / K, which holds for every
+// entry index of a chunk (e <= 16 * 128 * 32 = 2^16, K <= 32); token ->
+// block by a shift (B is a power of two)
+struct Div {
+    uint32_t m;
+    int lb;
+    __device__ __forceinline__ Div(int K, int B)
+        : m(0xffffffffu / (uint32_t)K + 1u), lb(31 - __builtin_clz((unsigned)B)) {}
+    __device__ __forceinline__ int row(int e) const { return (int)__umulhi((uint32_t)e, m); }
+    __device__ __forceinline__ int block(int t) const { return t >> lb; }
+};
+
 __device__ __forceinline__ int32_t* cm_base(const SegTable& st, int32_t* cmat, int s, int h)
 {
     return cmat + st.cmbase[s] + (int64_t)h * seq_nchunk(st, s) * seq_nblk(st, s);
@@ -50,19 +63,20 @@ __global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const 
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
     const int nent = (tl1 - tl0) * K;
     const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
+    const Div div(K, B);
     // kBatch loads in flight per thread before their LDS updates
     for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
         int jv[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * kThreads;
-            const int r = e / K, slot = e - r * K;
+            const int r = div.row(e), slot = e - r * K;
             jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * kThreads;
-            const int i = (tl0 + e / K) / B;
+            const int i = div.block(tl0 + div.row(e));
             if (jv[u] >= 0 && jv[u] < i) atomicAdd(&hist[jv[u]], 1);
         }
     }
@@ -169,20 +183,21 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     // reverse map is head-major, [H][tokens][K]: this chunk's records are
     // one contiguous run, written in order
     int32_t* rv = rev + ((size_t)h * st.cu[st.nseq] + t0 + tl0) * K;
+    const Div div(K, B);
     for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
         int jv[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * kThreads;
-            const int r = e / K, slot = e - r * K;
+            const int r = div.row(e), slot = e - r * K;
             jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * kThreads;
             if (e >= nent) break;
-            const int r = e / K, slot = e - r * K;
-            const int i = (tl0 + r) / B;
+            const int r = div.row(e), slot = e - r * K;
+            const int i = div.block(tl0 + r);
             int p = -1;
             if (jv[u] >= 0 && jv[u] < i) {
                 p = atomicAdd(&cur[jv[u]], 1);
