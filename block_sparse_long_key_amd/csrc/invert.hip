@@ -192,20 +192,22 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
             const int r = div.row(e), slot = e - r * K;
             jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
         }
+        // all LDS cursor bumps of the batch first, then the stores
+        int pv[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * kThreads;
-            if (e >= nent) break;
+            const int i = div.block(tl0 + div.row(e));
+            pv[u] = (e < nent && jv[u] >= 0 && jv[u] < i) ? atomicAdd(&cur[jv[u]], 1) : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int e = e0 + u * kThreads;
             const int r = div.row(e), slot = e - r * K;
-            const int i = div.block(tl0 + r);
-            int p = -1;
-            if (jv[u] >= 0 && jv[u] < i) {
-                p = atomicAdd(&cur[jv[u]], 1);
-                ent[p] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
-            }
+            if (pv[u] >= 0) ent[pv[u]] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
             // every slot is written, so each query's K positions form one
             // contiguous, fully written record
-            rv[e] = p;
+            if (e < nent) rv[e] = pv[u];
         }
     }
 }
