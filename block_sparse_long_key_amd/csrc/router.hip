@@ -269,6 +269,31 @@ __device__ __forceinline__ float opaque_inf()
 __device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
 __device__ __forceinline__ float fmin2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, -inf); }
 
+// sum over aligned groups of N = 16 or 32 lanes: DPP within each 16-lane row
+// (quad swaps, half-row and row mirrors), one cross-row shuffle for 32
+__device__ __forceinline__ float dpp_add(float x, int ctrl_sel)
+{
+    int y;
+    switch (ctrl_sel) {
+    case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // xor 1
+    case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // xor 2
+    case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // half-row mirror
+    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row mirror
+    }
+    return x + __int_as_float(y);
+}
+template <int N>
+__device__ __forceinline__ float row_sum(float x)
+{
+    static_assert(N == 16 || N == 32, "row_sum width");
+    x = dpp_add(x, 0);
+    x = dpp_add(x, 1);
+    x = dpp_add(x, 2);
+    x = dpp_add(x, 3);
+    if constexpr (N == 32) x += __shfl_xor(x, 16);
+    return x;
+}
+
 // block id carried in the low bits of a selection key
 __device__ __forceinline__ int key_block(float k, uint32_t lmask)
 {
@@ -302,8 +327,8 @@ __device__ __forceinline__ void merge_lanes(float (&x)[N])
 }
 
 template <int D, int BLK, int KMAX>
-// (d = 64 with short lists fits 96 VGPRs: ask for 5 waves per SIMD)
-__global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
+// (d = 64 with short lists fits 128 VGPRs: ask for 4 waves per SIMD)
+__global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
                                                              const float* __restrict__ cent,
                                                              int32_t* __restrict__ idx)
 {
@@ -432,21 +457,30 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 5 : 1)) void rou
 
     for (int j0 = 0; j0 < i; j0 += TB) {
         __syncthreads();
-        // stage the tile: hi / lo bf16 rows, and the row norms
-        for (int e = threadIdx.x; e < TB * (D / 4); e += NT) {
+        // stage the tile: hi / lo bf16 rows, and the row norms; the global
+        // loads of the whole tile are issued before any of them is used
+        constexpr int NIT = TB * (D / 4) / NT;
+        static_assert(TB * (D / 4) % NT == 0, "tile split");
+        float4 xs[NIT];
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = threadIdx.x + it * NT;
             const int r = e / (D / 4), c4 = e % (D / 4);
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 + r < i) x = *(const float4*)(cbase + (size_t)(j0 + r) * H * D + 4 * c4);
+            xs[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j0 + r < i) xs[it] = *(const float4*)(cbase + (size_t)(j0 + r) * H * D + 4 * c4);
+        }
+#pragma unroll
+        for (int it = 0; it < NIT; ++it) {
+            const int e = threadIdx.x + it * NT;
+            const int r = e / (D / 4), c4 = e % (D / 4);
+            const float4 x = xs[it];
             const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
             const uint32_t l01 = pack_bf16x2(x.x - bf16_lo(h01), x.y - bf16_hi(h01));
             const uint32_t l23 = pack_bf16x2(x.z - bf16_lo(h23), x.w - bf16_hi(h23));
             *(u32x2_t*)(chi + r * CS + 4 * c4) = u32x2_t{h01, h23};
             *(u32x2_t*)(clo + r * CS + 4 * c4) = u32x2_t{l01, l23};
-            float n2 = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
             // the D/4 consecutive threads of a row reduce its norm
-#pragma unroll
-            for (int m = 1; m < D / 4; m <<= 1) n2 += __shfl_xor(n2, m);
-            cmax2 = fmaxf(cmax2, n2);
+            cmax2 = fmaxf(cmax2, row_sum<D / 4>(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w));
         }
         __syncthreads();
         for (int bt = 0; bt < TB / 16; ++bt) {
