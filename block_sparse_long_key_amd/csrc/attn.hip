@@ -36,6 +36,9 @@
 namespace moba {
 namespace {
 
+// waves of a routed-attention workgroup (32 gathered rows each per tile)
+constexpr int kRoutedWaves = 4;
+
 __device__ __forceinline__ f32x4_t mfma_bf16(const u16x8_t& a, const u16x8_t& b, const f32x4_t& c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -369,7 +372,7 @@ __device__ __forceinline__ void store4(T* p, const float (&x)[4])
 // processed in tiles of 128 queries (4 waves x 2 sub-tiles x 16) while K_j
 // and V_j stay in LDS
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(256) void routed_attn_kernel(
+__global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     SegTable st, const Item* __restrict__ items, const uint32_t* __restrict__ entries,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float sl2,
     T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
@@ -385,7 +388,9 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     constexpr bool STAGE = sizeof(T) == 2 && D == 64;      // (d = 128: LDS would halve occupancy)
     constexpr int RB = D * (int)sizeof(T);            // partial row bytes
     constexpr int RS = RB + 16;                       // staged row stride
-    __shared__ __align__(16) char ostage[STAGE ? 4 * 16 * RS : 16];
+    __shared__ __align__(16) char ostage[STAGE ? kRoutedWaves * 16 * RS : 16];
+    constexpr int NT = 64 * kRoutedWaves;             // threads
+    constexpr int TR = 32 * kRoutedWaves;             // rows per tile
     // the hardware deals workgroups round-robin over the 8 XCDs; give each
     // XCD a contiguous run of items so one (sequence, head) stays in one L2
     const int64_t w = blockIdx.x;
@@ -407,7 +412,7 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
     // contiguous run of full rows
     const int64_t e0 = st.ebase[s] + (int64_t)h * L * K + it.begin;
     const uint32_t* ent = entries + e0;
-    for (int r = threadIdx.x; r < it.count; r += 256) sent[r] = ent[r];
+    for (int r = threadIdx.x; r < it.count; r += NT) sent[r] = ent[r];
 
     // gathered query fragments of the first tile are requested before the
     // K / V staging so the two overlap
@@ -440,10 +445,10 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
         }
     };
     if (base < it.count) fetch_q(base, qn, qfn, ent);
-    load_kv<T, D, BLK, 256>(sm, k, v, (size_t)(t0 + j * BLK) * H + h, H, BLK);
+    load_kv<T, D, BLK, NT>(sm, k, v, (size_t)(t0 + j * BLK) * H + h, H, BLK);
     __syncthreads();
 
-    for (; base < it.count; base += 128) {
+    for (; base < it.count; base += TR) {
         // current tile's fragments; the next tile's are requested now and
         // arrive while this one computes
         bool ok[2];
@@ -459,7 +464,7 @@ __global__ __launch_bounds__(256) void routed_attn_kernel(
                 for (int ks = 0; ks < W::QREG; ++ks) wt.qf[sb][ks] = qfn[sb][ks];
             }
         }
-        if (base + 128 < it.count) fetch_q(base + 128, qn, qfn, sent);
+        if (base + TR < it.count) fetch_q(base + TR, qn, qfn, sent);
         wt.scores(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
         float m2[2], sum[2];
 #pragma unroll
@@ -656,7 +661,7 @@ hipError_t routed_t(const Launch& L, const WsLayout& ws, char* wsp, const void* 
     if (nitems == 0) return hipSuccess;
     const int64_t per_xcd = (nitems + 7) / 8;
     const int64_t grid = per_xcd * 8;
-    hipLaunchKernelGGL((routed_attn_kernel<T, D, BLK>), dim3((unsigned)grid), dim3(256), 0, L.stream,
+    hipLaunchKernelGGL((routed_attn_kernel<T, D, BLK>), dim3((unsigned)grid), dim3(64 * kRoutedWaves), 0, L.stream,
                        L.st, (const Item*)(wsp + ws.items_off), (const uint32_t*)(wsp + ws.ent_off),
                        (const T*)q, (const T*)k, (const T*)v, sl2, (T*)(wsp + ws.po_off),
                        (float*)(wsp + ws.pl_off), nitems, per_xcd);

@@ -393,8 +393,12 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         qn2[sb] = acc;
     }
 
-    // per-lane key lists (descending, all KMAX slots live); the low LB
-    // mantissa bits of a key carry the block id j < i
+    // per-lane key lists (descending); the low LB mantissa bits of a key
+    // carry the block id j < i.  A lane keeps LL = KMAX - 1 keys (slot
+    // KMAX - 1 stays -inf): the query's top K is exact unless one lane holds
+    // more than LL of it, which the merge detects (a lane's last kept key
+    // above the merged K-th) and sends to the fp64 path.
+    constexpr int LL = KMAX - 1;
     float key[2][KMAX];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -436,7 +440,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                 for (int r = 0; r < 4; ++r)
                     acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
             }
-            const float thr = key[sb][KMAX - 1];
+            const float thr = key[sb][LL - 1];
             const float mx = fmax2(fmax2(acc[0], acc[1], pinf), fmax2(acc[2], acc[3], pinf), pinf);
             // a key exceeds its score by at most 2^(LB-23)|s|: skip the
             // group only when no key can reach the list
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                     const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
                     const float x = __uint_as_float((__float_as_uint(acc[r]) & ~lmask) | j);
 #pragma unroll
-                    for (int p = KMAX - 1; p >= 1; --p)
+                    for (int p = LL - 1; p >= 1; --p)
                         key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
                     key[sb][0] = fmax2(key[sb][0], x, pinf);
                 }
@@ -521,10 +525,16 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
             a = (p == K - 2) ? mk[p] : a;
             b = (p == K - 1) ? mk[p] : b;
         }
+        // a lane whose last kept key is above b may have dropped one of the
+        // top K: then nothing here is trusted (overflow -> fp64 path)
+        const float mylast = key[sb][LL - 1];
+        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
+        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
+        const bool overflow = lastmax > b;
         // keys are within 2^(LB-23)|s| of the MFMA scores
         const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
         const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
-        const bool flag = !(a - b > 2.0f * E);
+        const bool flag = overflow || !(a - b > 2.0f * E);
         if (g4 == 0 && valid[sb] && !flag) {
             int sel[KMAX];
 #pragma unroll
@@ -550,14 +560,11 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
 #pragma unroll
         for (int p = 0; p < MW; ++p) wk[p] = p < KMAX ? key[sb][p] : -INFINITY;
         merge_lanes<MW, KMAX>(wk);
-        const float mylast = key[sb][KMAX - 1];
-        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
-        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
         const float tlow = a - 2.0f * E;
         float next = wk[0];
 #pragma unroll
         for (int p = 1; p < MW; ++p) next = (p == K) ? wk[p] : next;
-        const bool cands = next < tlow && lastmax < tlow;
+        const bool cands = !overflow && next < tlow && lastmax < tlow;
         if (g4 == 0 && valid[sb] && flag) {
             int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
             if (cands) {

@@ -223,6 +223,31 @@ def test_route_exact_ties(period, seq, B, K):
     assert ndiff == 0
 
 
+def test_route_one_lane_holds_the_top_k():
+    """Blocks whose id mod 16 is below 4 score highest, so one of the four
+    lanes that share a query holds the whole top-k: more than the lane keeps,
+    which must be detected and re-selected exactly."""
+    H, d, B, K, seq = 2, 64, 64, 8, 4096
+    print(f"[lane overflow B{B} K{K}]", flush=True)
+    g = torch.Generator().manual_seed(77)
+    q = (torch.randn((seq, H, d), generator=g) * 0.1 + 1.0).to(torch.bfloat16)
+    k = torch.randn((seq, H, d), generator=g) * 0.1
+    blk = torch.arange(seq) // B
+    k += torch.where((blk % 16) < 4, 1.0, -1.0)[:, None, None]
+    k = k.to(torch.bfloat16)
+    cu = [0, seq]
+    cent = oracle.centroids(k, B, cu)
+    ref_idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    idx = moba().moba_route_topk(q.to(DEV), torch.from_numpy(cent).to(DEV), B, K, cu)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().reshape(ref_idx.shape)
+    # the construction does put all k-1 routed blocks of late rows in one
+    # lane (a lane scores the blocks j with the same (j mod 16) / 4)
+    late = ref_idx[B * 40:, :, :K - 1]
+    assert np.all((late % 16) < 4)
+    assert int(np.any(got != ref_idx, axis=-1).sum()) == 0
+
+
 @pytest.mark.parametrize("seqlens,H,d,B,K,dtype", [
     ([1000], 2, 64, 64, 4, "bf16"),           # ragged tail (1000 = 15*64 + 40)
     ([130, 1, 64, 300], 3, 64, 128, 8, "bf16"),  # short / single-token sequences
