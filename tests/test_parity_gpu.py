@@ -296,43 +296,49 @@ def test_scale_override_and_null_lse():
 
 
 # ------------------------------------------------- full size, sampled ----
-def test_headline_full_size_sampled():
-    """64K x 2 x 16 heads, d=64, B=128, top-8, bf16 (the benchmarked shape):
-    selection and output checked on a seeded sample of rows; invariants on
-    every row."""
-    s = workloads.spec("H")
+@pytest.mark.parametrize("name", ["H", "C3", "C4", "C5"])
+def test_full_size_sampled(name):
+    """Every workload at its full size (H: 64K x 2 x 16 heads, d=64, B=128,
+    top-8; C3 with key conv and the planted signal; C4 with B=64, top-16;
+    C5 varlen with d=128 and key conv): selection and output checked on a
+    seeded sample of rows; invariants on every row."""
+    s = workloads.spec(name)
     print(f"[full {s.name}] {s}", flush=True)
     x = workloads.make(s)
     cu = workloads.segments(s)
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
-    o, lse, idx, kk = moba().moba_fwd(q, k, v, s.block_size, s.top_k)
+    w = None if x["conv_w"] is None else x["conv_w"].to(DEV)
+    o, lse, idx, kk = moba().moba_fwd(q, k, v, s.block_size, s.top_k, conv_w=w,
+                                      cu_seqlens=x["cu_seqlens"])
     torch.cuda.synchronize()
+    H, K, B = s.heads, s.top_k, s.block_size
+    T = int(cu[-1])
     # invariants on every row (on the GPU)
-    T = s.batch * s.seq
-    gi = idx.reshape(T, s.heads, s.top_k)
-    tl = torch.arange(s.seq, device=DEV).repeat(s.batch)
-    own = (tl // s.block_size).to(torch.int32)[:, None]
+    gi = idx.reshape(T, H, K)
+    tl = torch.cat([torch.arange(cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]).to(DEV)
+    own = (tl // B).to(torch.int32)[:, None]
     valid = gi >= 0
     assert torch.all((gi == own[..., None]).any(-1))
-    assert torch.all(gi[valid.all(-1)][..., 1:] > gi[valid.all(-1)][..., :-1])
+    full = valid.all(-1)
+    assert torch.all(gi[full][..., 1:] > gi[full][..., :-1])
     assert torch.all(torch.where(valid, gi, torch.zeros_like(gi)) <= own[..., None])
-    nvalid = valid.sum(-1)
-    assert torch.all(nvalid == torch.clamp(own + 1, max=s.top_k))
-    # sampled rows against the oracle
+    assert torch.all(valid.sum(-1) == torch.clamp(own + 1, max=K))
+    # sampled rows against the oracle (which sees the same conv'd keys)
     g = np.random.default_rng(0)
     rows = np.unique(np.concatenate([
-        g.integers(0, T * s.heads, 1500),
-        np.arange(0, 16), T * s.heads - 1 - np.arange(0, 16)]))
-    cent = oracle.centroids(x["k"], s.block_size, cu)
-    ri, ga, gb, ex = oracle.route_rows(x["q"], cent, s.block_size, s.top_k, cu, rows)
-    gidx = idx.cpu().numpy().reshape(-1, s.top_k)
-    _check_idx(gidx[rows], ri, ga, gb, ex, "H full")
+        g.integers(0, T * H, 1500), np.arange(0, 16), T * H - 1 - np.arange(0, 16)]))
+    kc = x["k"]
+    if x["conv_w"] is not None:
+        kc = oracle.key_conv(x["k"], x["conv_w"], cu, mode=0, round_bf16=True)
+    cent = oracle.centroids(kc, B, cu)
+    ri, ga, gb, ex = oracle.route_rows(x["q"], cent, B, K, cu, rows)
+    gidx = idx.cpu().numpy().reshape(-1, K)
+    _check_idx(gidx[rows], ri, ga, gb, ex, f"{name} full")
     # the oracle attends with its own selection of the sampled rows
-    oidx = np.full((T * s.heads, s.top_k), -1, np.int32)
+    oidx = np.full((T * H, K), -1, np.int32)
     oidx[rows] = ri
-    ro, rl = oracle.attend_rows(x["q"], x["k"], x["v"], oidx.reshape(T, s.heads, s.top_k),
-                                s.block_size, s.top_k, cu, rows)
+    ro, rl = oracle.attend_rows(x["q"], kc, x["v"], oidx.reshape(T, H, K), B, K, cu, rows)
     same = np.all(gidx[rows] == ri, axis=-1)
     go = _np(o).reshape(-1, s.head_dim)[rows]
     gl = _np(lse).reshape(-1)[rows]
-    _check_o(go[same], gl[same], ro[same], rl[same], "bf16", rows=True, what="H full")
+    _check_o(go[same], gl[same], ro[same], rl[same], "bf16", rows=True, what=f"{name} full")
