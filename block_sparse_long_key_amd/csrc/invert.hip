@@ -5,7 +5,7 @@
 // varlen layout indexed by key block, which the gather-and-densify forward
 // consumes.  This is that step, written as a counting sort with no global
 // atomics:
-//   count   -- one workgroup per (sequence, head, chunk of 16 query blocks):
+//   count   -- one workgroup per (sequence, head, chunk of 32 query blocks):
 //              LDS histogram of the routed past blocks; row of the count
 //              matrix cm[chunk][j] for the lists j this chunk can reach;
 //   scan    -- one workgroup per (sequence, head): list totals, list offsets,
@@ -29,10 +29,11 @@ constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kBatch = 16;        // idx words loaded ahead per thread
 
-// entry e -> token row e / K by a multiply-high with ceil(2^32 / K), exact
-// while e * (ceil(2^32 / K) - 2^32 / K) < 2^32 / K, which holds for every
-// entry index of a chunk (e <= 16 * 128 * 32 = 2^16, K <= 32); token ->
-// block by a shift (B is a power of two)
+// entry e -> token row e / K by a multiply-high with M = ceil(2^32 / K):
+// e M / 2^32 exceeds e / K by less than e / 2^32, and the fractional part of
+// e / K is at most (K-1) / K, so the floor is exact for e < 2^32 / K (every
+// entry index of a chunk is below 2^18); token -> block by a shift (B is a
+// power of two)
 struct Div {
     uint32_t m;
     int lb;
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
     const int64_t ib = st.ibase[s] + (int64_t)h * seq_item_cap(st, s);
     const int64_t cap = seq_item_cap(st, s);
 
-    // list totals (chunk c reaches list j iff j < (c+1)*16)
+    // list totals (chunk c reaches list j iff j < (c+1)*kInvChunkBlocks)
     for (int j = threadIdx.x; j < n; j += kScanThreads) {
         int t = 0;
         for (int c = j / kInvChunkBlocks; c < nch; ++c) t += cm[(int64_t)c * n + j];

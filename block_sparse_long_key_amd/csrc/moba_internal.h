@@ -16,7 +16,7 @@ constexpr int kMaxSeqs = MOBA_MAX_SEQS;
 // most queries per routed-attention work item (looped in tiles of 128)
 constexpr int kItemRows = 2048;
 // query blocks per inversion chunk (one workgroup of the count/scatter passes)
-constexpr int kInvChunkBlocks = 16;
+constexpr int kInvChunkBlocks = 32;
 // largest number of blocks of one sequence (LDS histogram of the inversion)
 constexpr int kMaxBlocksPerSeq = 16384;
 
