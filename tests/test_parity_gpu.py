@@ -296,12 +296,12 @@ def test_scale_override_and_null_lse():
 
 
 # ------------------------------------------------- full size, sampled ----
-@pytest.mark.parametrize("name", ["H", "C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["H", "C3", "C4", "C5", "L"])
 def test_full_size_sampled(name):
     """Every workload at its full size (H: 64K x 2 x 16 heads, d=64, B=128,
     top-8; C3 with key conv and the planted signal; C4 with B=64, top-16;
-    C5 varlen with d=128 and key conv): selection and output checked on a
-    seeded sample of rows; invariants on every row."""
+    C5 varlen with d=128 and key conv; L: one 512K sequence): selection and
+    output checked on a seeded sample of rows; invariants on every row."""
     s = workloads.spec(name)
     print(f"[full {s.name}] {s}", flush=True)
     x = workloads.make(s)
