@@ -1,4 +1,5 @@
-"""CPU oracle of the MoBA forward pass (test infrastructure only).
+"""CPU oracle of the MoBA forward pass and of its attention backward
+(test infrastructure only).
 
 Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
 leg may import this package.  The product path (the HIP library and its
@@ -56,6 +57,9 @@ def _load():
         lib.moba_oracle_total_blocks.argtypes = [_P, _I, _I]
         lib.moba_oracle_route_rows.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P]
         lib.moba_oracle_attend_rows.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _I, _P, _P]
+        lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
+                                               _P, _P, _P, _P, _P, _I]
+        lib.moba_oracle_attend_bwd.restype = _I
         lib.moba_oracle_route_rows.restype = _I
         lib.moba_oracle_attend_rows.restype = _I
         for f in (lib.moba_oracle_key_conv, lib.moba_oracle_centroids,
@@ -220,3 +224,33 @@ def attend_rows(q, k, v, idx, B: int, K: int, cu, rows, scale: float = 0.0):
                                          len(rows), _ptr(o), _ptr(lse))
     assert rc == 0
     return o[rows], lse[rows]
+
+
+def attend_bwd(q, k, v, idx, dout, B: int, K: int, cu, scale: float = 0.0,
+               qsel=None, kbsel=None, nthreads: Optional[int] = None):
+    """Gradients of the attention output for the fixed selection idx.
+
+    dout is dL/dO ([T, H, d]).  Returns (dq, dk, dv), f64 [T, H, d].
+    qsel (bool [T, H]) limits the rows whose dq is computed, kbsel (bool
+    [total_blocks, H]) the key blocks whose dk / dv are computed; entries
+    outside them are NaN.
+    """
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    T, H, d = q.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, H, K)
+    c = _cu(cu)
+    dq = np.full((T, H, d), np.nan)
+    dk = np.full((T, H, d), np.nan)
+    dv = np.full((T, H, d), np.nan)
+    qs = None if qsel is None else np.ascontiguousarray(np.asarray(qsel, dtype=np.uint8).reshape(T, H))
+    ks = None if kbsel is None else np.ascontiguousarray(np.asarray(kbsel, dtype=np.uint8))
+    if ks is not None:
+        assert ks.shape == (total_blocks(cu, B), H)
+    rc = _load().moba_oracle_attend_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(dout),
+                                        H, d, B, K, _ptr(c), len(c) - 1, float(scale),
+                                        None if qs is None else _ptr(qs),
+                                        None if ks is None else _ptr(ks),
+                                        _ptr(dq), _ptr(dk), _ptr(dv),
+                                        nthreads or default_threads())
+    assert rc == 0
+    return dq, dk, dv

@@ -1,6 +1,7 @@
 /*
  * moba_oracle.c -- plain, slow, obviously-correct CPU reference of the
- * Mixture of Block Attention (MoBA) forward pass.
+ * Mixture of Block Attention (MoBA) forward pass and of the gradients of its
+ * attention step.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file; only the tests, the package's smoke check and the
@@ -38,7 +39,9 @@
  * oracle tests): conv against a library conv1d in fp64 and special cases,
  * centroids against a library mean, routing against brute-force argsort and
  * hand-computed integer cases, attention against library SDPA (dense and
- * explicit-mask) and closed-form special cases.
+ * explicit-mask) and closed-form special cases, the attention backward
+ * against the library's autograd of explicit-mask SDPA, central differences
+ * of the forward, and closed-form invariants.
  */
 #include <math.h>
 #include <pthread.h>
@@ -476,5 +479,135 @@ int moba_oracle_attend_rows(const float *q, const float *k, const float *v,
     }
     free(z);
     free(keys);
+    return 0;
+}
+
+/* =====================================================================
+ * Backward of step 5: gradients of O with respect to q, k and v for a
+ * fixed selection (summary page, "Backward Pass: Ricalcolo (Algoritmo 5)":
+ * FlashAttention-2 style, the scores and probabilities are recomputed from
+ * q and k instead of being stored).  The gradients are those of softmax
+ * attention over the row's key set (listed past blocks + own block
+ * causally, exactly as in step 5), with dO the gradient of the output:
+ *   z_tu  = scale q_t . k_u,   P_tu = exp(z_tu - LSE_t)
+ *   dv_u += P_tu dO_t
+ *   dP_tu = dO_t . v_u
+ *   D_t   = sum_u P_tu dP_tu
+ *   dS_tu = P_tu (dP_tu - D_t)
+ *   dq_t  = scale sum_u dS_tu k_u
+ *   dk_u += scale dS_tu q_t
+ * The block selection is piecewise constant in q and k, so nothing flows
+ * through the router (its gradient is zero almost everywhere).
+ * Subsets, for sampled checks at sizes where the whole backward is too
+ * slow: qsel (uint8 per row t*H+h, NULL = all) picks the rows whose dq is
+ * written; kbsel (uint8 per (global block, head), NULL = all) picks the key
+ * blocks whose dk / dv are written.  Unpicked outputs are left untouched;
+ * picked dk / dv are overwritten with the sum over every row.
+ * ===================================================================== */
+typedef struct {
+    const float *q, *k, *v, *dout;
+    const int *idx;
+    const unsigned char *qsel, *kbsel;
+    double *dq, *dk, *dv;
+    const int *cu, *boff;
+    int H, d, B, K;
+    double scale;
+} bwd_ctx;
+
+static void bwd_job(void *vctx, int job)
+{
+    bwd_ctx *c = (bwd_ctx *)vctx;
+    int s = job / c->H, h = job % c->H;
+    int t0 = c->cu[s], L = c->cu[s + 1] - t0;
+    int d = c->d, H = c->H;
+    int maxkeys = c->K * c->B + c->B;
+    double *z = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int *keys = (int *)malloc(sizeof(int) * (size_t)maxkeys);
+    /* the picked key rows of this (sequence, head) start from zero */
+    for (int u = 0; u < L; ++u) {
+        int g = c->boff[s] + u / c->B;
+        if (c->kbsel && !c->kbsel[(size_t)g * H + h]) continue;
+        double *dkr = c->dk + ((size_t)(t0 + u) * H + h) * d;
+        double *dvr = c->dv + ((size_t)(t0 + u) * H + h) * d;
+        for (int ch = 0; ch < d; ++ch) { dkr[ch] = 0.0; dvr[ch] = 0.0; }
+    }
+    for (int tl = 0; tl < L; ++tl) {
+        size_t t = (size_t)(t0 + tl);
+        int i = tl / c->B;
+        const int *row = c->idx + (t * H + h) * c->K;
+        int nk = 0;
+        for (int p = 0; p < c->K; ++p) {
+            int j = row[p];
+            if (j < 0 || j >= i) continue;
+            for (int u = j * c->B; u < (j + 1) * c->B && u < L; ++u) keys[nk++] = u;
+        }
+        for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
+        /* is this row needed at all? */
+        int want_q = !c->qsel || c->qsel[t * H + h];
+        int want_k = 0;
+        for (int e = 0; e < nk && !want_k; ++e)
+            want_k = !c->kbsel || c->kbsel[(size_t)(c->boff[s] + keys[e] / c->B) * H + h];
+        if (!want_q && !want_k) continue;
+        const float *qv = c->q + (t * H + h) * d;
+        const float *dov = c->dout + (t * H + h) * d;
+        double M = -INFINITY;
+        for (int e = 0; e < nk; ++e) {
+            const float *kv = c->k + ((size_t)(t0 + keys[e]) * H + h) * d;
+            double acc = 0.0;
+            for (int ch = 0; ch < d; ++ch) acc = acc + (double)qv[ch] * (double)kv[ch];
+            z[e] = c->scale * acc;
+            if (z[e] > M) M = z[e];
+        }
+        double l = 0.0;
+        for (int e = 0; e < nk; ++e) l += exp(z[e] - M);
+        double lse = M + log(l);
+        double Dt = 0.0;
+        for (int e = 0; e < nk; ++e) {
+            const float *vv = c->v + ((size_t)(t0 + keys[e]) * H + h) * d;
+            double acc = 0.0;
+            for (int ch = 0; ch < d; ++ch) acc = acc + (double)dov[ch] * (double)vv[ch];
+            dp[e] = acc;
+            z[e] = exp(z[e] - lse);              /* z now holds P */
+            Dt += z[e] * dp[e];
+        }
+        double *dqr = want_q ? c->dq + (t * H + h) * d : NULL;
+        if (dqr)
+            for (int ch = 0; ch < d; ++ch) dqr[ch] = 0.0;
+        for (int e = 0; e < nk; ++e) {
+            double P = z[e];
+            double dS = P * (dp[e] - Dt);
+            size_t ku = (size_t)(t0 + keys[e]) * H + h;
+            if (dqr) {
+                const float *kv = c->k + ku * d;
+                for (int ch = 0; ch < d; ++ch) dqr[ch] += c->scale * dS * (double)kv[ch];
+            }
+            if (!c->kbsel || c->kbsel[(size_t)(c->boff[s] + keys[e] / c->B) * H + h]) {
+                double *dkr = c->dk + ku * d;
+                double *dvr = c->dv + ku * d;
+                for (int ch = 0; ch < d; ++ch) {
+                    dkr[ch] += c->scale * dS * (double)qv[ch];
+                    dvr[ch] += P * (double)dov[ch];
+                }
+            }
+        }
+    }
+    free(z);
+    free(dp);
+    free(keys);
+}
+
+int moba_oracle_attend_bwd(const float *q, const float *k, const float *v,
+                           const int *idx, const float *dout, int H, int d, int B,
+                           int K, const int *cu, int nseq, double scale,
+                           const unsigned char *qsel, const unsigned char *kbsel,
+                           double *dq, double *dk, double *dv, int nthreads)
+{
+    if (B < 1 || K < 1) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    int *boff = block_offsets(cu, nseq, B);
+    bwd_ctx c = {q, k, v, dout, idx, qsel, kbsel, dq, dk, dv, cu, boff, H, d, B, K, scale};
+    run_jobs(bwd_job, &c, nseq * H, nthreads);
+    free(boff);
     return 0;
 }

@@ -397,3 +397,105 @@ def test_row_subsets_equal_full_runs():
     ro, rl = oracle.attend_rows(q, k, v, idx, B, K, cu, rows)
     assert np.array_equal(ro, o.reshape(-1, d)[rows])
     assert np.array_equal(rl, lse.reshape(-1)[rows])
+
+
+# ------------------------------------------------------------ backward ----
+# "Backward Pass: Ricalcolo (Algoritmo 5)": gradients of the attention over
+# the selected blocks, for a fixed selection.  Pinned against the library's
+# own autograd of masked attention, central differences of the (separately
+# pinned) forward, and closed-form invariants.
+def _bwd_case(seed, T=40, H=2, d=8, cu=(0, 17, 40)):
+    q, k, v, do = (_bf16(_rand((T, H, d), seed + i)) for i in range(4))
+    return q, k, v, do, list(cu)
+
+
+@pytest.mark.parametrize("B,K", [(4, 3), (8, 2), (4, 1), (8, 5)])
+def test_attend_bwd_matches_autograd_of_masked_sdpa(B, K):
+    q, k, v, do, cu = _bwd_case(40)
+    T, H, d = q.shape
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    scale = 0.41
+    dq, dk, dv = oracle.attend_bwd(q, k, v, idx, do, B, K, cu, scale=scale)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        L = b - a
+        for h in range(H):
+            m = torch.from_numpy(_mask_from_idx([idx[t, h].tolist() for t in range(a, b)], L, B))
+            tq, tk, tv = (torch.from_numpy(x[a:b, h]).double().requires_grad_() for x in (q, k, v))
+            o = F.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=m[None],
+                                               scale=scale)[0]
+            o.backward(torch.from_numpy(do[a:b, h]).double())
+            for ours, ref in ((dq, tq), (dk, tk), (dv, tv)):
+                assert np.allclose(ours[a:b, h], ref.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_attend_bwd_matches_central_differences():
+    B, K = 4, 3
+    q, k, v, do, cu = _bwd_case(50, T=24, H=1, d=4, cu=(0, 24))
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    grads = dict(zip("qkv", oracle.attend_bwd(q, k, v, idx, do, B, K, cu)))
+    base = {"q": q, "k": k, "v": v}
+
+    def loss(x):
+        o, _ = oracle.attend(x["q"], x["k"], x["v"], idx, B, K, cu)
+        return float(np.sum(o * do.astype(np.float64)))
+
+    g = np.random.default_rng(5)
+    for name in "qkv":
+        for _ in range(12):
+            t, c = int(g.integers(0, 24)), int(g.integers(0, 4))
+            xp = {n: a.copy() for n, a in base.items()}
+            xm = {n: a.copy() for n, a in base.items()}
+            xp[name][t, 0, c] += np.float32(1e-3)
+            xm[name][t, 0, c] -= np.float32(1e-3)
+            step = float(xp[name][t, 0, c]) - float(xm[name][t, 0, c])
+            fd = (loss(xp) - loss(xm)) / step
+            assert abs(fd - grads[name][t, 0, c]) <= 1e-5 * max(1.0, abs(fd)), (name, t, c)
+
+
+def test_attend_bwd_invariants():
+    B, K = 4, 3
+    q, k, v, do, cu = _bwd_case(60)
+    T, H, d = q.shape
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    dq, dk, dv = oracle.attend_bwd(q, k, v, idx, do, B, K, cu)
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        # each row's probabilities sum to one: sum_u dv_u = sum_t dO_t
+        assert np.allclose(dv[a:b].sum(0), do[a:b].astype(np.float64).sum(0), atol=1e-12)
+        # each row's dS sums to zero: sum_u dk_u = 0
+        assert np.allclose(dk[a:b].sum(0), 0.0, atol=1e-12)
+    # dO = 0: every gradient vanishes
+    z = oracle.attend_bwd(q, k, v, idx, np.zeros_like(do), B, K, cu)
+    assert all(np.all(x == 0.0) for x in z)
+    # equal value rows make O independent of q and k
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    dq1, dk1, dv1 = oracle.attend_bwd(q, k, vc, idx, do, B, K, cu)
+    assert np.abs(dq1).max() < 1e-12 and np.abs(dk1).max() < 1e-12
+    # the first token of a sequence sees only itself (P = 1, dS = 0)
+    assert np.all(dq[0] == 0.0) and np.all(dq[17] == 0.0)
+
+
+def test_attend_bwd_subsets_equal_full_runs():
+    B, K = 4, 3
+    q, k, v, do, cu = _bwd_case(70)
+    T, H, d = q.shape
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    full = oracle.attend_bwd(q, k, v, idx, do, B, K, cu)
+    g = np.random.default_rng(3)
+    qsel = g.random((T, H)) < 0.3
+    nb = oracle.total_blocks(cu, B)
+    kbsel = g.random((nb, H)) < 0.3
+    sub = oracle.attend_bwd(q, k, v, idx, do, B, K, cu, qsel=qsel, kbsel=kbsel)
+    assert np.array_equal(sub[0][qsel], full[0][qsel])
+    assert np.isnan(sub[0][~qsel]).all()
+    boff = np.concatenate([[0], np.cumsum([-(-(cu[s + 1] - cu[s]) // B) for s in range(len(cu) - 1)])])
+    for t in range(T):
+        s = int(np.searchsorted(cu, t, side="right") - 1)
+        gblk = boff[s] + (t - cu[s]) // B
+        for h in range(H):
+            for x, f in ((sub[1], full[1]), (sub[2], full[2])):
+                if kbsel[gblk, h]:
+                    assert np.array_equal(x[t, h], f[t, h])
+                else:
+                    assert np.isnan(x[t, h]).all()
