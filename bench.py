@@ -111,6 +111,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="H", choices=sorted(workloads.CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd (default): the forward pass; bwd: the attention "
+                         "backward (moba_attn_bwd) for the forward's selection")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -121,6 +124,8 @@ def main():
 
     import block_sparse_long_key_amd as moba
 
+    if args.which == "bwd":
+        return bench_bwd(args, moba)
     spec = workloads.spec(args.config)
     x = workloads.make(spec)
     dev = torch.device("cuda:0")
@@ -238,6 +243,70 @@ def main():
         out["cpu_baseline"] = cpu_baseline(spec, x)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_bwd(args, moba):
+    """One step = one moba_attn_bwd call (index inversion, D = dO.O, the
+    per-key-block list kernel and the dq merge) on the forward's selection,
+    o and lse, which are computed once before the timed region."""
+    spec = workloads.spec(args.config)
+    x = workloads.make(spec)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    w = None if x["conv_w"] is None else x["conv_w"].to(dev)
+    do = workloads.grad_output(spec).to(dev)
+    cu = x["cu_seqlens"]
+    B, K = spec.block_size, spec.top_k
+    o, lse, idx, kk = moba.moba_fwd(q, k, v, B, K, conv_w=w, cu_seqlens=cu)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(max(256, moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
+                     dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        moba.moba_attn_bwd(q, kk, v, idx, o, lse, do, B, K, cu_seqlens=cu, workspace=ws,
+                           out=(dq, dk, dv))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = wall * 1e3 / args.steps
+    ms_ev = [a.elapsed_time(b) for a, b in evs]
+    fl = workloads.eff_flops_bwd(spec)
+    value = fl["total"] / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": "MoBA attention bwd effective TFLOP/s (10 d FLOPs per attended key)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded i.i.d. N(0,1) q/k/v/dO, CPU torch.Generator)",
+        "config": {"workload": f"moba_attn_bwd {spec.name}: {spec.desc}",
+                   "batch": spec.batch, "seq_len": spec.seq, "heads": spec.heads,
+                   "head_dim": spec.head_dim, "block_size": B, "top_k": K,
+                   "F_eff_bwd": fl["total"]},
+        "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "event_ms_median": round(sorted(ms_ev)[len(ms_ev) // 2], 4),
+        "event_ms_min": round(min(ms_ev), 4),
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -1,4 +1,5 @@
-"""MI355X (gfx950) Mixture of Block Attention forward -- Python binding.
+"""MI355X (gfx950) Mixture of Block Attention forward and attention
+backward -- Python binding.
 
 A thin ctypes layer over ``libmoba_amd.so`` (C ABI in ``include/moba.h``).
 It only marshals arguments: it checks tensor devices, dtypes and layouts,
@@ -9,8 +10,8 @@ the calls raise -- there is no CPU fallback.
 
 Names follow the C ABI: ``moba_key_conv``, ``moba_centroids``,
 ``moba_route_topk``, ``moba_attn_fwd`` (plus its three stages
-``moba_attn_index``, ``moba_attn_routed``, ``moba_attn_combine``) and the
-convenience ``moba_fwd`` that chains them.
+``moba_attn_index``, ``moba_attn_routed``, ``moba_attn_combine``), the
+convenience ``moba_fwd`` that chains them, and ``moba_attn_bwd``.
 
 Tensors are ``[batch, seq, heads, head_dim]`` (uniform batch) or
 ``[total_tokens, heads, head_dim]`` with ``cu_seqlens`` (a python list or CPU
@@ -28,6 +29,7 @@ __all__ = [
     "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
     "moba_attn_fwd_workspace_bytes", "moba_total_blocks", "library_path",
+    "moba_attn_bwd", "moba_attn_bwd_workspace_bytes",
     "MobaError",
 ]
 
@@ -76,6 +78,7 @@ def _load():
         "moba_attn_index": [SH, P, P, SZ, P],
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
         "moba_attn_combine": [SH, P, P, P, P, F32, P, P, P, SZ, P],
+        "moba_attn_bwd": [SH, P, P, P, P, F32, P, P, P, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -83,6 +86,8 @@ def _load():
         f.restype = ctypes.c_int
     lib.moba_attn_fwd_workspace_bytes.argtypes = [SH]
     lib.moba_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moba_attn_bwd_workspace_bytes.argtypes = [SH]
+    lib.moba_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.moba_total_blocks.argtypes = [SH]
     lib.moba_total_blocks.restype = ctypes.c_int64
     lib.moba_status_string.argtypes = [ctypes.c_int]
@@ -163,6 +168,12 @@ def moba_attn_fwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
                                   cu_seqlens=None) -> int:
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
     return int(_load().moba_attn_fwd_workspace_bytes(ctypes.byref(sh)))
+
+
+def moba_attn_bwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
+                                  cu_seqlens=None) -> int:
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    return int(_load().moba_attn_bwd_workspace_bytes(ctypes.byref(sh)))
 
 
 def moba_key_conv(k: torch.Tensor, w: torch.Tensor, block_size: int,
@@ -287,3 +298,38 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
     idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens)
     o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
     return o, lse, idx, kk
+
+
+def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                  o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
+                  block_size: int, top_k: int, scale: Optional[float] = None,
+                  cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
+                  out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                  stream=None):
+    """Gradients (dq, dk, dv) of moba_attn_fwd's output for the selection idx.
+
+    o and lse are that forward's outputs; dout is dL/dO.  bf16 only.
+    """
+    _dev(q, k, v, idx, o, lse, dout)
+    if not (q.shape == k.shape == v.shape == o.shape == dout.shape):
+        raise MobaError("q, k, v, o, dout must share one shape")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise MobaError("q, k, v, o, dout must share one dtype")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != _rows(q) + (top_k,):
+        raise MobaError("idx must be int32 [..., heads, top_k]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != _rows(q):
+        raise MobaError("lse must be fp32 [..., heads]")
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _dev(dq, dk, dv)
+    if workspace is None:
+        need = moba_attn_bwd_workspace_bytes(q, block_size, top_k, cu_seqlens)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    rc = _load().moba_attn_bwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
+                               float(scale or 0.0), _p(o), _p(lse), _p(dout), _p(dq),
+                               _p(dk), _p(dv), _p(workspace), workspace.numel(),
+                               _stream(stream))
+    _check(rc, "moba_attn_bwd")
+    return dq, dk, dv

@@ -9,8 +9,9 @@
 //              LDS histogram of the routed past blocks; row of the count
 //              matrix cm[chunk][j] for the lists j this chunk can reach;
 //   scan    -- one workgroup per (sequence, head): list totals, list offsets,
-//              per-chunk positions (in place), and the work items (runs of
-//              <= 128 entries of one list) for the routed attention;
+//              per-chunk positions (in place), the work items (runs of
+//              <= kItemRows entries of one list) for the routed attention,
+//              and the (first entry, count) of every whole list;
 //   scatter -- same grid as count: entries (token << 5 | slot) written at the
 //              chunk's positions with LDS cursors, and the reverse map
 //              (query, slot) -> list position (-1 where nothing is routed),
@@ -87,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const 
 }
 
 __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int32_t* __restrict__ cmat,
-                                                               Item* __restrict__ items)
+                                                               Item* __restrict__ items,
+                                                               int2* __restrict__ lst)
 {
     extern __shared__ int32_t lds[];
     const int s = blockIdx.x, h = blockIdx.y;
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
             run += v;
         }
         const int total = run - beg;
+        lst[(int64_t)h * st.total_blocks + g0 + j] = make_int2(beg, total);
         const int nit = (total + kItemRows - 1) / kItemRows;
         for (int r = 0; r < nit; ++r) {
             Item it;
@@ -223,6 +226,7 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
     Item* items = (Item*)(wsp + ws.items_off);
     uint32_t* ent = (uint32_t*)(wsp + ws.ent_off);
     int32_t* rev = (int32_t*)(wsp + ws.rev_off);
+    int2* lst = (int2*)(wsp + ws.lst_off);
     int maxn = 0;
     for (int s = 0; s < st.nseq; ++s) maxn = maxn > seq_nblk(st, s) ? maxn : seq_nblk(st, s);
     dim3 gc(st.total_chunks, st.H);
@@ -230,7 +234,7 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(inv_scan_kernel, dim3(st.nseq, st.H), dim3(kScanThreads), (size_t)maxn * 8,
-                       L.stream, st, cmat, items);
+                       L.stream, st, cmat, items, lst);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(inv_scatter_kernel, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx,

@@ -87,7 +87,8 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
     return MOBA_OK;
 }
 
-WsLayout layout(const Launch& L)
+// bwd: the backward's workspace (index + its own buffers, no forward partials)
+WsLayout layout(const Launch& L, bool bwd = false)
 {
     WsLayout w;
     memset(&w, 0, sizeof(w));
@@ -99,9 +100,17 @@ WsLayout layout(const Launch& L)
         w.items_bytes = (size_t)st.total_items * sizeof(Item);
         w.ent_bytes = (size_t)st.ebase[st.nseq] * 4;
         w.rev_bytes = rows * st.K * 4;
-        // partials are indexed like the entries (list order)
-        w.po_bytes = (size_t)st.ebase[st.nseq] * L.D * esz;
-        w.pl_bytes = (size_t)st.ebase[st.nseq] * 4;
+        w.lst_bytes = (size_t)st.total_blocks * st.H * 8;
+        if (!bwd) {
+            // partials are indexed like the entries (list order)
+            w.po_bytes = (size_t)st.ebase[st.nseq] * L.D * esz;
+            w.pl_bytes = (size_t)st.ebase[st.nseq] * 4;
+        }
+    }
+    if (bwd) {
+        w.rs_bytes = rows * 8;
+        const size_t ent_rows = st.K > 1 ? (size_t)st.ebase[st.nseq] : 0;
+        w.pq_bytes = (ent_rows + rows) * L.D * 4;
     }
     size_t off = 0;
     w.cmat_off = off;  off += align256(w.cmat_bytes);
@@ -110,6 +119,9 @@ WsLayout layout(const Launch& L)
     w.rev_off = off;   off += align256(w.rev_bytes);
     w.po_off = off;    off += align256(w.po_bytes);
     w.pl_off = off;    off += align256(w.pl_bytes);
+    w.lst_off = off;   off += align256(w.lst_bytes);
+    w.rs_off = off;    off += align256(w.rs_bytes);
+    w.pq_off = off;    off += align256(w.pq_bytes);
     w.total = off;
     return w;
 }
@@ -118,9 +130,9 @@ moba_status hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_E
 
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 
-moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out)
+moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out, bool bwd = false)
 {
-    *out = layout(L);
+    *out = layout(L, bwd);
     if (out->total > 0) {
         if (!ws || ((uintptr_t)ws & 255u) != 0) return MOBA_ERR_INVALID_ARG;
         if (bytes < out->total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
@@ -163,6 +175,13 @@ size_t moba_attn_fwd_workspace_bytes(const moba_shape* shape)
     Launch L;
     if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
     return layout(L).total;
+}
+
+size_t moba_attn_bwd_workspace_bytes(const moba_shape* shape)
+{
+    Launch L;
+    if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
+    return layout(L, true).total;
 }
 
 moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w, int32_t width,
@@ -260,6 +279,35 @@ moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k,
     if (st != MOBA_OK) return st;
     return moba_attn_combine(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
                              workspace_bytes, stream);
+}
+
+moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+                          const int32_t* idx, float softmax_scale, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (L.dtype != MOBA_BF16) return MOBA_ERR_UNSUPPORTED;
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
+        !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
+        return MOBA_ERR_INVALID_ARG;
+    const void* ins[] = {q, k, v, o, dout, (const void*)lse, (const void*)idx};
+    const void* outs[] = {dq, dk, dv};
+    for (const void* a : outs) {
+        for (const void* b : ins)
+            if (a == b) return MOBA_ERR_INVALID_ARG;
+    }
+    if (dq == dk || dq == dv || dk == dv) return MOBA_ERR_INVALID_ARG;
+    WsLayout ws;
+    st = check_ws(L, workspace, workspace_bytes, &ws, true);
+    if (st != MOBA_OK) return st;
+    if (L.tokens == 0) return MOBA_OK;
+    hipError_t e = launch_inv(L, ws, (char*)workspace, idx);
+    if (e != hipSuccess) return MOBA_ERR_HIP;
+    return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout,
+                                      resolve_scale(softmax_scale, L.D), dq, dk, dv));
 }
 
 }  // extern "C"

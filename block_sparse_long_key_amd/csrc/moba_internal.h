@@ -119,6 +119,9 @@ struct WsLayout {
     size_t rev_off, rev_bytes;       // int32 [H][tokens][K]: list position of (t, slot), -1 if none
     size_t po_off, po_bytes;         // partial o rows, list order (I/O dtype, D per row)
     size_t pl_off, pl_bytes;         // partial lse, list order, fp32 (log2 units)
+    size_t lst_off, lst_bytes;       // int2 [H][total blocks]: (first entry, count) of each list
+    size_t rs_off, rs_bytes;         // backward: float2 [tokens][H] (lse in log2 units, dO . O)
+    size_t pq_off, pq_bytes;         // backward: fp32 dq pieces, list order, then own-block rows
     size_t total;
 };
 
@@ -137,6 +140,9 @@ hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
                               const void* q, const void* k, const void* v, float scale);
+hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
+                           const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, float scale, void* dq, void* dk, void* dv);
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, float scale, void* o, float* lse);

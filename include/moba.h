@@ -1,5 +1,6 @@
 /*
- * moba.h -- C ABI of the MI355X (gfx950) Mixture of Block Attention forward.
+ * moba.h -- C ABI of the MI355X (gfx950) Mixture of Block Attention forward
+ * and of its attention backward.
  *
  * The method is the one of "Optimizing Mixture of Block Attention" (Xiao,
  * Guo, Mazaheri, Han), as summarised on its summary pages:
@@ -167,6 +168,40 @@ moba_status moba_attn_combine(const moba_shape *shape, const void *q,
                               const int32_t *idx, float softmax_scale,
                               void *o, float *lse, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moba_attn_bwd -- gradients of moba_attn_fwd's O with respect to q, k and v
+ * for the fixed selection idx (summary page, "Backward Pass: Ricalcolo
+ * (Algoritmo 5)": recompute the scores and probabilities FlashAttention-2
+ * style, parallel over key blocks, gathering each block's queries as the
+ * forward does).  The selection is piecewise constant in q and k, so no
+ * gradient flows through the router; the gradient of k flows into k' only
+ * (the key convolution's input is the caller's business).
+ *   q, k, v, idx, softmax_scale: exactly as given to moba_attn_fwd.
+ *   o, lse: that call's outputs (lse is required here).
+ *   dout: dL/dO, same layout and dtype as o.
+ *   dq, dk, dv: outputs, same layout and dtype as q; fully written; must
+ *   not alias any input or each other.
+ *   For query t with key set U_t (as in moba_attn_fwd), with
+ *   P_tu = exp(scale q_t.k_u - lse_t) and D_t = dout_t . o_t:
+ *     dv_u = sum_t P_tu dout_t,  dS_tu = P_tu (dout_t . v_u - D_t),
+ *     dq_t = scale sum_u dS_tu k_u,  dk_u = scale sum_t dS_tu q_t.
+ *   bf16 only (MOBA_ERR_UNSUPPORTED for fp32): P and dS enter the matrix
+ *   products as bf16, every sum is fp32, outputs are rounded once.
+ *   workspace: at least moba_attn_bwd_workspace_bytes(), 256-byte aligned,
+ *   scratch on exit; it holds the inverted lists and one fp32 dq piece per
+ *   routed (query, slot) pair, so the result is deterministic (no atomics).
+ *   Same error behaviour as moba_attn_fwd.
+ */
+moba_status moba_attn_bwd(const moba_shape *shape, const void *q,
+                          const void *k, const void *v, const int32_t *idx,
+                          float softmax_scale, const void *o, const float *lse,
+                          const void *dout, void *dq, void *dk, void *dv,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Bytes of workspace moba_attn_bwd needs for `shape` (0 on invalid shape). */
+size_t moba_attn_bwd_workspace_bytes(const moba_shape *shape);
 
 /* Bytes of workspace moba_attn_fwd needs for `shape` (0 on invalid shape). */
 size_t moba_attn_fwd_workspace_bytes(const moba_shape *shape);

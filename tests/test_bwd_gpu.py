@@ -1,0 +1,151 @@
+"""GPU parity of the attention backward (moba_attn_bwd) against the oracle.
+
+The HIP path's forward (o, lse) feeds its backward, as in training; the
+oracle recomputes everything in fp64 from q, k, v, the selection and dO.
+Both sides get the same seeded inputs (workloads) and the oracle's own
+selection.
+
+Bar for bf16 (from the arithmetic: each output is rounded once to bf16,
+u = 2^-9, which alone gives a mean relative error near 0.7u; P and dS enter
+the products as bf16 and D_t comes from the bf16 forward output, each a
+further O(u) per term with random signs): for each of dq, dk, dv,
+    max |err| <= 1e-2 * max |ref|  (about 5u)   and
+    mean |err| <= 4e-3 * mean |ref| (about 2u).
+At full size the oracle covers sampled rows (dq) and sampled key blocks
+(dk, dv); every row is checked against the sum invariants
+sum_u dv_u = sum_t dO_t and sum_u dk_u = 0 per (sequence, head).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MAX_REL, MEAN_REL = 1e-2, 4e-3
+
+
+def moba():
+    import block_sparse_long_key_amd as m
+    return m
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _spec(base, seq=None, heads=None, seqlens=None, **kw):
+    s = workloads.spec(base)
+    if seqlens is not None:
+        s = dataclasses.replace(s, batch=1, seq=sum(seqlens), seqlens=tuple(seqlens))
+    elif seq is not None:
+        s = s.scaled(seq)
+    if heads is not None:
+        s = dataclasses.replace(s, heads=heads)
+    return dataclasses.replace(s, conv_width=0, plant=False, name=s.name + "-bwd", **kw)
+
+
+CASES = {
+    "H-2k": _spec("H", seq=2048, heads=4),
+    "C4-4k": _spec("C4", seq=4096, heads=2),
+    "C5-4k": _spec("C5", seq=4096, heads=2),
+    "d128-B64-ragged": _spec("C5", seqlens=(1000, 777), heads=2, block_size=64, top_k=4),
+    "ragged": _spec("H", seqlens=(1, 127, 129, 700, 0, 300), heads=2),
+    "top1": _spec("H", seq=1000, heads=2, top_k=1),
+    "top32-B64": _spec("C4", seq=4096, heads=1, top_k=32),
+}
+
+
+def _run(s):
+    x = workloads.make(s)
+    cu = workloads.segments(s)
+    do = workloads.grad_output(s)
+    B, K = s.block_size, s.top_k
+    idx, *_ = oracle.route(x["q"], oracle.centroids(x["k"], B, cu), B, K, cu)
+    m = moba()
+    q, k, v, dog = (t.to(DEV) for t in (x["q"], x["k"], x["v"], do))
+    idx_g = torch.from_numpy(idx).reshape(tuple(q.shape[:-1]) + (K,)).to(DEV)
+    cus = x["cu_seqlens"]
+    o, lse = m.moba_attn_fwd(q, k, v, idx_g, B, K, cu_seqlens=cus)
+    dq, dk, dv = m.moba_attn_bwd(q, k, v, idx_g, o, lse, dog, B, K, cu_seqlens=cus)
+    torch.cuda.synchronize()
+    return x, cu, do, idx, (dq, dk, dv)
+
+
+def _check(name, got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    mx_rel = err.max() / max(np.abs(ref).max(), 1e-30)
+    mean_rel = err.mean() / max(np.abs(ref).mean(), 1e-30)
+    print(f"[{name}] {what}: max|err|/max|ref| {mx_rel:.2e}  mean|err|/mean|ref| {mean_rel:.2e}",
+          flush=True)
+    assert mx_rel <= MAX_REL, f"{name} {what}: max rel {mx_rel:.3e}"
+    assert mean_rel <= MEAN_REL, f"{name} {what}: mean rel {mean_rel:.3e}"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_bwd_matches_oracle(name):
+    s = CASES[name]
+    print(f"[bwd {name}] {s}", flush=True)
+    x, cu, do, idx, got = _run(s)
+    H, d = s.heads, s.head_dim
+    ref = oracle.attend_bwd(x["q"], x["k"], x["v"], idx, do, s.block_size, s.top_k, cu)
+    for g, r, w in zip(got, ref, ("dq", "dk", "dv")):
+        _check(name, _np(g).reshape(-1, H, d), r, w)
+
+
+def test_bwd_repeatable():
+    """dq is bitwise repeatable (each (query, slot) piece is computed alone
+    and the pieces are added in slot order).  dk / dv sum a list's rows in
+    list order, which the index pass fills with LDS atomics, so two runs may
+    differ by fp32 summation order: at most a few bf16 units in the last
+    place, far inside the parity bar."""
+    s = CASES["H-2k"]
+    x, cu, do, idx, a = _run(s)
+    _, _, _, _, b = _run(s)
+    assert torch.equal(a[0], b[0])
+    for u, w in zip(a[1:], b[1:]):
+        uf, wf = u.float(), w.float()
+        diff = (uf - wf).abs()
+        assert float(diff.max()) <= 2 ** -6 * float(uf.abs().max())
+        assert float(diff.mean()) <= 2 ** -9 * float(uf.abs().mean())
+
+
+def test_bwd_full_size_sampled():
+    s = dataclasses.replace(workloads.spec("H"))
+    print(f"[bwd full {s.name}] {s}", flush=True)
+    x, cu, do, idx, got = _run(s)
+    H, d, B = s.heads, s.head_dim, s.block_size
+    dq, dk, dv = (_np(t).reshape(-1, H, d).astype(np.float64) for t in got)
+    T = dq.shape[0]
+    dof = do.float().numpy().reshape(-1, H, d).astype(np.float64)
+    # invariants on every row
+    for si in range(len(cu) - 1):
+        a, b = cu[si], cu[si + 1]
+        sv = dv[a:b].sum(0)
+        assert np.all(np.abs(sv - dof[a:b].sum(0)) <= 2 ** -7 * np.abs(dv[a:b]).sum(0) + 1e-3)
+        assert np.all(np.abs(dk[a:b].sum(0)) <= 2 ** -7 * np.abs(dk[a:b]).sum(0) + 1e-3)
+    # sampled rows and key blocks against the oracle
+    g = np.random.default_rng(11)
+    qsel = np.zeros((T, H), bool)
+    qsel.reshape(-1)[g.choice(T * H, 1024, replace=False)] = True
+    nb = oracle.total_blocks(cu, B)
+    kbsel = np.zeros((nb, H), bool)
+    for h in range(H):
+        kbsel[g.choice(nb), h] = True
+        kbsel[0, h] = True if h == 0 else kbsel[0, h]     # the most-routed-to block
+    ref = oracle.attend_bwd(x["q"], x["k"], x["v"], idx, do, B, s.top_k, cu,
+                            qsel=qsel, kbsel=kbsel)
+    _check("H", dq[qsel], ref[0][qsel], "dq (sampled rows)")
+    boff = np.concatenate([[0], np.cumsum([-(-(cu[i + 1] - cu[i]) // B) for i in range(len(cu) - 1)])])
+    tok_blk = np.empty(T, np.int64)
+    for si in range(len(cu) - 1):
+        tl = np.arange(cu[si + 1] - cu[si])
+        tok_blk[cu[si]:cu[si + 1]] = boff[si] + tl // B
+    km = kbsel[tok_blk]                      # [T, H]
+    _check("H", dk[km], ref[1][km], "dk (sampled blocks)")
+    _check("H", dv[km], ref[2][km], "dv (sampled blocks)")

@@ -23,7 +23,7 @@ sys.path.insert(0, ROOT)
 from block_sparse_long_key_amd import build as libbuild  # noqa: E402
 
 NEED = 8
-SOURCES = ["router.hip", "attn.hip"]
+SOURCES = ["router.hip", "attn.hip", "attn_bwd.hip"]
 
 
 def _regs(op):

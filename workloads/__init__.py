@@ -28,7 +28,7 @@ from typing import List, Optional
 import torch
 
 __all__ = ["Spec", "CONFIGS", "spec", "make", "segments", "eff_flops",
-           "routed_pairs"]
+           "routed_pairs", "grad_output", "eff_flops_bwd"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -160,6 +160,20 @@ def make(s, seed: Optional[int] = None, device="cpu"):
     return out
 
 
+def grad_output(s, seed: Optional[int] = None, device="cpu") -> torch.Tensor:
+    """dL/dO for the attention backward: standard normal, shaped like q, in
+    the config dtype, from its own generator (seed + 10007) so the forward
+    inputs stay those of make()."""
+    if isinstance(s, str):
+        s = spec(s)
+    g = torch.Generator().manual_seed((s.seed if seed is None else seed) + 10007)
+    if s.seqlens is not None:
+        shape = (s.seq, s.heads, s.head_dim)
+    else:
+        shape = (s.batch, s.seq, s.heads, s.head_dim)
+    return torch.randn(shape, generator=g, dtype=torch.float32).to(s.torch_dtype).to(device)
+
+
 def routed_pairs(s: Spec) -> int:
     """Number of (query, routed past block) pairs over all (sequence, head).
 
@@ -195,3 +209,11 @@ def eff_flops(s: Spec) -> dict:
     routed *= 4 * d * s.heads
     diag *= 4 * d * s.heads
     return {"routed": routed, "diag": diag, "total": routed + diag}
+
+
+def eff_flops_bwd(s: Spec) -> dict:
+    """Effective FLOPs of the attention backward: per (query, key) pair the
+    recomputed scores, dP, dV, dK and dQ products, 2*d FLOPs each (10*d),
+    i.e. 2.5 times the forward's 4*d."""
+    f = eff_flops(s)
+    return {n: v * 5 // 2 for n, v in f.items()}
