@@ -104,6 +104,19 @@ def cpu_baseline(spec, x, nthreads=None):
     }
 
 
+def _calib_copy(args, dev):
+    """One plain device copy of --calib-copy-mib MiB (a kernel of known size
+    for scaling the HBM byte counters)."""
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -167,14 +180,7 @@ def main():
         moba.moba_attn_combine(q, kk, v, idx, B, K, ws, o, lse, None, cu)
         mark(5)
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    _calib_copy(args, dev)
 
     for _ in range(args.warmup):
         step()
@@ -264,6 +270,7 @@ def bench_bwd(args, moba):
     ws = torch.empty(max(256, moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    _calib_copy(args, dev)
 
     def step():
         moba.moba_attn_bwd(q, kk, v, idx, o, lse, do, B, K, cu_seqlens=cu, workspace=ws,
