@@ -60,6 +60,8 @@ def _load():
         lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
                                                _P, _P, _P, _P, _P, _I]
         lib.moba_oracle_attend_bwd.restype = _I
+        lib.moba_oracle_key_conv_bwd.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I]
+        lib.moba_oracle_key_conv_bwd.restype = _I
         lib.moba_oracle_route_rows.restype = _I
         lib.moba_oracle_attend_rows.restype = _I
         for f in (lib.moba_oracle_key_conv, lib.moba_oracle_centroids,
@@ -254,3 +256,23 @@ def attend_bwd(q, k, v, idx, dout, B: int, K: int, cu, scale: float = 0.0,
                                         nthreads or default_threads())
     assert rc == 0
     return dq, dk, dv
+
+
+def key_conv_bwd(k, w, g, cu, mode: int = 0, nthreads: Optional[int] = None):
+    """Gradients of the key convolution given g = dL/dk'.
+
+    Returns (dk f64 [T, H, d], dw f64 [H, d, W]).
+    """
+    k, g = _f32(k), _f32(g)
+    w = np.ascontiguousarray(_f32(w) if not isinstance(w, np.ndarray) else w, dtype=np.float32)
+    T, H, d = k.shape
+    W = w.shape[-1]
+    assert w.shape == (H, d, W) and g.shape == k.shape
+    c = _cu(cu)
+    dk = np.empty((T, H, d), dtype=np.float64)
+    dw = np.empty((H, d, W), dtype=np.float64)
+    rc = _load().moba_oracle_key_conv_bwd(_ptr(k), _ptr(w), _ptr(g), H, d, W, mode, _ptr(c),
+                                          len(c) - 1, _ptr(dk), _ptr(dw),
+                                          nthreads or default_threads())
+    assert rc == 0
+    return dk, dw

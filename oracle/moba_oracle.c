@@ -611,3 +611,69 @@ int moba_oracle_attend_bwd(const float *q, const float *k, const float *v,
     free(boff);
     return 0;
 }
+
+/* =====================================================================
+ * Backward of step 1 (key convolution, Appendice B formal form): given
+ * g = dL/dk', the gradients with respect to k and to the filter w, in fp64.
+ *   u_t  = sum_l w_l k_{t-l}                    (the conv, taps inside the
+ *                                                sequence only)
+ *   mode 0:  e_t = g_t                          (k' = u)
+ *   mode 1:  e_t = g_t * s'(u_t),               (k' = k + SiLU(u))
+ *            s'(u) = sig(u) (1 + u (1 - sig(u))), sig(u) = 1/(1+exp(-u))
+ *   dk_t = [mode 1: g_t] + sum_l w_l e_{t+l}    (t+l inside the sequence)
+ *   dw_l = sum over sequences and t of e_t k_{t-l}   (t-l inside it)
+ * per (head, channel).  One job per head (dw sums over every sequence).
+ * ===================================================================== */
+typedef struct {
+    const float *k, *w, *g;
+    double *dk, *dw;
+    const int *cu;
+    int nseq, H, d, W, mode;
+} convb_ctx;
+
+static void convb_job(void *vctx, int h)
+{
+    convb_ctx *c = (convb_ctx *)vctx;
+    int H = c->H, d = c->d, W = c->W;
+    for (int ch = 0; ch < d; ++ch) {
+        const float *wv = c->w + ((size_t)h * d + ch) * W;
+        double *dwv = c->dw + ((size_t)h * d + ch) * W;
+        for (int l = 0; l < W; ++l) dwv[l] = 0.0;
+        for (int s = 0; s < c->nseq; ++s) {
+            int t0 = c->cu[s], t1 = c->cu[s + 1];
+            for (int t = t0; t < t1; ++t) {
+                size_t row = ((size_t)t * H + h) * d + ch;
+                double acc = (c->mode == 1) ? (double)c->g[row] : 0.0;
+                for (int l = 0; l < W; ++l) {
+                    int tt = t + l;
+                    if (tt >= t1) break;
+                    size_t r2 = ((size_t)tt * H + h) * d + ch;
+                    double e = (double)c->g[r2];
+                    if (c->mode == 1) {
+                        double u = 0.0;
+                        for (int m = 0; m < W; ++m)
+                            if (tt - m >= t0)
+                                u += (double)c->w[((size_t)h * d + ch) * W + m] *
+                                     (double)c->k[((size_t)(tt - m) * H + h) * d + ch];
+                        double sg = 1.0 / (1.0 + exp(-u));
+                        e *= sg * (1.0 + u * (1.0 - sg));
+                    }
+                    acc += (double)wv[l] * e;
+                    /* dw_l gets e_{tt} k_{tt-l} = e_{t+l} k_t */
+                    dwv[l] += e * (double)c->k[row];
+                }
+                c->dk[row] = acc;
+            }
+        }
+    }
+}
+
+int moba_oracle_key_conv_bwd(const float *k, const float *w, const float *g, int H,
+                             int d, int W, int mode, const int *cu, int nseq,
+                             double *dk, double *dw, int nthreads)
+{
+    if (W < 1 || (mode != 0 && mode != 1)) return 1;
+    convb_ctx c = {k, w, g, dk, dw, cu, nseq, H, d, W, mode};
+    run_jobs(convb_job, &c, H, nthreads);
+    return 0;
+}

@@ -499,3 +499,88 @@ def test_attend_bwd_subsets_equal_full_runs():
                     assert np.array_equal(x[t, h], f[t, h])
                 else:
                     assert np.isnan(x[t, h]).all()
+
+
+# ------------------------------------------------------- conv backward ----
+def _conv_autograd64(k, w, g, cu, mode):
+    """Library autograd of the key conv in fp64 (per-sequence conv1d with
+    flipped weights and left padding, plus k + silu(conv) for mode 1)."""
+    T, H, d = k.shape
+    W = w.shape[-1]
+    wt = torch.from_numpy(w[:, :, ::-1].copy()).double().reshape(H * d, 1, W).requires_grad_()
+    kt = torch.from_numpy(k).double().requires_grad_()
+    outs = []
+    for s in range(len(cu) - 1):
+        x = kt[cu[s]:cu[s + 1]].reshape(-1, H * d).T[None]
+        y = F.conv1d(F.pad(x, (W - 1, 0)), wt, groups=H * d)[0].T.reshape(-1, H, d)
+        if mode == 1:
+            y = kt[cu[s]:cu[s + 1]] + F.silu(y)
+        outs.append(y)
+    out = torch.cat(outs)
+    out.backward(torch.from_numpy(g).double())
+    dw = wt.grad.reshape(H, d, W).numpy()[:, :, ::-1]
+    return kt.grad.numpy(), dw
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("W", [1, 3, 4])
+def test_conv_bwd_matches_autograd_conv1d(mode, W):
+    T, H, d = 60, 2, 8
+    cu = [0, 1, 25, 60]
+    k = _bf16(_rand((T, H, d), 81))
+    g = _bf16(_rand((T, H, d), 82))
+    w = _rand((H, d, W), 83) * np.float32(1 / math.sqrt(W))
+    dk, dw = oracle.key_conv_bwd(k, w, g, cu, mode)
+    rk, rw = _conv_autograd64(k, w, g, cu, mode)
+    assert np.allclose(dk, rk, rtol=1e-12, atol=1e-12)
+    assert np.allclose(dw, rw, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_bwd_matches_central_differences():
+    T, H, d, W = 12, 1, 2, 3
+    cu = [0, 12]
+    k = _rand((T, H, d), 84)
+    g = _rand((T, H, d), 85)
+    w = _rand((H, d, W), 86)
+    for mode in (0, 1):
+        dk, dw = oracle.key_conv_bwd(k, w, g, cu, mode)
+
+        def loss(kk, ww):
+            # the conv in fp64 through the library (the oracle's own forward
+            # rounds to fp32 by design, too coarse for differences)
+            x = torch.from_numpy(kk[:, 0].T.copy()).double()[None]
+            wt = torch.from_numpy(ww[0, :, ::-1].copy()).double()[:, None]
+            y = F.conv1d(F.pad(x, (W - 1, 0)), wt, groups=d)[0].T
+            if mode == 1:
+                y = torch.from_numpy(kk[:, 0]).double() + F.silu(y)
+            return float((y * torch.from_numpy(g[:, 0]).double()).sum())
+
+        for (t, c) in [(0, 0), (5, 1), (11, 0)]:
+            kp, km = k.copy(), k.copy()
+            kp[t, 0, c] += np.float32(1e-3)
+            km[t, 0, c] -= np.float32(1e-3)
+            fd = (loss(kp, w) - loss(km, w)) / (float(kp[t, 0, c]) - float(km[t, 0, c]))
+            assert abs(fd - dk[t, 0, c]) <= 1e-5 * max(1.0, abs(fd))
+        for (c, l) in [(0, 0), (1, 2)]:
+            wp, wm = w.copy(), w.copy()
+            wp[0, c, l] += np.float32(1e-3)
+            wm[0, c, l] -= np.float32(1e-3)
+            fd = (loss(k, wp) - loss(k, wm)) / (float(wp[0, c, l]) - float(wm[0, c, l]))
+            assert abs(fd - dw[0, c, l]) <= 1e-5 * max(1.0, abs(fd))
+
+
+def test_conv_bwd_identity_filter_passes_gradient_through():
+    T, H, d, W = 20, 2, 4, 3
+    cu = [0, 7, 20]
+    k, g = _rand((T, H, d), 87), _rand((T, H, d), 88)
+    w = np.zeros((H, d, W), np.float32)
+    w[:, :, 0] = 1.0                                   # k' = k
+    dk, dw = oracle.key_conv_bwd(k, w, g, cu, 0)
+    assert np.array_equal(dk, g.astype(np.float64))
+    # dw_l = sum_t g_t k_{t-l} within each sequence
+    ref = np.zeros((H, d, W))
+    for s in range(2):
+        a, b = cu[s], cu[s + 1]
+        for l in range(W):
+            ref[:, :, l] += (g[a + l:b].astype(np.float64) * k[a:b - l]).sum(0)
+    assert np.allclose(dw, ref, rtol=1e-12, atol=1e-12)
