@@ -255,7 +255,8 @@ def main():
 def bench_bwd(args, moba):
     """One step = one moba_attn_bwd call (index inversion, D = dO.O, the
     per-key-block list kernel and the dq merge) on the forward's selection,
-    o and lse, which are computed once before the timed region."""
+    o and lse, which are computed once before the timed region; with a key
+    convolution, also moba_key_conv_bwd (dk' -> dk, dw)."""
     spec = workloads.spec(args.config)
     x = workloads.make(spec)
     dev = torch.device("cuda:0")
@@ -272,9 +273,17 @@ def bench_bwd(args, moba):
     stream = torch.cuda.current_stream()
     _calib_copy(args, dev)
 
+    wsc = None
+    if w is not None:
+        wsc = torch.empty(max(256, moba.moba_key_conv_bwd_workspace_bytes(k, B, w.shape[2], cu)),
+                          dtype=torch.uint8, device=dev)
+
     def step():
         moba.moba_attn_bwd(q, kk, v, idx, o, lse, do, B, K, cu_seqlens=cu, workspace=ws,
                            out=(dq, dk, dv))
+        if w is not None:
+            # dL/dk' -> dL/dk and dL/dw through the key convolution
+            moba.moba_key_conv_bwd(k, w, dk, B, "plain", cu_seqlens=cu, workspace=wsc)
 
     for _ in range(args.warmup):
         step()

@@ -29,7 +29,8 @@ __all__ = [
     "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
     "moba_attn_fwd_workspace_bytes", "moba_total_blocks", "library_path",
-    "moba_attn_bwd", "moba_attn_bwd_workspace_bytes",
+    "moba_attn_bwd", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
+    "moba_key_conv_bwd_workspace_bytes",
     "MobaError",
 ]
 
@@ -79,6 +80,7 @@ def _load():
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
         "moba_attn_combine": [SH, P, P, P, P, F32, P, P, P, SZ, P],
         "moba_attn_bwd": [SH, P, P, P, P, F32, P, P, P, P, P, P, P, SZ, P],
+        "moba_key_conv_bwd": [SH, P, P, I32, I32, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -86,6 +88,8 @@ def _load():
         f.restype = ctypes.c_int
     lib.moba_attn_fwd_workspace_bytes.argtypes = [SH]
     lib.moba_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moba_key_conv_bwd_workspace_bytes.argtypes = [SH, I32]
+    lib.moba_key_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.moba_attn_bwd_workspace_bytes.argtypes = [SH]
     lib.moba_attn_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.moba_total_blocks.argtypes = [SH]
@@ -198,6 +202,35 @@ def moba_key_conv(k: torch.Tensor, w: torch.Tensor, block_size: int,
                                _p(cent if with_centroids else None), _stream(stream))
     _check(rc, "moba_key_conv")
     return (out, cent) if with_centroids else out
+
+
+def moba_key_conv_bwd_workspace_bytes(k: torch.Tensor, block_size: int, width: int,
+                                      cu_seqlens=None) -> int:
+    sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
+    return int(_load().moba_key_conv_bwd_workspace_bytes(ctypes.byref(sh), int(width)))
+
+
+def moba_key_conv_bwd(k: torch.Tensor, w: torch.Tensor, dk_out: torch.Tensor, block_size: int,
+                      mode: str = "plain", cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
+                      stream=None):
+    """Gradients of moba_key_conv given dk_out = dL/dk'.  Returns (dk, dw)."""
+    _dev(k, w, dk_out)
+    if dk_out.shape != k.shape or dk_out.dtype != k.dtype:
+        raise MobaError("dk_out must match k")
+    if w.dtype != torch.float32 or w.dim() != 3 or w.shape[0] != k.shape[-2] or w.shape[1] != k.shape[-1]:
+        raise MobaError("w must be fp32 [heads, head_dim, width]")
+    sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
+    W = int(w.shape[2])
+    if workspace is None:
+        need = moba_key_conv_bwd_workspace_bytes(k, block_size, W, cu_seqlens)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    dk = torch.empty_like(k)
+    dw = torch.empty_like(w)
+    rc = _load().moba_key_conv_bwd(ctypes.byref(sh), _p(k), _p(w), W, _CONV_MODES[mode],
+                                   _p(dk_out), _p(dk), _p(dw), _p(workspace), workspace.numel(),
+                                   _stream(stream))
+    _check(rc, "moba_key_conv_bwd")
+    return dk, dw
 
 
 def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,

@@ -200,6 +200,32 @@ moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w
     return hip_status(launch_conv_pool(L, k, w, width, mode, k_out, cent));
 }
 
+size_t moba_key_conv_bwd_workspace_bytes(const moba_shape* shape, int32_t width)
+{
+    Launch L;
+    if (make_launch(shape, &L, nullptr) != MOBA_OK || width < 1 || width > 8) return 0;
+    return align256((size_t)L.st.total_blocks * L.st.H * L.D * width * 4);
+}
+
+moba_status moba_key_conv_bwd(const moba_shape* shape, const void* k, const float* w, int32_t width,
+                              int32_t mode, const void* dk_out, void* dk, float* dw, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (mode != MOBA_CONV_PLAIN && mode != MOBA_CONV_SILU_RESIDUAL) return MOBA_ERR_INVALID_ARG;
+    if (width < 1) return MOBA_ERR_INVALID_ARG;
+    if (width > 8) return MOBA_ERR_UNSUPPORTED;
+    if (!ptr_ok(k) || !ptr_ok(w) || !ptr_ok(dk_out) || !ptr_ok(dk) || !ptr_ok(dw))
+        return MOBA_ERR_INVALID_ARG;
+    if (dk == k || dk == dk_out) return MOBA_ERR_INVALID_ARG;
+    const size_t need = moba_key_conv_bwd_workspace_bytes(shape, width);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    return hip_status(launch_conv_bwd(L, k, w, width, mode, dk_out, dk, dw, (float*)workspace));
+}
+
 moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, hipStream_t stream)
 {
     Launch L;

@@ -136,6 +136,8 @@ struct Launch {
 
 hipError_t launch_conv_pool(const Launch& L, const void* k, const float* w, int W,
                             int mode, void* k_out, float* cent);
+hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W, int mode,
+                           const void* gk, void* dk, float* dw, float* dwp);
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx);
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,

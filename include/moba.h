@@ -102,6 +102,32 @@ moba_status moba_key_conv(const moba_shape *shape, const void *k,
                           void *k_out, float *cent, hipStream_t stream);
 
 /*
+ * moba_key_conv_bwd -- gradients of moba_key_conv (Appendice B, formal form)
+ * given dk_out = dL/dk' (same layout and dtype as k):
+ *   e_t  = dk_out_t                 (MOBA_CONV_PLAIN)
+ *        = dk_out_t * s'(u_t)       (MOBA_CONV_SILU_RESIDUAL; u_t the tap sum,
+ *                                    s'(u) = sig(u) (1 + u (1 - sig(u))))
+ *   dk_t = [SiLU form: dk_out_t] + sum_l w_l e_{t+l}   (t+l in the sequence)
+ *   dw[h][c][l] = sum over all tokens t of e_t k_{t-l}  (t-l in the sequence)
+ *   dk: same layout and dtype as k (fp32 sums, rounded once); must not alias
+ *   k or dk_out.  dw: fp32 [heads][head_dim][width], fully written; the sum
+ *   over tokens is fp32 per key block and fp64 across blocks, in a fixed
+ *   order (deterministic).
+ *   workspace: at least moba_key_conv_bwd_workspace_bytes() (one fp32
+ *   partial of dw per key block), 256-byte aligned, scratch on exit.
+ *   Same validation and errors as moba_key_conv.
+ */
+moba_status moba_key_conv_bwd(const moba_shape *shape, const void *k,
+                              const float *w, int32_t width, int32_t mode,
+                              const void *dk_out, void *dk, float *dw,
+                              void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Bytes of workspace moba_key_conv_bwd needs (0 on invalid shape / width). */
+size_t moba_key_conv_bwd_workspace_bytes(const moba_shape *shape,
+                                         int32_t width);
+
+/*
  * moba_centroids -- block means kbar_j (router-score equation).
  *   cent: fp32 [total_blocks][heads][head_dim].  Each mean is the exact
  *   fp64 sum of the block's keys, divided by the block's key count and

@@ -149,3 +149,45 @@ def test_bwd_full_size_sampled():
     km = kbsel[tok_blk]                      # [T, H]
     _check("H", dk[km], ref[1][km], "dk (sampled blocks)")
     _check("H", dv[km], ref[2][km], "dv (sampled blocks)")
+
+
+# ------------------------------------------------ key-convolution backward
+CONV_CASES = {
+    # name: (spec, mode, width override)
+    "C3-plain-W3": (_spec("C3", seq=4096, heads=4), "plain", 3),
+    "C5-plain-W4-d128": (_spec("C5", seq=8192, heads=2), "plain", 4),
+    "silu-W3-ragged": (_spec("H", seqlens=(1, 127, 129, 700, 0, 300), heads=2), "silu_residual", 3),
+    "W1": (_spec("H", seq=1000, heads=2), "plain", 1),
+    "W8-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 8),
+    "f32-W4": (_spec("C1"), "plain", 4),
+    "C3-full-W3": (dataclasses.replace(workloads.spec("C3"), plant=False), "plain", 3),
+}
+
+
+@pytest.mark.parametrize("name", list(CONV_CASES))
+def test_key_conv_bwd_matches_oracle(name):
+    s, mode, W = CONV_CASES[name]
+    print(f"[conv bwd {name}] {s} mode={mode} W={W}", flush=True)
+    x = workloads.make(s)
+    cu = workloads.segments(s)
+    g = workloads.grad_output(s)
+    gen = torch.Generator().manual_seed(s.seed + 20011)
+    w = torch.randn((s.heads, s.head_dim, W), generator=gen) * (1.0 / W) ** 0.5
+    m = moba()
+    dk, dw = m.moba_key_conv_bwd(x["k"].to(DEV), w.to(DEV), g.to(DEV), s.block_size, mode,
+                                 cu_seqlens=x["cu_seqlens"])
+    torch.cuda.synchronize()
+    rk, rw = oracle.key_conv_bwd(x["k"], w.numpy(), g, cu, 0 if mode == "plain" else 1)
+    H, d = s.heads, s.head_dim
+    dk = _np(dk).reshape(-1, H, d).astype(np.float64)
+    dw = dw.cpu().numpy().astype(np.float64)
+    # dk: fp32 sums rounded once to the I/O dtype
+    rel = 2.0 ** -8 if s.dtype == "bf16" else 1e-6
+    ek = np.abs(dk - rk)
+    assert np.all(ek <= rel * np.abs(rk) + 1e-6 * np.abs(rk).max()), \
+        f"dk max err {ek.max():.3e}"
+    # dw: fp32 per key block, fp64 across blocks
+    ew = np.abs(dw - rw)
+    print(f"[conv bwd {name}] dk max err {ek.max():.2e}  dw max err / max |dw| "
+          f"{ew.max() / np.abs(rw).max():.2e}", flush=True)
+    assert ew.max() <= 1e-5 * np.abs(rw).max()
