@@ -216,7 +216,55 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     }
 }
 
+// Block sizes above 128: a selected block of B = r * 128 keys is the union
+// of its r sub-blocks of 128 keys, and the query's own block splits into the
+// sub-blocks before its own sub-block (every key of which precedes the
+// query) and its own sub-block (token-causal).  Attention over the selection
+// is therefore attention over 128-key blocks with this expanded list, which
+// the 128-key kernels run unchanged.  One thread per (token, head) row.
+__global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int r, int Kp,
+                                                             const int32_t* __restrict__ idx,
+                                                             int32_t* __restrict__ pidx, int64_t rows)
+{
+    const int64_t row = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (row >= rows) return;
+    const int H = stl.H, K = stl.K;
+    const int t = (int)(row / H);
+    int s = 0;
+    {
+        int lo = 0, hi = stl.nseq - 1;          // last s with cu[s] <= t
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (stl.cu[mid] <= t) lo = mid; else hi = mid - 1;
+        }
+        s = lo;
+    }
+    const int tl = t - stl.cu[s];
+    const int il = tl / stl.B;                   // logical own block
+    const int pt = tl >> 7;                      // physical own block
+    const int32_t* in = idx + row * K;
+    int32_t* out = pidx + row * Kp;
+    int n = 0;
+    for (int p = 0; p < K; ++p) {
+        const int j = in[p];
+        if (j < 0 || j >= il) continue;
+        for (int c = 0; c < r && n < Kp; ++c) out[n++] = j * r + c;
+    }
+    for (int pb = il * r; pb < pt && n < Kp; ++pb) out[n++] = pb;
+    for (; n < Kp; ++n) out[n] = -1;
+}
+
 }  // namespace
+
+hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx)
+{
+    const int64_t rows = (int64_t)Ll.tokens * Ll.st.H;
+    if (rows == 0) return hipSuccess;
+    const int r = Ll.st.B / 128;
+    hipLaunchKernelGGL(expand_idx_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                       Ll.stream, Ll.st, r, Kp, idx, pidx, rows);
+    return hipGetLastError();
+}
 
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx)
 {

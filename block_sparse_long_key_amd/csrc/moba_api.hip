@@ -25,11 +25,19 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
     if (sh->heads < 1 || sh->seq < 0 || sh->batch < 1) return MOBA_ERR_INVALID_ARG;
     if (sh->dtype != MOBA_F32 && sh->dtype != MOBA_BF16) return MOBA_ERR_INVALID_ARG;
     if (sh->head_dim != 64 && sh->head_dim != 128) return MOBA_ERR_UNSUPPORTED;
-    if (sh->block_size != 64 && sh->block_size != 128) return MOBA_ERR_UNSUPPORTED;
+    if (sh->block_size != 64 && sh->block_size != 128 && sh->block_size != 256 &&
+        sh->block_size != 512)
+        return MOBA_ERR_UNSUPPORTED;
     if (sh->top_k < 1) return MOBA_ERR_INVALID_ARG;
     if (sh->top_k > 32) return MOBA_ERR_UNSUPPORTED;
-    // fp32 keeps a whole key block of K and V in LDS: B * d <= 8192
-    if (sh->dtype == MOBA_F32 && sh->head_dim * sh->block_size > 8192) return MOBA_ERR_UNSUPPORTED;
+    // blocks of 256 / 512 keys are attended as 2 / 4 blocks of 128: the
+    // expanded selection must fit 32 slots
+    if (sh->block_size > 128 && sh->top_k > 8) return MOBA_ERR_UNSUPPORTED;
+    // the fp32 router runs one thread per query of a block (<= 256)
+    if (sh->dtype == MOBA_F32 && sh->block_size > 256) return MOBA_ERR_UNSUPPORTED;
+    // fp32 keeps a whole (128-key) block of K and V in LDS: B * d <= 8192
+    const int att_b = sh->block_size < 128 ? sh->block_size : 128;
+    if (sh->dtype == MOBA_F32 && sh->head_dim * att_b > 8192) return MOBA_ERR_UNSUPPORTED;
 
     memset(L, 0, sizeof(*L));
     SegTable& st = L->st;
@@ -88,7 +96,9 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
 }
 
 // bwd: the backward's workspace (index + its own buffers, no forward partials)
-WsLayout layout(const Launch& L, bool bwd = false)
+// expand: the selection is re-expressed in 128-key blocks first (block
+// sizes 256 / 512); L is then the 128-key launch
+WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
 {
     WsLayout w;
     memset(&w, 0, sizeof(w));
@@ -112,6 +122,7 @@ WsLayout layout(const Launch& L, bool bwd = false)
         const size_t ent_rows = st.K > 1 ? (size_t)st.ebase[st.nseq] : 0;
         w.pq_bytes = (ent_rows + rows) * L.D * 4;
     }
+    if (expand) w.px_bytes = rows * st.K * 4;
     size_t off = 0;
     w.cmat_off = off;  off += align256(w.cmat_bytes);
     w.items_off = off; off += align256(w.items_bytes);
@@ -122,6 +133,7 @@ WsLayout layout(const Launch& L, bool bwd = false)
     w.lst_off = off;   off += align256(w.lst_bytes);
     w.rs_off = off;    off += align256(w.rs_bytes);
     w.pq_off = off;    off += align256(w.pq_bytes);
+    w.px_off = off;    off += align256(w.px_bytes);
     w.total = off;
     return w;
 }
@@ -130,9 +142,29 @@ moba_status hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_E
 
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 
-moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out, bool bwd = false)
+// The attention entry points work on 128-key blocks when the shape's blocks
+// are larger: Ll is the shape's own launch (routing granularity), La the
+// one the attention kernels run with (block 128, top_k * B / 128 slots).
+moba_status attn_launch(const moba_shape* sh, hipStream_t stream, Launch* Ll, Launch* La)
 {
-    *out = layout(L, bwd);
+    moba_status st = make_launch(sh, Ll, stream);
+    if (st != MOBA_OK) return st;
+    if (sh->block_size <= 128) {
+        *La = *Ll;
+        return MOBA_OK;
+    }
+    moba_shape p = *sh;
+    p.block_size = 128;
+    p.top_k = sh->top_k * (sh->block_size / 128);
+    return make_launch(&p, La, stream);
+}
+
+bool expands(const Launch& Ll) { return Ll.st.B > 128; }
+
+moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out, bool bwd = false,
+                     bool expand = false)
+{
+    *out = layout(L, bwd, expand);
     if (out->total > 0) {
         if (!ws || ((uintptr_t)ws & 255u) != 0) return MOBA_ERR_INVALID_ARG;
         if (bytes < out->total) return MOBA_ERR_WORKSPACE_TOO_SMALL;
@@ -172,16 +204,16 @@ int64_t moba_total_blocks(const moba_shape* shape)
 
 size_t moba_attn_fwd_workspace_bytes(const moba_shape* shape)
 {
-    Launch L;
-    if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
-    return layout(L).total;
+    Launch Ll, La;
+    if (attn_launch(shape, nullptr, &Ll, &La) != MOBA_OK) return 0;
+    return layout(La, false, expands(Ll)).total;
 }
 
 size_t moba_attn_bwd_workspace_bytes(const moba_shape* shape)
 {
-    Launch L;
-    if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
-    return layout(L, true).total;
+    Launch Ll, La;
+    if (attn_launch(shape, nullptr, &Ll, &La) != MOBA_OK) return 0;
+    return layout(La, true, expands(Ll)).total;
 }
 
 moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w, int32_t width,
@@ -247,30 +279,43 @@ moba_status moba_route_topk(const moba_shape* shape, const void* q, const float*
     return hip_status(launch_route(L, q, cent, idx));
 }
 
+// the index pass on the (possibly expanded) selection
+hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, char* wsp,
+                     const int32_t* idx)
+{
+    if (expands(Ll)) {
+        int32_t* px = (int32_t*)(wsp + ws.px_off);
+        hipError_t e = launch_expand_idx(Ll, La.st.K, idx, px);
+        if (e != hipSuccess) return e;
+        idx = px;
+    }
+    return launch_inv(La, ws, wsp, idx);
+}
+
 moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* workspace,
                             size_t workspace_bytes, hipStream_t stream)
 {
-    Launch L;
-    moba_status st = make_launch(shape, &L, stream);
+    Launch Ll, L;
+    moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
-    st = check_ws(L, workspace, workspace_bytes, &ws);
+    st = check_ws(L, workspace, workspace_bytes, &ws, false, expands(Ll));
     if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
-    return hip_status(launch_inv(L, ws, (char*)workspace, idx));
+    return hip_status(run_index(Ll, L, ws, (char*)workspace, idx));
 }
 
 moba_status moba_attn_routed(const moba_shape* shape, const void* q, const void* k, const void* v,
                              float softmax_scale, void* workspace, size_t workspace_bytes,
                              hipStream_t stream)
 {
-    Launch L;
-    moba_status st = make_launch(shape, &L, stream);
+    Launch Ll, L;
+    moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
-    st = check_ws(L, workspace, workspace_bytes, &ws);
+    st = check_ws(L, workspace, workspace_bytes, &ws, false, expands(Ll));
     if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
     return hip_status(launch_routed_attn(L, ws, (char*)workspace, q, k, v,
@@ -281,14 +326,14 @@ moba_status moba_attn_combine(const moba_shape* shape, const void* q, const void
                               const int32_t* idx, float softmax_scale, void* o, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    Launch L;
-    moba_status st = make_launch(shape, &L, stream);
+    Launch Ll, L;
+    moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o))
         return MOBA_ERR_INVALID_ARG;
     if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
-    st = check_ws(L, workspace, workspace_bytes, &ws);
+    st = check_ws(L, workspace, workspace_bytes, &ws, false, expands(Ll));
     if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
     return hip_status(launch_diag_combine(L, ws, (char*)workspace, q, k, v, idx,
@@ -312,8 +357,8 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, hipStream_t stream)
 {
-    Launch L;
-    moba_status st = make_launch(shape, &L, stream);
+    Launch Ll, L;
+    moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
     if (L.dtype != MOBA_BF16) return MOBA_ERR_UNSUPPORTED;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
@@ -327,10 +372,10 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
     }
     if (dq == dk || dq == dv || dk == dv) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
-    st = check_ws(L, workspace, workspace_bytes, &ws, true);
+    st = check_ws(L, workspace, workspace_bytes, &ws, true, expands(Ll));
     if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
-    hipError_t e = launch_inv(L, ws, (char*)workspace, idx);
+    hipError_t e = run_index(Ll, L, ws, (char*)workspace, idx);
     if (e != hipSuccess) return MOBA_ERR_HIP;
     return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout,
                                       resolve_scale(softmax_scale, L.D), dq, dk, dv));

@@ -122,6 +122,7 @@ struct WsLayout {
     size_t lst_off, lst_bytes;       // int2 [H][total blocks]: (first entry, count) of each list
     size_t rs_off, rs_bytes;         // backward: float2 [tokens][H] (lse in log2 units, dO . O)
     size_t pq_off, pq_bytes;         // backward: fp32 dq pieces, list order, then own-block rows
+    size_t px_off, px_bytes;         // block sizes > 128: int32 [tokens][H][K'] selection in 128-key blocks
     size_t total;
 };
 
@@ -140,6 +141,7 @@ hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W
                            const void* gk, void* dk, float* dw, float* dwp);
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx);
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx);
+hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
                               const void* q, const void* k, const void* v, float scale);
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,

@@ -780,25 +780,38 @@ hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_
     if (K <= 8) {
         hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
         hipLaunchKernelGGL((route_fix_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-    } else if (K <= 16) {
-        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+    } else if constexpr (BLK <= 128) {
+        // (blocks of 256 / 512 keys are limited to top_k <= 8 by the API)
+        if (K <= 16) {
+            hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+            hipLaunchKernelGGL((route_fix_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        } else {
+            hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
+            hipLaunchKernelGGL((route_fix_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        }
     } else {
-        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_b(const Launch& L, const void* q, const float* cent, int32_t* idx)
+{
+    switch (L.st.B) {
+        case 64: return launch_mfma<D, 64>(L, q, cent, idx);
+        case 128: return launch_mfma<D, 128>(L, q, cent, idx);
+        case 256: return launch_mfma<D, 256>(L, q, cent, idx);
+        case 512: return launch_mfma<D, 512>(L, q, cent, idx);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
-    if (L.dtype == MOBA_BF16) {
-        if (L.D == 64) return L.st.B == 64 ? launch_mfma<64, 64>(L, q, cent, idx)
-                                           : launch_mfma<64, 128>(L, q, cent, idx);
-        return L.st.B == 64 ? launch_mfma<128, 64>(L, q, cent, idx)
-                            : launch_mfma<128, 128>(L, q, cent, idx);
-    }
+    if (L.dtype == MOBA_BF16)
+        return L.D == 64 ? launch_mfma_b<64>(L, q, cent, idx) : launch_mfma_b<128>(L, q, cent, idx);
     return L.D == 64 ? launch_d<float, 64>(L, q, cent, idx)
                      : launch_d<float, 128>(L, q, cent, idx);
 }

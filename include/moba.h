@@ -40,9 +40,17 @@
  *     Nothing is printed, nothing throws.
  *   - Calls are stateless and may be issued from several host threads.
  *
- * Support matrix: head_dim 64 or 128; block_size 64 or 128; top_k 1..32;
- * conv width 1..8; dtype bf16 (fast path) or fp32 (correctness path);
- * num_seqs <= MOBA_MAX_SEQS (varlen); tokens * heads < 2^27 per call.
+ * Support matrix: head_dim 64 or 128; block_size 64, 128, 256 or 512
+ * (256 / 512: top_k <= 8, the summary page's MoBA-256 / MoBA-512 variants,
+ * "Configurazione MoBA"); top_k 1..32; conv width 1..8; dtype bf16 (fast
+ * path) or fp32 (correctness path; block_size * head_dim <= 8192 counting
+ * blocks above 128 as 128, block_size <= 256); num_seqs <= MOBA_MAX_SEQS
+ * (varlen); tokens * heads < 2^27 per call.
+ * Blocks of 256 / 512 keys: routing (centroids, scores, top-k) works on the
+ * blocks as given; the attention calls attend a selected block as its 2 / 4
+ * sub-blocks of 128 keys (the same key set, so the same result), with the
+ * query's own block split into the sub-blocks before its own sub-block and
+ * its own sub-block (token-causal).
  */
 #ifndef MOBA_H_
 #define MOBA_H_

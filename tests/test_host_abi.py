@@ -66,8 +66,23 @@ def test_total_blocks_and_workspace(lib):
     assert big >= s.batch * s.seq * s.heads * s.top_k * (s.head_dim * 2 + 4)
 
 
+def test_large_blocks_attend_as_128_key_blocks(lib):
+    # MoBA-256 / MoBA-512 shapes are accepted; their attention workspace is
+    # that of 128-key blocks with top_k * B / 128 slots plus the expanded
+    # selection, so even top_k = 1 (own block only) has routed lists
+    for B, K in ((256, 4), (512, 2), (256, 1)):
+        sh = _shape(batch=2, seq=4096, B=B, K=K)
+        assert lib.moba_total_blocks(ctypes.byref(sh)) == 2 * 4096 // B
+        ws = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh))
+        ref = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(_shape(batch=2, seq=4096, B=128,
+                                                                   K=K * B // 128)))
+        assert ws >= ref + 2 * 4096 * sh.heads * (K * B // 128) * 4
+        assert lib.moba_attn_bwd_workspace_bytes(ctypes.byref(sh)) > 0
+
+
 @pytest.mark.parametrize("kw,code", [
-    (dict(d=96), UNSUPPORTED), (dict(B=32), UNSUPPORTED), (dict(B=256), UNSUPPORTED),
+    (dict(d=96), UNSUPPORTED), (dict(B=32), UNSUPPORTED), (dict(B=1024), UNSUPPORTED),
+    (dict(B=256, K=9), UNSUPPORTED), (dict(dtype=0, B=512), UNSUPPORTED),
     (dict(K=0), INVALID), (dict(K=33), UNSUPPORTED), (dict(dtype=7), INVALID),
     (dict(heads=0), INVALID), (dict(batch=65), UNSUPPORTED),
     (dict(dtype=0, d=128, B=128), UNSUPPORTED),

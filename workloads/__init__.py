@@ -84,6 +84,12 @@ CONFIGS = {
                     "top-8 bf16, key conv W=4"),
     "H": Spec("H", 6, 2, 65536, 16, 64, 128, 8, "bf16",
               desc="b2 H16 N65536 d64 B128 top-8 bf16 (64K, B=128, top-8)"),
+    # the pages' larger-block variants at the same 7/8 sparsity (MoBA-256:
+    # B=256 k=4; MoBA-512: B=512 k=2), at the efficiency setting's shape
+    "M256": Spec("M256", 8, 2, 65536, 16, 64, 256, 4, "bf16",
+                 desc="b2 H16 N65536 d64 B256 top-4 bf16 (MoBA-256)"),
+    "M512": Spec("M512", 9, 2, 65536, 16, 64, 512, 2, "bf16",
+                 desc="b2 H16 N65536 d64 B512 top-2 bf16 (MoBA-512)"),
     # long context (the efficiency figure's longest sequence), not a SURVEY
     # config: one 512K sequence, 16 heads, d=64, B=128, top-8
     "L": Spec("L", 7, 1, 524288, 16, 64, 128, 8, "bf16",
