@@ -191,3 +191,45 @@ def test_key_conv_bwd_matches_oracle(name):
     print(f"[conv bwd {name}] dk max err {ek.max():.2e}  dw max err / max |dw| "
           f"{ew.max() / np.abs(rw).max():.2e}", flush=True)
     assert ew.max() <= 1e-5 * np.abs(rw).max()
+
+
+# ------------------------------------------------------- attention sink ----
+SINK_CASES = {
+    "sink-B128": _spec("H", seq=8192, heads=2, sink=True),
+    "sink-B64-varlen": _spec("C4", seqlens=(5000, 3000), heads=2, sink=True),
+}
+
+
+@pytest.mark.parametrize("name", list(SINK_CASES))
+def test_attention_sink_long_lists(name):
+    """Block 0 is selected by (nearly) every query, so its list holds ~all
+    queries of the sequence: several forward work items of one list and one
+    long backward list.  Selection, forward and backward against the
+    oracle."""
+    s = SINK_CASES[name]
+    print(f"[sink {name}] {s}", flush=True)
+    x = workloads.make(s)
+    cu = workloads.segments(s)
+    B, K, H, d = s.block_size, s.top_k, s.heads, s.head_dim
+    ref = oracle.forward(x["q"], x["k"], x["v"], B, K, cu)
+    sel0 = np.mean([(ref["idx"][cu[i] + B:cu[i + 1]] == 0).any(-1).mean()
+                    for i in range(len(cu) - 1)])
+    assert sel0 > 0.95, f"sink not formed ({sel0:.2f})"
+    m = moba()
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    cus = x["cu_seqlens"]
+    cent = m.moba_centroids(k, B, cus)
+    idx = m.moba_route_topk(q, cent, B, K, cus)
+    torch.cuda.synchronize()
+    from test_parity_gpu import _check_idx, _check_o
+    _check_idx(idx.cpu().numpy().reshape(-1, H, K), ref["idx"], ref["gap_a"], ref["gap_b"],
+               ref["exempt"], name)
+    idx_ref = torch.from_numpy(ref["idx"]).reshape(tuple(q.shape[:-1]) + (K,)).to(DEV)
+    o, lse = m.moba_attn_fwd(q, k, v, idx_ref, B, K, cu_seqlens=cus)
+    do = workloads.grad_output(s)
+    dq, dk, dv = m.moba_attn_bwd(q, k, v, idx_ref, o, lse, do.to(DEV), B, K, cu_seqlens=cus)
+    torch.cuda.synchronize()
+    _check_o(o, lse, ref["o"], ref["lse"], s.dtype, what=name)
+    rq, rk, rv = oracle.attend_bwd(x["q"], x["k"], x["v"], ref["idx"], do, B, K, cu)
+    for g_, r_, w_ in zip((dq, dk, dv), (rq, rk, rv), ("dq", "dk", "dv")):
+        _check(name, _np(g_).reshape(-1, H, d), r_, w_)

@@ -45,6 +45,7 @@ class Spec:
     conv_width: int = 0       # 0 = no key convolution
     seqlens: Optional[tuple] = None   # varlen lengths (batch must be 1)
     plant: bool = False       # C3's planted per-query-block signal
+    sink: bool = False        # every query's router favours block 0 (attention sink)
     desc: str = ""
 
     @property
@@ -131,6 +132,25 @@ def _plant(q: torch.Tensor, k: torch.Tensor, s: Spec, g: torch.Generator):
                     k[b, j * B:(j + 1) * B, h, :] += 0.5 * qhat
 
 
+def _sink(q: torch.Tensor, k: torch.Tensor, s: Spec, g: torch.Generator):
+    """Attention-sink structure: one random unit direction u per head; every
+    query gets +2u and every key of block 0 of each sequence gets +4u, so
+    block 0 has the highest router score for (nearly) every query and its
+    key-block list holds (nearly) all queries of the sequence."""
+    u = torch.randn((s.heads, s.head_dim), generator=g, dtype=torch.float32)
+    u = u / u.norm(dim=-1, keepdim=True)
+    q += 2.0 * u
+    B = s.block_size
+    if s.seqlens is not None:
+        starts = [0]
+        for l in s.seqlens[:-1]:
+            starts.append(starts[-1] + l)
+        for a, l in zip(starts, s.seqlens):
+            k[a:a + min(B, l)] += 4.0 * u
+    else:
+        k[:, :B] += 4.0 * u
+
+
 def make(s, seed: Optional[int] = None, device="cpu"):
     """Draw the inputs of config `s` (a Spec or a config name).
 
@@ -154,6 +174,8 @@ def make(s, seed: Optional[int] = None, device="cpu"):
                         dtype=torch.float32) * math.sqrt(1.0 / s.conv_width)
     if s.plant:
         _plant(q, k, s, g)
+    if s.sink:
+        _sink(q, k, s, g)
     dt = s.torch_dtype
     out = {
         "q": q.to(dt).to(device),
