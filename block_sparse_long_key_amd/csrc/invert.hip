@@ -18,9 +18,10 @@
 //              stored head-major [H][tokens][K] so both its writer and its
 //              reader (one query block of one head) touch contiguous runs.
 // The own block is not listed (the own-block kernel handles it); -1 and
-// out-of-range ids are skipped.  Order inside a list is not deterministic,
-// which the routed attention does not depend on (each row of a tile is
-// computed independently).
+// out-of-range ids are skipped.  Order inside a list: the forward's fast
+// placement depends on wave timing, which the routed attention does not
+// depend on (each row of a tile is computed independently); the backward
+// asks for a placement that depends only on idx (see inv_scatter_kernel).
 #include "moba_internal.h"
 
 namespace moba {
@@ -29,6 +30,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kScanThreads = 1024;
 constexpr int kBatch = 16;        // idx words loaded ahead per thread
+// largest blocks per sequence for the repeatable scatter (4 x 4 B of LDS
+// cursors per block: 64 KB)
+constexpr int kDetMaxBlocks = 4096;
 
 // entry e -> token row e / K by a multiply-high with M = ceil(2^32 / K):
 // e M / 2^32 exceeds e / K by less than e / 2^32, and the fractional part of
@@ -165,6 +169,14 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
     }
 }
 
+// DET = false: LDS cursors shared by the 4 waves (entries of one list land
+// in an order that depends on wave timing; the forward does not depend on
+// it).  DET = true: each wave owns a contiguous quarter of the chunk's
+// tokens and its own cursors, based at the chunk position plus the counts of
+// the earlier waves (a counting pass first), so every entry's position
+// depends only on the idx contents -- the backward sums its list-ordered
+// rows into dK / dV, which are then bitwise repeatable.
+template <bool DET>
 __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ cmat,
                                                               uint32_t* __restrict__ entries,
@@ -178,8 +190,6 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     const int B = st.B, K = st.K, H = st.H;
     const int ib0 = cl * kInvChunkBlocks, ib1 = min(n, ib0 + kInvChunkBlocks);
     const int32_t* pos = cm_base(st, const_cast<int32_t*>(cmat), s, h) + (int64_t)cl * n;
-    for (int j = threadIdx.x; j < ib1; j += kThreads) cur[j] = pos[j];
-    __syncthreads();
     uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K;
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);
     const int nent = (tl1 - tl0) * K;
@@ -188,30 +198,71 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     // one contiguous run, written in order
     int32_t* rv = rev + ((size_t)h * st.cu[st.nseq] + t0 + tl0) * K;
     const Div div(K, B);
-    for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // DET: wave w takes entries [e_lo, e_hi) (whole tokens), lanes stride 64
+    const int ntok = tl1 - tl0, tpw = (ntok + 3) / 4;
+    const int e_lo = DET ? min(ntok, wave * tpw) * K : 0;
+    const int e_hi = DET ? min(ntok, (wave + 1) * tpw) * K : nent;
+    const int first = DET ? e_lo + lane : threadIdx.x;
+    constexpr int STEP = DET ? 64 : kThreads;
+    int32_t* wc = DET ? cur + wave * ib1 : cur;        // this wave's cursors
+    if constexpr (DET) {
+        for (int j = threadIdx.x; j < 4 * ib1; j += kThreads) cur[j] = 0;
+        __syncthreads();
+        for (int e0 = first; e0 < e_hi; e0 += STEP * kBatch) {
+            int jv[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + u * STEP;
+                const int r = div.row(e), slot = e - r * K;
+                jv[u] = e < e_hi ? src[(size_t)r * H * K + slot] : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int e = e0 + u * STEP;
+                const int i = div.block(tl0 + div.row(e));
+                if (e < e_hi && jv[u] >= 0 && jv[u] < i) atomicAdd(&wc[jv[u]], 1);
+            }
+        }
+        __syncthreads();
+        // cursors: chunk position + counts of the earlier waves
+        for (int j = threadIdx.x; j < ib1; j += kThreads) {
+            int run = pos[j];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const int t = cur[w * ib1 + j];
+                cur[w * ib1 + j] = run;
+                run += t;
+            }
+        }
+    } else {
+        for (int j = threadIdx.x; j < ib1; j += kThreads) cur[j] = pos[j];
+    }
+    __syncthreads();
+    for (int e0 = first; e0 < e_hi; e0 += STEP * kBatch) {
         int jv[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int e = e0 + u * kThreads;
+            const int e = e0 + u * STEP;
             const int r = div.row(e), slot = e - r * K;
-            jv[u] = e < nent ? src[(size_t)r * H * K + slot] : -1;
+            jv[u] = e < e_hi ? src[(size_t)r * H * K + slot] : -1;
         }
         // all LDS cursor bumps of the batch first, then the stores
         int pv[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int e = e0 + u * kThreads;
+            const int e = e0 + u * STEP;
             const int i = div.block(tl0 + div.row(e));
-            pv[u] = (e < nent && jv[u] >= 0 && jv[u] < i) ? atomicAdd(&cur[jv[u]], 1) : -1;
+            pv[u] = (e < e_hi && jv[u] >= 0 && jv[u] < i) ? atomicAdd(&wc[jv[u]], 1) : -1;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            const int e = e0 + u * kThreads;
+            const int e = e0 + u * STEP;
             const int r = div.row(e), slot = e - r * K;
             if (pv[u] >= 0) ent[pv[u]] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
             // every slot is written, so each query's K positions form one
             // contiguous, fully written record
-            if (e < nent) rv[e] = pv[u];
+            if (e < e_hi) rv[e] = pv[u];
         }
     }
 }
@@ -266,7 +317,7 @@ hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32
     return hipGetLastError();
 }
 
-hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx)
+hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx, bool det)
 {
     const SegTable& st = L.st;
     if (st.K <= 1 || st.total_chunks == 0) return hipSuccess;
@@ -285,8 +336,13 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
                        L.stream, st, cmat, items, lst);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(inv_scatter_kernel, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx,
-                       cmat, ent, rev);
+    // the repeatable placement keeps 4 cursor sets in LDS
+    if (det && maxn <= kDetMaxBlocks)
+        hipLaunchKernelGGL(inv_scatter_kernel<true>, gc, dim3(kThreads), (size_t)maxn * 16, L.stream, st, idx,
+                           cmat, ent, rev);
+    else
+        hipLaunchKernelGGL(inv_scatter_kernel<false>, gc, dim3(kThreads), (size_t)maxn * 4, L.stream, st, idx,
+                           cmat, ent, rev);
     return hipGetLastError();
 }
 

@@ -281,7 +281,7 @@ moba_status moba_route_topk(const moba_shape* shape, const void* q, const float*
 
 // the index pass on the (possibly expanded) selection
 hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, char* wsp,
-                     const int32_t* idx)
+                     const int32_t* idx, bool det = false)
 {
     if (expands(Ll)) {
         int32_t* px = (int32_t*)(wsp + ws.px_off);
@@ -289,7 +289,7 @@ hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, cha
         if (e != hipSuccess) return e;
         idx = px;
     }
-    return launch_inv(La, ws, wsp, idx);
+    return launch_inv(La, ws, wsp, idx, det);
 }
 
 moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* workspace,
@@ -375,7 +375,8 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
     st = check_ws(L, workspace, workspace_bytes, &ws, true, expands(Ll));
     if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
-    hipError_t e = run_index(Ll, L, ws, (char*)workspace, idx);
+    // repeatable list order: dK / dV sum each list's rows in that order
+    hipError_t e = run_index(Ll, L, ws, (char*)workspace, idx, true);
     if (e != hipSuccess) return MOBA_ERR_HIP;
     return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout,
                                       resolve_scale(softmax_scale, L.D), dq, dk, dv));

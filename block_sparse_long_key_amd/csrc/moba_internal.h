@@ -140,7 +140,9 @@ hipError_t launch_conv_pool(const Launch& L, const void* k, const float* w, int 
 hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W, int mode,
                            const void* gk, void* dk, float* dw, float* dwp);
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx);
-hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx);
+// det: place each list's entries in an order that depends only on idx
+hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
+                      bool det = false);
 hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
                               const void* q, const void* k, const void* v, float scale);

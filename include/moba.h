@@ -224,7 +224,9 @@ moba_status moba_attn_combine(const moba_shape *shape, const void *q,
  *   products as bf16, every sum is fp32, outputs are rounded once.
  *   workspace: at least moba_attn_bwd_workspace_bytes(), 256-byte aligned,
  *   scratch on exit; it holds the inverted lists and one fp32 dq piece per
- *   routed (query, slot) pair, so the result is deterministic (no atomics).
+ *   routed (query, slot) pair.  No atomics on results: dq, dk and dv are
+ *   bitwise repeatable (dk / dv for sequences of up to 4096 blocks; longer
+ *   ones may differ between runs by fp32 summation order).
  *   Same error behaviour as moba_attn_fwd.
  */
 moba_status moba_attn_bwd(const moba_shape *shape, const void *q,
