@@ -394,11 +394,14 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     }
 
     // per-lane key lists (descending); the low LB mantissa bits of a key
-    // carry the block id j < i.  A lane keeps LL = KMAX - 1 keys (slot
-    // KMAX - 1 stays -inf): the query's top K is exact unless one lane holds
+    // carry the block id j < i.  A lane keeps LL < KMAX keys (slots LL..
+    // KMAX - 1 stay -inf): the query's top K is exact unless one lane holds
     // more than LL of it, which the merge detects (a lane's last kept key
     // above the merged K-th) and sends to the fp64 path.
-    constexpr int LL = KMAX - 1;
+    // (measured: with k = 8 every slot pays for itself -- 6 slots send too
+    // many rows to fp64; with k = 16 a lane holds more than 13 of the top k
+    // too rarely to matter, and 13 slots route C4 7 % faster)
+    constexpr int LL = KMAX >= 16 ? KMAX - 3 : KMAX - 1;
     float key[2][KMAX];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
