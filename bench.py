@@ -165,7 +165,7 @@ def main():
                 ev[i].record(stream)
         mark(0)
         if w is not None:
-            moba.moba_key_conv(k, w, B, "plain", cu, with_centroids=True, out=kc, cent=cent)
+            moba.moba_key_conv(k, w, B, spec.conv_mode, cu, with_centroids=True, out=kc, cent=cent)
             kk = kc
         else:
             moba.moba_centroids(k, B, cu, out=cent)
@@ -222,7 +222,8 @@ def main():
         "config": {"workload": f"moba_fwd {spec.name}: {spec.desc}",
                    "batch": spec.batch, "seq_len": spec.seq, "heads": spec.heads,
                    "head_dim": spec.head_dim, "block_size": B, "top_k": K,
-                   "key_conv_width": spec.conv_width, "F_eff": fl["total"]},
+                   "key_conv_width": spec.conv_width, "key_conv_mode": spec.conv_mode,
+                   "F_eff": fl["total"]},
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()},
         "event_ms_per_step": round(sum(ms_steps) / len(ms_steps), 4),
@@ -266,7 +267,7 @@ def bench_bwd(args, moba):
     do = workloads.grad_output(spec).to(dev)
     cu = x["cu_seqlens"]
     B, K = spec.block_size, spec.top_k
-    o, lse, idx, kk = moba.moba_fwd(q, k, v, B, K, conv_w=w, cu_seqlens=cu)
+    o, lse, idx, kk = moba.moba_fwd(q, k, v, B, K, conv_w=w, conv_mode=spec.conv_mode, cu_seqlens=cu)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(256, moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
                      dtype=torch.uint8, device=dev)
@@ -283,7 +284,7 @@ def bench_bwd(args, moba):
                            out=(dq, dk, dv))
         if w is not None:
             # dL/dk' -> dL/dk and dL/dw through the key convolution
-            moba.moba_key_conv_bwd(k, w, dk, B, "plain", cu_seqlens=cu, workspace=wsc)
+            moba.moba_key_conv_bwd(k, w, dk, B, spec.conv_mode, cu_seqlens=cu, workspace=wsc)
 
     for _ in range(args.warmup):
         step()

@@ -296,12 +296,14 @@ def test_scale_override_and_null_lse():
 
 
 # ------------------------------------------------- full size, sampled ----
-@pytest.mark.parametrize("name", ["H", "C3", "C4", "C5", "L"])
+@pytest.mark.parametrize("name", ["H", "C3", "C4", "C5", "L", "M256", "M512", "H5"])
 def test_full_size_sampled(name):
     """Every workload at its full size (H: 64K x 2 x 16 heads, d=64, B=128,
     top-8; C3 with key conv and the planted signal; C4 with B=64, top-16;
-    C5 varlen with d=128 and key conv; L: one 512K sequence): selection and
-    output checked on a seeded sample of rows; invariants on every row."""
+    C5 varlen with d=128 and key conv; L: one 512K sequence; M256 / M512:
+    B=256 top-4 and B=512 top-2; H5: the kconv5 k + SiLU(conv) form):
+    selection and output checked on a seeded sample of rows; invariants on
+    every row."""
     s = workloads.spec(name)
     print(f"[full {s.name}] {s}", flush=True)
     x = workloads.make(s)
@@ -309,7 +311,7 @@ def test_full_size_sampled(name):
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     w = None if x["conv_w"] is None else x["conv_w"].to(DEV)
     o, lse, idx, kk = moba().moba_fwd(q, k, v, s.block_size, s.top_k, conv_w=w,
-                                      cu_seqlens=x["cu_seqlens"])
+                                      conv_mode=s.conv_mode, cu_seqlens=x["cu_seqlens"])
     torch.cuda.synchronize()
     H, K, B = s.heads, s.top_k, s.block_size
     T = int(cu[-1])
@@ -329,7 +331,8 @@ def test_full_size_sampled(name):
         g.integers(0, T * H, 1500), np.arange(0, 16), T * H - 1 - np.arange(0, 16)]))
     kc = x["k"]
     if x["conv_w"] is not None:
-        kc = oracle.key_conv(x["k"], x["conv_w"], cu, mode=0, round_bf16=True)
+        kc = oracle.key_conv(x["k"], x["conv_w"], cu, mode=0 if s.conv_mode == "plain" else 1,
+                             round_bf16=True)
     cent = oracle.centroids(kc, B, cu)
     ri, ga, gb, ex = oracle.route_rows(x["q"], cent, B, K, cu, rows)
     gidx = idx.cpu().numpy().reshape(-1, K)

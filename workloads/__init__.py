@@ -43,6 +43,7 @@ class Spec:
     top_k: int
     dtype: str                # "f32" | "bf16"
     conv_width: int = 0       # 0 = no key convolution
+    conv_mode: str = "plain"  # "plain" or "silu_residual" (k + SiLU(conv), the page's form)
     seqlens: Optional[tuple] = None   # varlen lengths (batch must be 1)
     plant: bool = False       # C3's planted per-query-block signal
     sink: bool = False        # every query's router favours block 0 (attention sink)
@@ -91,6 +92,11 @@ CONFIGS = {
                  desc="b2 H16 N65536 d64 B256 top-4 bf16 (MoBA-256)"),
     "M512": Spec("M512", 9, 2, 65536, 16, 64, 512, 2, "bf16",
                  desc="b2 H16 N65536 d64 B512 top-2 bf16 (MoBA-512)"),
+    # the pages' best-quality variant "MoBA-128 + kconv5": the key conv in
+    # the page's k + SiLU(conv) form with W = 5, at the efficiency shape
+    "H5": Spec("H5", 10, 2, 65536, 16, 64, 128, 8, "bf16", conv_width=5,
+               conv_mode="silu_residual",
+               desc="b2 H16 N65536 d64 B128 top-8 bf16, key conv W=5 k+SiLU(conv) (kconv5)"),
     # long context (the efficiency figure's longest sequence), not a SURVEY
     # config: one 512K sequence, 16 heads, d=64, B=128, top-8
     "L": Spec("L", 7, 1, 524288, 16, 64, 128, 8, "bf16",
