@@ -312,10 +312,7 @@ struct Wave2 {
 // A partial-output row is stored permuted so that each lane's values are
 // contiguous: dim 16*dt + 4*g + r (the O^T accumulator layout) lives at
 // g*(D/4) + 4*dt + r.  Lane g reads / writes D/4 consecutive elements.
-// NT: a global partial row, written with the non-temporal hint (it is read
-// back only by the merge kernel, much later; keeping it out of the way in L2
-// leaves room for the gathered query rows, which other lists reuse)
-template <typename T, int NDT, bool NT = false>
+template <typename T, int NDT>
 __device__ __forceinline__ void store_lane_row(T* p, const float (&x)[NDT][4])
 {
     if constexpr (sizeof(T) == 2) {
@@ -327,15 +324,12 @@ __device__ __forceinline__ void store_lane_row(T* p, const float (&x)[NDT][4])
                 const int dt = 2 * c + e / 2, r = 2 * (e % 2);
                 w[e] = pack_bf16x2(x[dt][r], x[dt][r + 1]);
             }
-            if constexpr (NT) __builtin_nontemporal_store(w, (u32x4_t*)(p + 8 * c));
-            else *(u32x4_t*)(p + 8 * c) = w;
+            *(u32x4_t*)(p + 8 * c) = w;
         }
     } else {
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            const f32x4_t w = {x[dt][0], x[dt][1], x[dt][2], x[dt][3]};
-            if constexpr (NT) __builtin_nontemporal_store(w, (f32x4_t*)(p + 4 * dt));
-            else *(f32x4_t*)(p + 4 * dt) = w;
+            *(f32x4_t*)(p + 4 * dt) = f32x4_t{x[dt][0], x[dt][1], x[dt][2], x[dt][3]};
         }
     }
 }
@@ -499,13 +493,22 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
                     const int qc = 64 * n + lane, r = qc / CPR, c = qc % CPR;
                     const u32x4_t w = *(const u32x4_t*)(st_w + r * RS + c * 16);
                     if (row0 + r < it.count)
+                        // whole rows, non-temporal: read back only by the merge
+                        // kernel, much later; kept out of the way in L2 they
+                        // leave room for the gathered query rows other lists
+                        // reuse (routed reads 1.76 -> 1.40 GB at 2 x 64K)
                         __builtin_nontemporal_store(w, (u32x4_t*)((char*)po + (size_t)(e0 + row0 + r) * RB + c * 16));
                 }
             } else {
-                if (ok[sb]) store_lane_row<T, NDT, true>(po + prow * D + g4 * (D / 4), x);
+                // (64-byte pieces of rows: a non-temporal hint would skip the
+                // L2 merge of the pieces -- measured 2x slower at d = 128)
+                if (ok[sb]) store_lane_row<T, NDT>(po + prow * D + g4 * (D / 4), x);
             }
-            if (ok[sb] && g4 == 0)
-                __builtin_nontemporal_store(m2[sb] + __builtin_amdgcn_logf(sum[sb]), pl + prow);
+            if (ok[sb] && g4 == 0) {
+                const float lv = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+                if constexpr (STAGE) __builtin_nontemporal_store(lv, pl + prow);
+                else pl[prow] = lv;
+            }
         }
     }
 }
