@@ -234,10 +234,6 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 // provably the only blocks that can still be selected, the row carries them
 // (K fp64 re-scorings); otherwise the row is marked for an fp64 re-scoring
 // of every past block.
-__device__ __forceinline__ bool ranks_before(float sa, int ja, float sb, int jb)
-{
-    return sa > sb || (sa == sb && ja < jb);
-}
 __device__ __forceinline__ bool ranks_before64(double sa, int ja, double sb, int jb)
 {
     return sa > sb || (sa == sb && ja < jb);
@@ -409,7 +405,6 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         for (int p = 0; p < KMAX; ++p) key[sb][p] = -INFINITY;
     const int LB = 32 - __builtin_clz((unsigned)(i - 1) | 1u);
     const uint32_t lmask = (1u << LB) - 1u;
-    const float kdel = ldexpf(1.0f, LB - 23) * 1.01f;
     float cmax2 = 0.f;                      // max |c|^2 over the past blocks
 
     // score one group of 16 blocks (LDS rows 16*bt..) against both sub-tiles
@@ -443,20 +438,26 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                 for (int r = 0; r < 4; ++r)
                     acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
             }
+            // keys: the scores with their low LB mantissa bits replaced by j.
+            // A key at or below the lane's last kept key changes nothing, so
+            // each insertion runs only where some lane's key passes the
+            // threshold of the group's start (the wave skips it otherwise)
             const float thr = key[sb][LL - 1];
-            const float mx = fmax2(fmax2(acc[0], acc[1], pinf), fmax2(acc[2], acc[3], pinf), pinf);
-            // a key exceeds its score by at most 2^(LB-23)|s|: skip the
-            // group only when no key can reach the list
-            if (__builtin_fmaf(fabsf(mx), kdel, mx) >= thr) {
+            float x[4];
+            bool pass[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    // key: the score with its low LB mantissa bits replaced by j
-                    const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
-                    const float x = __uint_as_float((__float_as_uint(acc[r]) & ~lmask) | j);
+            for (int r = 0; r < 4; ++r) {
+                const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
+                x[r] = __uint_as_float((__float_as_uint(acc[r]) & ~lmask) | j);
+                pass[r] = x[r] > thr;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (pass[r]) {
 #pragma unroll
                     for (int p = LL - 1; p >= 1; --p)
-                        key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x);
-                    key[sb][0] = fmax2(key[sb][0], x, pinf);
+                        key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x[r]);
+                    key[sb][0] = fmax2(key[sb][0], x[r], pinf);
                 }
             }
         }
