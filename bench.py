@@ -132,7 +132,7 @@ def main():
                          "known-size kernel for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
 
     import block_sparse_long_key_amd as moba

@@ -97,8 +97,8 @@ CONFIGS = {
     "H5": Spec("H5", 10, 2, 65536, 16, 64, 128, 8, "bf16", conv_width=5,
                conv_mode="silu_residual",
                desc="b2 H16 N65536 d64 B128 top-8 bf16, key conv W=5 k+SiLU(conv) (kconv5)"),
-    # long context (the efficiency figure's longest sequence), not a SURVEY
-    # config: one 512K sequence, 16 heads, d=64, B=128, top-8
+    # long context (the efficiency figure's longest sequence): one 512K
+    # sequence, 16 heads, d=64, B=128, top-8
     "L": Spec("L", 7, 1, 524288, 16, 64, 128, 8, "bf16",
               desc="b1 H16 N524288 d64 B128 top-8 bf16 (512K long context)"),
 }
