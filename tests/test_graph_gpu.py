@@ -1,0 +1,61 @@
+"""The library's calls only enqueue kernels (no allocation, memset or
+synchronisation), so a whole forward and backward can be captured in a HIP
+graph and replayed.  Each replay, with eager work and synchronisations in
+between, must equal the eager result bitwise (both passes are
+deterministic)."""
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def test_forward_and_backward_replay_from_a_graph():
+    import block_sparse_long_key_amd as moba
+    s = workloads.spec("H").scaled(4096, "-graph")
+    x = workloads.make(s)
+    B, K = s.block_size, s.top_k
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    do = workloads.grad_output(s).to(DEV)
+    nb = moba.moba_total_blocks(q, B)
+    cent = torch.empty((nb, s.heads, s.head_dim), dtype=torch.float32, device=DEV)
+    idx = torch.empty(q.shape[:-1] + (K,), dtype=torch.int32, device=DEV)
+    o = torch.empty_like(q)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    wsf = torch.empty(moba.moba_attn_fwd_workspace_bytes(q, B, K), dtype=torch.uint8, device=DEV)
+    wsb = torch.empty(moba.moba_attn_bwd_workspace_bytes(q, B, K), dtype=torch.uint8, device=DEV)
+    state = {}
+
+    def step():
+        moba.moba_centroids(k, B, out=cent)
+        moba.moba_route_topk(q, cent, B, K, out=idx)
+        _, lse = moba.moba_attn_fwd(q, k, v, idx, B, K, workspace=wsf, out=o)
+        state["lse"] = lse
+        moba.moba_attn_bwd(q, k, v, idx, o, lse, do, B, K, workspace=wsb, out=grads)
+
+    # eager reference (also warms up the library on this stream)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (idx, o, state["lse"], *grads)]
+
+    g = torch.cuda.CUDAGraph()
+    for t in (idx, o, *grads):
+        t.zero_()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (idx, o, *grads):
+            t.fill_(7)                       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [idx, o, state["lse"], *grads]
+        for a, b, name in zip(got, ref, ("idx", "o", "lse", "dq", "dk", "dv")):
+            assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
