@@ -11,7 +11,9 @@ the calls raise -- there is no CPU fallback.
 Names follow the C ABI: ``moba_key_conv``, ``moba_centroids``,
 ``moba_route_topk``, ``moba_attn_fwd`` (plus its three stages
 ``moba_attn_index``, ``moba_attn_routed``, ``moba_attn_combine``), the
-convenience ``moba_fwd`` that chains them, and ``moba_attn_bwd``.
+convenience ``moba_fwd`` that chains them, ``moba_attn_bwd`` and
+``moba_key_conv_bwd``, and ``moba_attention``: the whole layer as a
+differentiable op (torch autograd glue around the same calls).
 
 Tensors are ``[batch, seq, heads, head_dim]`` (uniform batch) or
 ``[total_tokens, heads, head_dim]`` with ``cu_seqlens`` (a python list or CPU
@@ -30,7 +32,7 @@ __all__ = [
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
     "moba_attn_fwd_workspace_bytes", "moba_total_blocks", "library_path",
     "moba_attn_bwd", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
-    "moba_key_conv_bwd_workspace_bytes",
+    "moba_key_conv_bwd_workspace_bytes", "moba_attention",
     "MobaError",
 ]
 
@@ -366,3 +368,42 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                                _stream(stream))
     _check(rc, "moba_attn_bwd")
     return dq, dk, dv
+
+
+class _MobaAttention(torch.autograd.Function):
+    """Autograd glue: the forward is moba_fwd, the backward moba_attn_bwd
+    (then moba_key_conv_bwd when a key convolution ran).  The block
+    selection is piecewise constant in q and k, so no gradient reaches the
+    router."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale):
+        o, lse, idx, kk = moba_fwd(q, k, v, block_size, top_k, conv_w, conv_mode,
+                                   cu_seqlens, scale)
+        ctx.save_for_backward(q, k, v, conv_w, o, lse, idx, kk)
+        ctx.cfg = (block_size, top_k, conv_mode, cu_seqlens, scale)
+        ctx.mark_non_differentiable(lse)
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, _dlse):
+        q, k, v, conv_w, o, lse, idx, kk = ctx.saved_tensors
+        block_size, top_k, conv_mode, cu_seqlens, scale = ctx.cfg
+        dq, dkk, dv = moba_attn_bwd(q, kk, v, idx, o, lse, do.contiguous(), block_size, top_k,
+                                    scale, cu_seqlens)
+        dk, dw = dkk, None
+        if conv_w is not None:
+            dk, dw = moba_key_conv_bwd(k, conv_w, dkk, block_size, conv_mode, cu_seqlens)
+        return dq, dk, dv, dw, None, None, None, None, None
+
+
+def moba_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
+                   top_k: int, conv_w: Optional[torch.Tensor] = None,
+                   conv_mode: str = "plain", cu_seqlens=None,
+                   scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MoBA attention as a differentiable op: returns (o, lse).
+
+    Gradients flow to q, k, v and the conv filter (bf16 backward; the
+    selection itself carries none).
+    """
+    return _MobaAttention.apply(q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale)

@@ -229,3 +229,50 @@ def test_attention_sink_long_lists(name):
     rq, rk, rv = oracle.attend_bwd(x["q"], x["k"], x["v"], ref["idx"], do, B, K, cu)
     for g_, r_, w_ in zip((dq, dk, dv), (rq, rk, rv), ("dq", "dk", "dv")):
         _check(name, _np(g_).reshape(-1, H, d), r_, w_)
+
+
+# ------------------------------------------------------- autograd wrapper --
+@pytest.mark.parametrize("conv", [None, "plain"])
+def test_autograd_wrapper_matches_the_oracle(conv):
+    """moba_attention as a torch autograd op: o.backward(dO) gives the
+    oracle's gradients for q, v, k (through the key conv when there is one)
+    and the conv filter.  (The plain conv's k' is bit-exact, so the GPU's own
+    selection equals the oracle's; the k + SiLU form's gradient is checked
+    in the conv tests above.)"""
+    s = _spec("H", seq=2048, heads=2)
+    if conv is not None:
+        s = dataclasses.replace(s, conv_width=3, conv_mode=conv)
+    x = workloads.make(s)
+    cu = workloads.segments(s)
+    B, K, H, d = s.block_size, s.top_k, s.heads, s.head_dim
+    do = workloads.grad_output(s)
+    m = moba()
+    q, k, v = (x[n].to(DEV).requires_grad_() for n in ("q", "k", "v"))
+    w = None if x["conv_w"] is None else x["conv_w"].to(DEV).requires_grad_()
+    o, lse = m.moba_attention(q, k, v, B, K, conv_w=w, conv_mode=s.conv_mode)
+    o.backward(do.to(DEV))
+    torch.cuda.synchronize()
+    mode = 0 if s.conv_mode == "plain" else 1
+    ref = oracle.forward(x["q"], x["k"], x["v"], B, K, cu, conv_w=x["conv_w"], conv_mode=mode)
+    gi = m.moba_route_topk(q.detach(), m.moba_centroids(
+        m.moba_key_conv(k.detach(), w.detach(), B, s.conv_mode) if w is not None else k.detach(), B),
+        B, K)
+    assert np.array_equal(gi.cpu().numpy().reshape(ref["idx"].shape), ref["idx"])
+    rq, rkk, rv = oracle.attend_bwd(x["q"], ref["k_conv"], x["v"], ref["idx"], do, B, K, cu)
+    _check(f"autograd-{conv}", _np(q.grad).reshape(-1, H, d), rq, "dq")
+    _check(f"autograd-{conv}", _np(v.grad).reshape(-1, H, d), rv, "dv")
+    if w is None:
+        _check(f"autograd-{conv}", _np(k.grad).reshape(-1, H, d), rkk, "dk")
+        return
+    # chain through the conv from the oracle's dk'.  The GPU rounds dk' to
+    # bf16 before the conv backward and dk again after it: two roundings,
+    # so twice the single-rounding bar
+    rk, rw = oracle.key_conv_bwd(x["k"], x["conv_w"].numpy(), rkk.astype(np.float32), cu, mode)
+    gk = _np(k.grad).reshape(-1, H, d).astype(np.float64)
+    ek = np.abs(gk - rk)
+    print(f"[autograd-{conv}] dk max {ek.max() / np.abs(rk).max():.2e} "
+          f"mean {ek.mean() / np.abs(rk).mean():.2e}", flush=True)
+    assert ek.max() <= 2 * MAX_REL * np.abs(rk).max()
+    assert ek.mean() <= 2 * MEAN_REL * np.abs(rk).mean()
+    ew = np.abs(w.grad.cpu().numpy() - rw)
+    assert ew.max() <= 1e-2 * np.abs(rw).max(), ew.max()
