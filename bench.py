@@ -54,17 +54,19 @@ def _traffic(per_launch_algo_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, x, nthreads=None):
+def cpu_baseline(spec, x, nthreads=None, max_slices=32):
     """The CPU oracle (as it stands) on a bounded sample: the first
-    `nthreads` (sequence, head) slices of the workload, each a full forward
-    of one head of one sequence, run one slice per thread."""
+    `max_slices` (sequence, head) slices of the workload (all 32 at the
+    default workload, i.e. the whole forward), each a full forward of one
+    head of one sequence, on up to 16 threads (one slice per thread at a
+    time)."""
     import numpy as np
 
     import oracle
 
     avail = len(os.sched_getaffinity(0))
-    n = nthreads or min(16, avail)
-    n = max(1, min(n, spec.batch * spec.heads))
+    threads = nthreads or min(16, avail)
+    n = max(1, min(max_slices, spec.batch * spec.heads))
     b_sl = []
     H = spec.heads
     q = x["q"].float().numpy()
@@ -84,7 +86,7 @@ def cpu_baseline(spec, x, nthreads=None):
     t0 = time.perf_counter()
     oracle.forward(qs.reshape(-1, 1, spec.head_dim), ks.reshape(-1, 1, spec.head_dim),
                    vs.reshape(-1, 1, spec.head_dim), spec.block_size, spec.top_k, cu,
-                   conv_w=w, nthreads=n)
+                   conv_w=w, nthreads=threads)
     dt = time.perf_counter() - t0
     f_sample = workloads.eff_flops(spec)["total"] * n / (spec.batch * spec.heads)
     model = ""
@@ -96,9 +98,9 @@ def cpu_baseline(spec, x, nthreads=None):
     except OSError:
         pass
     return {
-        "value": f_sample / dt / 1e12, "unit": "TFLOP/s", "cores": n, "kind": "oracle",
+        "value": f_sample / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{n} of {spec.batch * spec.heads} (sequence, head) slices, full forward "
-                  f"(centroids, routing, attention) in fp64 C, one slice per thread; "
+                  f"(centroids, routing, attention) in fp64 C on {threads} threads; "
                   f"{dt:.1f} s; cpu: {model}",
         "seconds": dt,
     }
