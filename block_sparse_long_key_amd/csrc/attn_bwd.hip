@@ -123,8 +123,13 @@ struct BwdSmem {
     int64_t dest[kTileRows];                    // dq piece row, -1 = none
 };
 
+// waves per list workgroup: d = 128 with 128-key blocks splits the keys over
+// 8 waves (16 each) so the per-wave dK / dV accumulators fit 2 waves per SIMD
 template <int D, int BLK>
-__global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void bwd_list_kernel(
+constexpr int bwd_waves() { return (D == 128 && BLK == 128) ? 8 : 4; }
+
+template <int D, int BLK>
+__global__ __launch_bounds__((64 * bwd_waves<D, BLK>()), 2) void bwd_list_kernel(
     SegTable st, const int2* __restrict__ lst, const uint32_t* __restrict__ entries,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ rowstat, float sl2, float scale,
@@ -134,13 +139,15 @@ __global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void
     using S = BwdSmem<D, BLK>;
     __shared__ __align__(16) S sm;
     constexpr int RS = S::RS, SS = S::SS;
-    constexpr int KPW = BLK / 4;                // keys per wave
+    constexpr int NW = bwd_waves<D, BLK>();
+    constexpr int NT = 64 * NW;
+    constexpr int KPW = BLK / NW;               // keys per wave
     constexpr int NKS = KPW / 16;               // 16-key sub-blocks per wave
     constexpr int NDT = D / 16;                 // 16-dim blocks
     constexpr int CPR = D / 8;                  // 16-byte chunks per staged row
-    constexpr int RPP = kBwdThreads / CPR;      // staged rows per pass
+    constexpr int RPP = NT / CPR;               // staged rows per pass
     constexpr int NPASS = kTileRows / RPP;
-    constexpr int NB = D / 32;                  // dQ^T blocks per wave (of 2 * NDT)
+    constexpr int NB = 2 * NDT / NW;            // dQ^T blocks per wave (of 2 * NDT)
     static_assert(NKS >= 1 && NPASS >= 1, "shape");
 
     // contiguous runs of lists per XCD (the hardware deals workgroups
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void
     // ---- K_j, V_j to LDS (rows >= nq zero)
     {
         const size_t row0 = (size_t)(t0 + j * BLK) * H + h;
-        for (int e = tid; e < BLK * CPR; e += kBwdThreads) {
+        for (int e = tid; e < BLK * CPR; e += NT) {
             const int u = e / CPR, c = e % CPR;
             u32x4_t kk = {0u, 0u, 0u, 0u}, vv = kk;
             if (u < nq) {
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void
     // fragments (A operands of dQ^T) are the same for every tile; they are
     // read from LDS once and kept in registers
     constexpr bool KREG = D == 64;
-    const int qs_w = wave >> 1;                  // this wave's dQ^T query sub-block
+    const int qs_w = wave / (NW / 2);            // this wave's dQ^T query sub-block
     u16x8_t kbr[KREG ? NKS : 1][KREG ? D / 32 : 1], vbr[KREG ? NKS : 1][KREG ? D / 32 : 1];
     u16x8_t kar[KREG ? NB : 1][KREG ? BLK / 32 : 1];
     auto kfrag = [&](int ks, int kk) -> u16x8_t {
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void
         return *(const u16x8_t*)(sm.v + (kw0 + 16 * ks + l16) * RS + 32 * kk + 8 * g4);
     };
     auto ktfrag = [&](int b, int kk) -> u16x8_t {
-        const int dt = (wave & 1) * NB + b;
+        const int dt = (wave % (NW / 2)) * NB + b;
         const int r0 = 32 * kk + 8 * g4 + (l16 >> 2);
         return cat(tr_read(sm.k + r0 * RS + 16 * dt + 4 * (l16 & 3)),
                    tr_read(sm.k + (r0 + 4) * RS + 16 * dt + 4 * (l16 & 3)));
@@ -372,7 +379,7 @@ __global__ __launch_bounds__(kBwdThreads, (D == 128 && BLK == 128 ? 1 : 2)) void
         // ---- dQ^T = K^T dS^T for query sub-block qs_w, NB dim blocks
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int dt = (wave & 1) * NB + b;
+            const int dt = (wave % (NW / 2)) * NB + b;
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < BLK / 32; ++kk) {
@@ -471,7 +478,7 @@ hipError_t bwd_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, 
     {
         const int64_t nlists = (int64_t)st.total_blocks * st.H;
         const int64_t per_xcd = (nlists + 7) / 8;
-        hipLaunchKernelGGL((bwd_list_kernel<D, BLK>), dim3((unsigned)(per_xcd * 8)), dim3(kBwdThreads), 0,
+        hipLaunchKernelGGL((bwd_list_kernel<D, BLK>), dim3((unsigned)(per_xcd * 8)), dim3(64 * bwd_waves<D, BLK>()), 0,
                            L.stream, st, (const int2*)(wsp + ws.lst_off), (const uint32_t*)(wsp + ws.ent_off),
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            (const uint16_t*)dout, (const float2*)rowstat, scale * 1.4426950408889634f,
