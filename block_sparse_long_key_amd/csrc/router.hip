@@ -30,8 +30,12 @@ namespace moba {
 namespace {
 
 constexpr int kTile = 32;
-// idx slot-0 marker: row awaiting the exact fp64 re-selection
+// idx slot-0 markers between the two router kernels: row awaiting the full
+// fp64 re-selection; row carrying a hint (finalists and a bound)
 constexpr int32_t kPending = (int32_t)0x80000000;
+constexpr int32_t kHint = (int32_t)0x80000001;
+constexpr int kHintMinK = 6;           // F = 2K-4 finalists: at least K+2
+constexpr int kHintNone = 0xffff;      // empty finalist slot; block ids stay below
 
 template <int KMAX>
 __device__ __forceinline__ void insert_desc(float (&sc)[KMAX], int (&ix)[KMAX], int K,
@@ -322,6 +326,17 @@ __device__ __forceinline__ void merge_lanes(float (&x)[N])
     }
 }
 
+// (query block g, head h) of workgroup blockIdx.x in a 1-D grid of
+// total_blocks * H: head-major, each head's blocks from the last (the longest
+// scan) to the first, so the long workgroups start early and short ones fill
+// the tail.
+__device__ __forceinline__ void route_item(const SegTable& st, int& g, int& h)
+{
+    const int w = blockIdx.x;
+    h = w / st.total_blocks;
+    g = st.total_blocks - 1 - (w - h * st.total_blocks);
+}
+
 template <int D, int BLK, int KMAX>
 // (d = 64 with short lists fits 128 VGPRs: ask for 4 waves per SIMD)
 __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
@@ -337,7 +352,8 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     __shared__ __align__(16) uint16_t clo[TB * CS];
     __shared__ float red[NW];
 
-    const int g = blockIdx.x, h = blockIdx.y;
+    int g, h;
+    route_item(st, g, h);
     const int H = st.H, K = st.K;
     const int s = seq_of_block(st, g);
     const int i = g - st.boff[s];
@@ -537,7 +553,8 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         const bool overflow = lastmax > b;
         // keys are within 2^(LB-23)|s| of the MFMA scores
         const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
-        const float E = E0 * sqrtf(qn2[sb]) * cmax + dk + 1e-30f;
+        const float Er = E0 * sqrtf(qn2[sb]) * cmax + 1e-30f;     // MFMA score vs fp64 score
+        const float E = Er + dk;
         const bool flag = overflow || !(a - b > 2.0f * E);
         if (g4 == 0 && valid[sb] && !flag) {
             int sel[KMAX];
@@ -552,18 +569,25 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         }
         if (!__ballot(valid[sb] && flag)) continue;
 
-        // near-tie: every block that can still be selected has a key >= a - 2E
-        // (its exact score is >= a - E), and b is one of them.  If the
-        // (K+1)-th key of the query is below a - 2E and no lane dropped a key
-        // that high, the K best keys are exactly the candidates: hand them to
-        // route_fix_kernel in the row (slot p = -(j + 2)), which re-scores
-        // them in fp64 and drops the worst.  Otherwise mark the row for a
-        // full fp64 re-selection.
         constexpr int MW = 2 * KMAX;
         float wk[MW];
 #pragma unroll
         for (int p = 0; p < MW; ++p) wk[p] = p < KMAX ? key[sb][p] : -INFINITY;
         merge_lanes<MW, KMAX>(wk);
+        // near-tie: every block that can still be selected has a key >= a - 2E
+        // (its exact score is >= a - E), and b is one of them.  If the
+        // (K+1)-th key of the query is below a - 2E and no lane dropped a key
+        // that high, the K best keys are exactly the candidates: hand them to
+        // route_fix_kernel in the row (slot p = -(j + 2)), which re-scores
+        // them in fp64 and drops the worst.
+        // Otherwise (k >= 6, ids of 16 bits) the row becomes a hint: the
+        // blocks of its F = 2K-4 best keys (two ids per slot) and an upper
+        // bound ub on the fp64 score of every other block -- its key is at
+        // most kn = max(wk[F], lastmax), its MFMA score at most kn plus the id
+        // bits, its fp64 score at most that plus Er.  route_fix_kernel scores
+        // the F in fp64; if the (K-1)-th of them is above ub they hold the
+        // selection.  Failing that (or with no room for a hint) the row is
+        // marked for a full fp64 re-selection.
         const float tlow = a - 2.0f * E;
         float next = wk[0];
 #pragma unroll
@@ -575,6 +599,30 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
 #pragma unroll
                 for (int p = 0; p < KMAX; ++p)
                     if (p < K) out[p] = -(key_block(wk[p], lmask) + 2);
+            } else if (K >= kHintMinK && i <= kHintNone) {
+                const int F = 2 * K - 4;
+                float kf = wk[0];
+#pragma unroll
+                for (int p = 1; p < MW; ++p) kf = (p == F) ? wk[p] : kf;
+                const float kn = fmaxf(kf, lastmax);
+                const float ub = kn == -INFINITY ? -INFINITY
+                                                 : (kn + ldexpf(fabsf(kn), LB - 22)) + Er;
+                out[0] = kHint;
+                out[1] = __float_as_int(ub);
+#pragma unroll
+                for (int p = 0; p + 2 < KMAX; ++p) {
+                    if (p + 2 < K) {
+                        uint32_t w = 0;
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            const float kk = wk[2 * p + u];
+                            const int j = key_block(kk, lmask);
+                            const uint32_t id = (kk > -INFINITY && j < i) ? (uint32_t)j : (uint32_t)kHintNone;
+                            w |= id << (16 * u);
+                        }
+                        out[2 + p] = (int32_t)w;
+                    }
+                }
             } else {
                 out[0] = kPending;
             }
@@ -602,7 +650,7 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
     const int lane = threadIdx.x;
     const int grp = lane / KMAX, p = lane % KMAX;
     {
-        uint64_t cm = __ballot(s0 != kPending && s0 <= -2);
+        uint64_t cm = __ballot(s0 != kPending && s0 != kHint && s0 <= -2);
         while (cm) {
             // this group's row: the grp-th set bit of cm
             uint64_t m = cm;
@@ -654,6 +702,98 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
     }
 }
 
+// Hint rows (slot 0 = kHint; slot 1 = ub as float bits; slots 2.. = the
+// block ids of the row's best F = 2K-4 keys, two per slot, kHintNone for
+// none): the hint rows of a 64-row chunk are taken 64/(2 KMAX) at a time,
+// one lane per (row, finalist).  A lane scores its finalist in fp64 and
+// ranks it against the row's others by (score desc, id asc); if the
+// (K-1)-th score is above ub, no other block can reach it and the K-1 best
+// finalists are written in ascending block order, the own block last.
+// Returns the rows (bits of the chunk) whose bound failed.
+template <int D, int BLK, int KMAX>
+__device__ __forceinline__ uint64_t fix_hint_rows(const SegTable& st, const uint16_t* __restrict__ q,
+                                                  const float* cbase, int32_t* __restrict__ idx,
+                                                  int s, int i, int h, int r0, int32_t s0)
+{
+    constexpr int FP = 2 * KMAX;                 // lanes per row (F <= FP)
+    constexpr int RPW = 64 / FP;                 // rows per pass
+    const int H = st.H, K = st.K, F = 2 * K - 4;
+    const int lane = threadIdx.x;
+    const int grp = lane / FP, p = lane % FP;
+    uint64_t failed = 0;
+    uint64_t cm = __ballot(s0 == kHint);
+    while (cm) {
+        // this group's row: the grp-th set bit of cm
+        uint64_t m = cm;
+        for (int t = 0; t < grp; ++t) m &= m - 1;
+        const int src = m ? __builtin_ctzll(m) : -1;
+        for (int t = 0; t < RPW; ++t) cm &= cm - 1;
+        double sc = -INFINITY;
+        int j = 0x7fffffff;
+        float ub = INFINITY;
+        int32_t* row = nullptr;
+        if (src >= 0) {
+            row = idx + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * K;
+            ub = __int_as_float(row[1]);
+            if (p < F) {
+                const uint32_t w = (uint32_t)row[2 + p / 2];
+                const int id = (int)((p & 1) ? (w >> 16) : (w & 0xffffu));
+                if (id != kHintNone) {
+                    j = id;
+                    const uint16_t* qp = q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D;
+                    const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
+                    double acc = 0.0;
+#pragma unroll
+                    for (int c8 = 0; c8 < D / 8; ++c8) {
+                        const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
+                        const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
+                        acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
+                        acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
+                        acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
+                    }
+                    sc = acc;
+                }
+            }
+        }
+        const bool real = j != 0x7fffffff;
+        int rank = 0;
+#pragma unroll
+        for (int e = 0; e < FP; ++e) {
+            const double os = __shfl(sc, grp * FP + e);
+            const int oj = __shfl(j, grp * FP + e);
+            rank += ranks_before64(os, oj, sc, j) ? 1 : 0;
+        }
+        const bool keep = real && rank < K - 1;
+        // the (K-1)-th score of the row (-inf with fewer real finalists)
+        double t = (real && rank == K - 2) ? sc : -INFINITY;
+#pragma unroll
+        for (int e = 1; e < FP; e <<= 1) t = fmax(t, __shfl_xor(t, e));
+        const bool exact = src >= 0 && t > (double)ub;
+        int pos = 0;
+#pragma unroll
+        for (int e = 0; e < FP; ++e) {
+            const int oj = __shfl(j, grp * FP + e);
+            const int ok = __shfl(keep ? 1 : 0, grp * FP + e);
+            pos += (ok && oj < j) ? 1 : 0;
+        }
+        if (exact && keep) row[pos] = j;
+        if (exact && p == 0) row[K - 1] = i;
+        if (src >= 0 && !exact && p == 0) row[0] = kPending;
+#pragma unroll
+        for (int g = 0; g < RPW; ++g) {
+            const int gs = __shfl(src, g * FP);
+            const int ge = __shfl(exact ? 1 : 0, g * FP);
+            if (gs >= 0 && !ge) failed |= 1ull << gs;
+        }
+    }
+    return failed;
+}
+
 // Marked rows (slot 0 = kPending), rare: lanes score past blocks j = lane,
 // lane + 64, ... and keep their best KMAX by (score desc, index asc) in a
 // sorted list; K-1 rounds of a wave-wide argmax over the list heads then
@@ -661,13 +801,14 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
 template <int D, int BLK, int KMAX>
 __device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16_t* __restrict__ q,
                                                 const float* cbase, int32_t* __restrict__ idx,
-                                                float* qstage, int s, int i, int h, int r0, int32_t s0)
+                                                float* qstage, int s, int i, int h, int r0, int32_t s0,
+                                                uint64_t more)
 {
     const int H = st.H, K = st.K;
     const int lane = threadIdx.x;
     {
-        const bool mine = s0 == kPending;
-        uint64_t fm = __ballot(mine);
+        // rows marked by the MFMA kernel, and hint rows whose bound failed
+        uint64_t fm = __ballot(s0 == kPending) | more;
         while (fm) {
             const int src = __builtin_ctzll(fm);
             fm &= fm - 1;
@@ -729,15 +870,17 @@ __device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16
     }
 }
 
-// One wave per query block: one look at its rows, then the candidate rows
-// and the (rare) marked rows of each 64-row chunk.
+// One wave per (query block, head), in the MFMA kernel's order: one look at
+// its rows, then the candidate rows and the (rare) marked rows of each
+// 64-row chunk.
 template <int D, int BLK, int KMAX>
 __global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_fix_kernel(SegTable st, const uint16_t* __restrict__ q,
                                                                       const float* __restrict__ cent,
                                                                       int32_t* __restrict__ idx)
 {
     __shared__ __align__(16) float qstage[D];
-    const int g = blockIdx.x, h = blockIdx.y;
+    int g, h;
+    route_item(st, g, h);
     const int H = st.H, K = st.K;
     const int s = seq_of_block(st, g);
     const int i = g - st.boff[s];
@@ -750,7 +893,8 @@ __global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_fix_kernel(SegT
         int32_t s0 = 0;
         if (r0 + lane < BLK && tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
         fix_candidate_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
-        fix_marked_rows<D, BLK, KMAX>(st, q, cbase, idx, qstage, s, i, h, r0, s0);
+        const uint64_t failed = fix_hint_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
+        fix_marked_rows<D, BLK, KMAX>(st, q, cbase, idx, qstage, s, i, h, r0, s0, failed);
     }
 }
 
@@ -774,29 +918,30 @@ hipError_t launch_d(const Launch& L, const void* q, const float* cent, int32_t* 
 
 }  // namespace
 
+template <int D, int BLK, int KMAX>
+hipError_t launch_mfma_k(const Launch& L, const uint16_t* q, const float* cent, int32_t* idx)
+{
+    const dim3 grid((unsigned)L.st.total_blocks * L.st.H);
+    hipLaunchKernelGGL((route_mfma_kernel<D, BLK, KMAX>), grid, dim3(2 * BLK), 0, L.stream, L.st, q, cent,
+                       idx);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_fix_kernel<D, BLK, KMAX>), grid, dim3(64), 0, L.stream, L.st, q, cent, idx);
+    return hipGetLastError();
+}
+
 template <int D, int BLK>
 hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_t* idx)
 {
-    dim3 grid(L.st.total_blocks, L.st.H);
-    dim3 block(2 * BLK);
     const int K = L.st.K;
     const uint16_t* qq = (const uint16_t*)q;
-    if (K <= 8) {
-        hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 8>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-        hipLaunchKernelGGL((route_fix_kernel<D, BLK, 8>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-    } else if constexpr (BLK <= 128) {
+    if (K <= 8) return launch_mfma_k<D, BLK, 8>(L, qq, cent, idx);
+    if constexpr (BLK <= 128) {
         // (blocks of 256 / 512 keys are limited to top_k <= 8 by the API)
-        if (K <= 16) {
-            hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 16>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-            hipLaunchKernelGGL((route_fix_kernel<D, BLK, 16>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-        } else {
-            hipLaunchKernelGGL((route_mfma_kernel<D, BLK, 32>), grid, block, 0, L.stream, L.st, qq, cent, idx);
-            hipLaunchKernelGGL((route_fix_kernel<D, BLK, 32>), grid, dim3(64), 0, L.stream, L.st, qq, cent, idx);
-        }
-    } else {
-        return hipErrorInvalidValue;
+        if (K <= 16) return launch_mfma_k<D, BLK, 16>(L, qq, cent, idx);
+        return launch_mfma_k<D, BLK, 32>(L, qq, cent, idx);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <int D>
