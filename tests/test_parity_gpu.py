@@ -248,6 +248,29 @@ def test_route_one_lane_holds_the_top_k():
     assert int(np.any(got != ref_idx, axis=-1).sum()) == 0
 
 
+@pytest.mark.parametrize("seq,B,K", [(65536, 64, 8), (65536, 64, 16), (40000, 64, 6)])
+def test_route_long_scan_every_row(seq, B, K):
+    """A 1024-block sequence: block ids take 10 key bits, so a few percent of
+    the rows are flagged and most of them go through the fix kernel's fp64
+    re-scoring of their best 2k-4 blocks against the bound on all others
+    (k = 6 is the smallest k with room for that).  Every row must equal the
+    oracle's selection."""
+    H, d = 1, 64
+    print(f"[long scan seq {seq} B{B} K{K}]", flush=True)
+    g = torch.Generator().manual_seed(seq + K)
+    q = torch.randn((seq, H, d), generator=g).to(torch.bfloat16)
+    k = torch.randn((seq, H, d), generator=g).to(torch.bfloat16)
+    cu = [0, seq]
+    cent = oracle.centroids(k, B, cu)
+    ref_idx, ga, gb, ex = oracle.route(q, cent, B, K, cu)
+    idx = moba().moba_route_topk(q.to(DEV), torch.from_numpy(cent).to(DEV), B, K, cu)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy().reshape(ref_idx.shape)
+    ndiff = int(np.any(got != ref_idx, axis=-1).sum())
+    print(f"[long scan K{K}] rows differing: {ndiff}; near-tie rows: {int(ex.sum())}")
+    assert ndiff == 0
+
+
 @pytest.mark.parametrize("seqlens,H,d,B,K,dtype", [
     ([1000], 2, 64, 64, 4, "bf16"),           # ragged tail (1000 = 15*64 + 40)
     ([130, 1, 64, 300], 3, 64, 128, 8, "bf16"),  # short / single-token sequences
