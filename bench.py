@@ -155,7 +155,8 @@ def main():
     idx = torch.empty(q.shape[:-1] + (K,), dtype=torch.int32, device=dev)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:-1], dtype=torch.float32, device=dev)
-    ws = torch.empty(max(256, moba.moba_attn_fwd_workspace_bytes(q, B, K, cu)),
+    ws = torch.empty(max(256, moba.moba_attn_fwd_workspace_bytes(q, B, K, cu),
+                         moba.moba_route_topk_workspace_bytes(q, B, K, cu)),
                      dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     names = (["conv_pool"] if w is not None else ["pool"]) + ["route", "index", "routed_attn",
@@ -173,7 +174,7 @@ def main():
             moba.moba_centroids(k, B, cu, out=cent)
             kk = k
         mark(1)
-        moba.moba_route_topk(q, cent, B, K, cu, out=idx)
+        moba.moba_route_topk(q, cent, B, K, cu, out=idx, workspace=ws)
         mark(2)
         moba.moba_attn_index(idx, q, B, K, ws, cu)
         mark(3)

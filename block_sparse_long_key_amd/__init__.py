@@ -30,12 +30,14 @@ import torch
 __all__ = [
     "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
-    "moba_attn_fwd_workspace_bytes", "moba_total_blocks", "library_path",
+    "moba_attn_fwd_workspace_bytes", "moba_route_topk_workspace_bytes", "moba_total_blocks",
+    "library_path",
     "moba_attn_bwd", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
     "moba_key_conv_bwd_workspace_bytes", "moba_attention",
     "MobaError",
 ]
 
+_ABI_VERSION = 2                 # MOBA_ABI_VERSION of include/moba.h
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoba_amd.so")
 _lib = None
@@ -76,7 +78,7 @@ def _load():
     sig = {
         "moba_key_conv": [SH, P, P, I32, I32, P, P, P],
         "moba_centroids": [SH, P, P, P],
-        "moba_route_topk": [SH, P, P, P, P],
+        "moba_route_topk": [SH, P, P, P, P, SZ, P],
         "moba_attn_fwd": [SH, P, P, P, P, F32, P, P, P, SZ, P],
         "moba_attn_index": [SH, P, P, SZ, P],
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
@@ -90,6 +92,8 @@ def _load():
         f.restype = ctypes.c_int
     lib.moba_attn_fwd_workspace_bytes.argtypes = [SH]
     lib.moba_attn_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.moba_route_topk_workspace_bytes.argtypes = [SH]
+    lib.moba_route_topk_workspace_bytes.restype = ctypes.c_size_t
     lib.moba_key_conv_bwd_workspace_bytes.argtypes = [SH, I32]
     lib.moba_key_conv_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.moba_attn_bwd_workspace_bytes.argtypes = [SH]
@@ -99,6 +103,9 @@ def _load():
     lib.moba_status_string.argtypes = [ctypes.c_int]
     lib.moba_status_string.restype = ctypes.c_char_p
     lib.moba_abi_version.restype = ctypes.c_int32
+    if lib.moba_abi_version() != _ABI_VERSION:
+        raise MobaError(f"{_LIB_PATH} has C ABI version {lib.moba_abi_version()}, this binding "
+                        f"expects {_ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 
@@ -176,6 +183,12 @@ def moba_attn_fwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
     return int(_load().moba_attn_fwd_workspace_bytes(ctypes.byref(sh)))
 
 
+def moba_route_topk_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
+                                    cu_seqlens=None) -> int:
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    return int(_load().moba_route_topk_workspace_bytes(ctypes.byref(sh)))
+
+
 def moba_attn_bwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
                                   cu_seqlens=None) -> int:
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
@@ -250,13 +263,21 @@ def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,
 
 def moba_route_topk(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k: int,
                     cu_seqlens=None, out: Optional[torch.Tensor] = None,
-                    stream=None) -> torch.Tensor:
-    """Causal top-k block ids: int32 [..., heads, top_k], ascending, -1 padded."""
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Causal top-k block ids: int32 [..., heads, top_k], ascending, -1 padded.
+
+    workspace: uint8 device tensor of at least moba_route_topk_workspace_bytes
+    (a moba_attn_fwd workspace of that size may be shared); allocated here
+    when None."""
     _dev(q, cent)
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
     if out is None:
         out = torch.empty(_rows(q) + (top_k,), dtype=torch.int32, device=q.device)
-    _check(_load().moba_route_topk(ctypes.byref(sh), _p(q), _p(cent), _p(out), _stream(stream)),
+    need = int(_load().moba_route_topk_workspace_bytes(ctypes.byref(sh)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_load().moba_route_topk(ctypes.byref(sh), _p(q), _p(cent), _p(out), _p(workspace),
+                                   workspace.numel(), _stream(stream)),
            "moba_route_topk")
     return out
 
@@ -330,7 +351,11 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
     else:
         kk = k
         cent = moba_centroids(k, block_size, cu_seqlens)
-    idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens)
+    if workspace is None:
+        need = max(moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens),
+                   moba_route_topk_workspace_bytes(q, block_size, top_k, cu_seqlens), 256)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens, workspace=workspace)
     o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
     return o, lse, idx, kk
 

@@ -2,6 +2,7 @@
 // sequence/block tables, workspace carving and kernel launches.  No
 // allocation, no synchronisation, no printing.
 #include <math.h>
+#include <algorithm>
 #include <string.h>
 
 #include "moba_internal.h"
@@ -11,8 +12,6 @@ using namespace moba;
 namespace {
 
 constexpr int64_t kMaxRows = (int64_t)1 << 27;   // tokens * heads (entry encoding)
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -268,15 +267,24 @@ moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, 
     return hip_status(launch_conv_pool(L, k, nullptr, 0, 0, nullptr, cent));
 }
 
+size_t moba_route_topk_workspace_bytes(const moba_shape* shape)
+{
+    Launch L;
+    if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
+    return std::max(route_ws_bytes(L), (size_t)256);
+}
+
 moba_status moba_route_topk(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
-                            hipStream_t stream)
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     Launch L;
     moba_status st = make_launch(shape, &L, stream);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(q) || !ptr_ok(cent) || !ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
+    if (workspace_bytes < std::max(route_ws_bytes(L), (size_t)256)) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (L.tokens == 0) return MOBA_OK;
-    return hip_status(launch_route(L, q, cent, idx));
+    return hip_status(launch_route(L, q, cent, workspace, idx));
 }
 
 // the index pass on the (possibly expanded) selection

@@ -139,7 +139,20 @@ hipError_t launch_conv_pool(const Launch& L, const void* k, const float* w, int 
                             int mode, void* k_out, float* cent);
 hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W, int mode,
                            const void* gk, void* dk, float* dw, float* dwp);
-hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx);
+// The router's workspace: the centroids split for the MFMA scores (bf16 high
+// and low parts, [block][head][d] like the centroids) and their squared
+// norms ([block][head]).
+struct RouteWs {
+    uint16_t* hi;
+    uint16_t* lo;
+    float* n2;
+};
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+size_t route_ws_bytes(const Launch& L);
+RouteWs route_ws(const Launch& L, void* workspace);
+// bf16 queries use the workspace; fp32 queries do not read it
+hipError_t launch_route(const Launch& L, const void* q, const float* cent, void* workspace,
+                        int32_t* idx);
 // det: place each list's entries in an order that depends only on idx
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
                       bool det = false);

@@ -269,31 +269,6 @@ __device__ __forceinline__ float opaque_inf()
 __device__ __forceinline__ float fmax2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, inf); }
 __device__ __forceinline__ float fmin2(float a, float b, float inf) { return __builtin_amdgcn_fmed3f(a, b, -inf); }
 
-// sum over aligned groups of N = 16 or 32 lanes: DPP within each 16-lane row
-// (quad swaps, half-row and row mirrors), one cross-row shuffle for 32
-__device__ __forceinline__ float dpp_add(float x, int ctrl_sel)
-{
-    int y;
-    switch (ctrl_sel) {
-    case 0: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false); break;   // xor 1
-    case 1: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false); break;   // xor 2
-    case 2: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false); break;  // half-row mirror
-    default: y = __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false); break; // row mirror
-    }
-    return x + __int_as_float(y);
-}
-template <int N>
-__device__ __forceinline__ float row_sum(float x)
-{
-    static_assert(N == 16 || N == 32, "row_sum width");
-    x = dpp_add(x, 0);
-    x = dpp_add(x, 1);
-    x = dpp_add(x, 2);
-    x = dpp_add(x, 3);
-    if constexpr (N == 32) x += __shfl_xor(x, 16);
-    return x;
-}
-
 // block id carried in the low bits of a selection key
 __device__ __forceinline__ int key_block(float k, uint32_t lmask)
 {
@@ -326,6 +301,44 @@ __device__ __forceinline__ void merge_lanes(float (&x)[N])
     }
 }
 
+// Split of the fp32 centroids for the MFMA scores, once per (block, head):
+// hi = bf16(c), lo = bf16(c - hi) (c - hi is exact in fp32), and |c|^2 in
+// fp32.  Eight channels per thread; the D/8 threads of a row sum its norm.
+template <int D>
+__global__ __launch_bounds__(256) void route_prep_kernel(int64_t rows, const float* __restrict__ cent,
+                                                         uint16_t* __restrict__ chg, uint16_t* __restrict__ clg,
+                                                         float* __restrict__ cng)
+{
+    constexpr int TPR = D / 8;                     // threads per centroid row
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t row = t / TPR;
+    const int c8 = (int)(t % TPR);
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (row < rows) {
+        const float4 a = *(const float4*)(cent + row * D + 8 * c8);
+        const float4 b = *(const float4*)(cent + row * D + 8 * c8 + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    u32x4_t hi, lo;
+    float n2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t h = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+        hi[e] = h;
+        lo[e] = pack_bf16x2(x[2 * e] - bf16_lo(h), x[2 * e + 1] - bf16_hi(h));
+        n2 = __builtin_fmaf(x[2 * e], x[2 * e], n2);
+        n2 = __builtin_fmaf(x[2 * e + 1], x[2 * e + 1], n2);
+    }
+#pragma unroll
+    for (int m = 1; m < TPR; m <<= 1) n2 += __shfl_xor(n2, m);
+    if (row < rows) {
+        *(u32x4_t*)(chg + row * D + 8 * c8) = hi;
+        *(u32x4_t*)(clg + row * D + 8 * c8) = lo;
+        if (c8 == 0) cng[row] = n2;
+    }
+}
+
 // (query block g, head h) of workgroup blockIdx.x in a 1-D grid of
 // total_blocks * H: head-major, each head's blocks from the last (the longest
 // scan) to the first, so the long workgroups start early and short ones fill
@@ -340,7 +353,9 @@ __device__ __forceinline__ void route_item(const SegTable& st, int& g, int& h)
 template <int D, int BLK, int KMAX>
 // (d = 64 with short lists fits 128 VGPRs: ask for 4 waves per SIMD)
 __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void route_mfma_kernel(SegTable st, const uint16_t* __restrict__ q,
-                                                             const float* __restrict__ cent,
+                                                             const uint16_t* __restrict__ chg,
+                                                             const uint16_t* __restrict__ clg,
+                                                             const float* __restrict__ cng,
                                                              int32_t* __restrict__ idx)
 {
     constexpr int TB = 64;                 // centroid rows per LDS tile
@@ -360,7 +375,10 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     const int L = seq_len(st, s);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
-    const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
+    const size_t cofs = (size_t)st.boff[s] * H * D + (size_t)h * D;
+    const uint16_t* hbase = chg + cofs;
+    const uint16_t* lbase = clg + cofs;
+    const float* nbase = cng + (size_t)st.boff[s] * H + h;
 
     int tl[2];
     bool valid[2];
@@ -481,30 +499,34 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
 
     for (int j0 = 0; j0 < i; j0 += TB) {
         __syncthreads();
-        // stage the tile: hi / lo bf16 rows, and the row norms; the global
-        // loads of the whole tile are issued before any of them is used
-        constexpr int NIT = TB * (D / 4) / NT;
-        static_assert(TB * (D / 4) % NT == 0, "tile split");
-        float4 xs[NIT];
+        // stage the tile: hi / lo bf16 rows (split once by route_prep_kernel)
+        // and the row norms; the global loads of the whole tile are issued
+        // before any of them is used
+        constexpr int NCH = TB * (D / 8);           // 16-byte chunks of a tile
+        constexpr int NIT = (NCH + NT - 1) / NT;
+        u32x4_t xh[NIT], xl[NIT];
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = threadIdx.x + it * NT;
-            const int r = e / (D / 4), c4 = e % (D / 4);
-            xs[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j0 + r < i) xs[it] = *(const float4*)(cbase + (size_t)(j0 + r) * H * D + 4 * c4);
+            const int r = e / (D / 8), c8 = e % (D / 8);
+            xh[it] = u32x4_t{0u, 0u, 0u, 0u};
+            xl[it] = xh[it];
+            if (e < NCH && j0 + r < i) {
+                const size_t off = (size_t)(j0 + r) * H * D + 8 * c8;
+                xh[it] = *(const u32x4_t*)(hbase + off);
+                xl[it] = *(const u32x4_t*)(lbase + off);
+            }
         }
+        if (threadIdx.x < TB && j0 + (int)threadIdx.x < i)
+            cmax2 = fmaxf(cmax2, nbase[(size_t)(j0 + threadIdx.x) * H]);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = threadIdx.x + it * NT;
-            const int r = e / (D / 4), c4 = e % (D / 4);
-            const float4 x = xs[it];
-            const uint32_t h01 = pack_bf16x2(x.x, x.y), h23 = pack_bf16x2(x.z, x.w);
-            const uint32_t l01 = pack_bf16x2(x.x - bf16_lo(h01), x.y - bf16_hi(h01));
-            const uint32_t l23 = pack_bf16x2(x.z - bf16_lo(h23), x.w - bf16_hi(h23));
-            *(u32x2_t*)(chi + r * CS + 4 * c4) = u32x2_t{h01, h23};
-            *(u32x2_t*)(clo + r * CS + 4 * c4) = u32x2_t{l01, l23};
-            // the D/4 consecutive threads of a row reduce its norm
-            cmax2 = fmaxf(cmax2, row_sum<D / 4>(x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w));
+            const int r = e / (D / 8), c8 = e % (D / 8);
+            if (e < NCH) {
+                *(u32x4_t*)(chi + r * CS + 8 * c8) = xh[it];
+                *(u32x4_t*)(clo + r * CS + 8 * c8) = xl[it];
+            }
         }
         __syncthreads();
         for (int bt = 0; bt < TB / 16; ++bt) {
@@ -919,11 +941,12 @@ hipError_t launch_d(const Launch& L, const void* q, const float* cent, int32_t* 
 }  // namespace
 
 template <int D, int BLK, int KMAX>
-hipError_t launch_mfma_k(const Launch& L, const uint16_t* q, const float* cent, int32_t* idx)
+hipError_t launch_mfma_k(const Launch& L, const uint16_t* q, const float* cent, const RouteWs& w,
+                         int32_t* idx)
 {
     const dim3 grid((unsigned)L.st.total_blocks * L.st.H);
-    hipLaunchKernelGGL((route_mfma_kernel<D, BLK, KMAX>), grid, dim3(2 * BLK), 0, L.stream, L.st, q, cent,
-                       idx);
+    hipLaunchKernelGGL((route_mfma_kernel<D, BLK, KMAX>), grid, dim3(2 * BLK), 0, L.stream, L.st, q, w.hi,
+                       w.lo, w.n2, idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((route_fix_kernel<D, BLK, KMAX>), grid, dim3(64), 0, L.stream, L.st, q, cent, idx);
@@ -931,36 +954,58 @@ hipError_t launch_mfma_k(const Launch& L, const uint16_t* q, const float* cent, 
 }
 
 template <int D, int BLK>
-hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, int32_t* idx)
+hipError_t launch_mfma(const Launch& L, const void* q, const float* cent, const RouteWs& w, int32_t* idx)
 {
     const int K = L.st.K;
     const uint16_t* qq = (const uint16_t*)q;
-    if (K <= 8) return launch_mfma_k<D, BLK, 8>(L, qq, cent, idx);
+    const int64_t rows = (int64_t)L.st.total_blocks * L.st.H;
+    const int64_t threads = rows * (D / 8);
+    hipLaunchKernelGGL((route_prep_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, L.stream,
+                       rows, cent, w.hi, w.lo, w.n2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (K <= 8) return launch_mfma_k<D, BLK, 8>(L, qq, cent, w, idx);
     if constexpr (BLK <= 128) {
         // (blocks of 256 / 512 keys are limited to top_k <= 8 by the API)
-        if (K <= 16) return launch_mfma_k<D, BLK, 16>(L, qq, cent, idx);
-        return launch_mfma_k<D, BLK, 32>(L, qq, cent, idx);
+        if (K <= 16) return launch_mfma_k<D, BLK, 16>(L, qq, cent, w, idx);
+        return launch_mfma_k<D, BLK, 32>(L, qq, cent, w, idx);
     }
     return hipErrorInvalidValue;
 }
 
 template <int D>
-hipError_t launch_mfma_b(const Launch& L, const void* q, const float* cent, int32_t* idx)
+hipError_t launch_mfma_b(const Launch& L, const void* q, const float* cent, const RouteWs& w, int32_t* idx)
 {
     switch (L.st.B) {
-        case 64: return launch_mfma<D, 64>(L, q, cent, idx);
-        case 128: return launch_mfma<D, 128>(L, q, cent, idx);
-        case 256: return launch_mfma<D, 256>(L, q, cent, idx);
-        case 512: return launch_mfma<D, 512>(L, q, cent, idx);
+        case 64: return launch_mfma<D, 64>(L, q, cent, w, idx);
+        case 128: return launch_mfma<D, 128>(L, q, cent, w, idx);
+        case 256: return launch_mfma<D, 256>(L, q, cent, w, idx);
+        case 512: return launch_mfma<D, 512>(L, q, cent, w, idx);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_route(const Launch& L, const void* q, const float* cent, int32_t* idx)
+RouteWs route_ws(const Launch& L, void* workspace)
+{
+    const size_t rows = (size_t)L.st.total_blocks * L.st.H;
+    const size_t half = align256(rows * L.D * sizeof(uint16_t));
+    char* p = (char*)workspace;
+    return RouteWs{(uint16_t*)p, (uint16_t*)(p + half), (float*)(p + 2 * half)};
+}
+
+size_t route_ws_bytes(const Launch& L)
+{
+    const size_t rows = (size_t)L.st.total_blocks * L.st.H;
+    return 2 * align256(rows * L.D * sizeof(uint16_t)) + align256(rows * sizeof(float));
+}
+
+hipError_t launch_route(const Launch& L, const void* q, const float* cent, void* workspace, int32_t* idx)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
-    if (L.dtype == MOBA_BF16)
-        return L.D == 64 ? launch_mfma_b<64>(L, q, cent, idx) : launch_mfma_b<128>(L, q, cent, idx);
+    if (L.dtype == MOBA_BF16) {
+        const RouteWs w = route_ws(L, workspace);
+        return L.D == 64 ? launch_mfma_b<64>(L, q, cent, w, idx) : launch_mfma_b<128>(L, q, cent, w, idx);
+    }
     return L.D == 64 ? launch_d<float, 64>(L, q, cent, idx)
                      : launch_d<float, 128>(L, q, cent, idx);
 }

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 1
+#define MOBA_ABI_VERSION 2
 #define MOBA_MAX_SEQS 64
 
 typedef enum {
@@ -155,10 +155,21 @@ moba_status moba_centroids(const moba_shape *shape, const void *k,
  *   The selection is exact with respect to scores computed in fp64: the
  *   kernel scores in fp32 with a rigorous error bound and re-scores in fp64
  *   any query whose k-1-th and k-th scores are closer than that bound.
+ *   workspace: device memory of at least moba_route_topk_workspace_bytes(),
+ *   256-byte aligned (bf16 queries: the centroids split into bf16 high and
+ *   low parts and their squared norms, written by the call; fp32 queries do
+ *   not use it); contents on entry ignored, scratch on exit.  NULL or
+ *   misaligned -> MOBA_ERR_INVALID_ARG, too small ->
+ *   MOBA_ERR_WORKSPACE_TOO_SMALL.  A moba_attn_fwd workspace of at least
+ *   this size may be reused (calls stream-ordered).
  */
 moba_status moba_route_topk(const moba_shape *shape, const void *q,
                             const float *cent, int32_t *idx,
+                            void *workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/* Bytes of workspace moba_route_topk needs for `shape` (0 on invalid shape). */
+size_t moba_route_topk_workspace_bytes(const moba_shape *shape);
 
 /*
  * moba_attn_fwd -- attention over the selected blocks (task definition).

@@ -31,7 +31,7 @@ def test_forward_and_backward_replay_from_a_graph():
 
     def step():
         moba.moba_centroids(k, B, out=cent)
-        moba.moba_route_topk(q, cent, B, K, out=idx)
+        moba.moba_route_topk(q, cent, B, K, out=idx, workspace=wsf)
         _, lse = moba.moba_attn_fwd(q, k, v, idx, B, K, workspace=wsf, out=o)
         state["lse"] = lse
         moba.moba_attn_bwd(q, k, v, idx, o, lse, do, B, K, workspace=wsb, out=grads)

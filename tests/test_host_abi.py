@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
     assert "moba_attn_fwd" in names and "moba_route_topk" in names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.moba_abi_version() == 1
+    assert lib.moba_abi_version() == 2
     assert lib.moba_status_string(0) == b"ok"
     assert lib.moba_status_string(WS_SMALL) == b"workspace too small"
 
@@ -91,10 +91,30 @@ def test_large_blocks_attend_as_128_key_blocks(lib):
 def test_bad_shapes_rejected_on_host(lib, kw, code):
     sh = _shape(**kw)
     p = ctypes.c_void_p(16 * 1024)          # never dereferenced: validation fails first
-    rc = lib.moba_route_topk(ctypes.byref(sh), p, p, p, None)
+    rc = lib.moba_route_topk(ctypes.byref(sh), p, p, p, p, 1 << 30, None)
     assert rc == code
     assert lib.moba_total_blocks(ctypes.byref(sh)) == -1
     assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def test_route_workspace(lib):
+    """The router's workspace holds the split centroids: bf16 high and low
+    parts [block][head][d] and fp32 squared norms [block][head]."""
+    def a256(x):
+        return (x + 255) // 256 * 256
+    for d in (64, 128):
+        sh = _shape(batch=2, seq=1000, heads=3, d=d, B=64)
+        rows = 2 * 16 * 3
+        assert lib.moba_route_topk_workspace_bytes(ctypes.byref(sh)) == \
+            2 * a256(rows * d * 2) + a256(rows * 4)
+    assert lib.moba_route_topk_workspace_bytes(ctypes.byref(_shape(heads=0))) == 0
+    sh = _shape()
+    good = ctypes.c_void_p(1 << 20)
+    odd = ctypes.c_void_p((1 << 20) + 64)
+    need = lib.moba_route_topk_workspace_bytes(ctypes.byref(sh))
+    assert lib.moba_route_topk(ctypes.byref(sh), good, good, good, None, need, None) == INVALID
+    assert lib.moba_route_topk(ctypes.byref(sh), good, good, good, odd, need, None) == INVALID
+    assert lib.moba_route_topk(ctypes.byref(sh), good, good, good, good, need - 1, None) == WS_SMALL
 
 
 def test_null_misaligned_and_small_workspace_rejected(lib):
@@ -103,7 +123,7 @@ def test_null_misaligned_and_small_workspace_rejected(lib):
     odd = ctypes.c_void_p((1 << 20) + 4)
     assert lib.moba_centroids(ctypes.byref(sh), None, good, None) == INVALID
     assert lib.moba_centroids(ctypes.byref(sh), odd, good, None) == INVALID
-    assert lib.moba_route_topk(None, good, good, good, None) == INVALID
+    assert lib.moba_route_topk(None, good, good, good, good, 1 << 30, None) == INVALID
     need = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh))
     rc = lib.moba_attn_fwd(ctypes.byref(sh), good, good, good, good, 0.0, good, None, good,
                            need - 1, None)
