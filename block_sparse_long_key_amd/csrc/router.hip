@@ -429,9 +429,10 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     // more than LL of it, which the merge detects (a lane's last kept key
     // above the merged K-th) and sends to the fp64 path.
     // (measured: with k = 8 every slot pays for itself -- 6 slots send too
-    // many rows to fp64; with k = 16 a lane holds more than 13 of the top k
-    // too rarely to matter, and 13 slots route C4 7 % faster)
-    constexpr int LL = KMAX >= 16 ? KMAX - 3 : KMAX - 1;
+    // many rows to fp64; with k = 16 a lane holds 11 of the query's top 15
+    // rarely enough (about 4 rows in 10^4) that 11 slots route 1024 blocks
+    // 12 % faster than 15 and 4 % faster than 13, while 10 slots are slower)
+    constexpr int LL = KMAX >= 16 ? KMAX - 5 : KMAX - 1;
     float key[2][KMAX];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
