@@ -379,17 +379,21 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
-    __shared__ uint32_t sent[kItemRows];
+    // d = 64: the item's entries in LDS; d = 128 reads them from global
+    // memory (L2), so LDS keeps room for the staged rows at 2 workgroups/CU
+    constexpr bool LDS_ENT = D == 64 || sizeof(T) != 2;
+    __shared__ uint32_t sent[LDS_ENT ? kItemRows : 1];
     constexpr int NDT = D / 16;
     using W = Wave2<T, D, BLK>;
     // bf16: each wave stages its 16 partial rows of a sub-tile in LDS and
     // stores them as whole contiguous 16-byte chunks (64 lanes = 1 KB per
     // instruction) instead of half rows; rows padded by 16 B so the 8-lane
     // b128 writes hit distinct banks
-    constexpr bool STAGE = sizeof(T) == 2 && D == 64;      // (d = 128: LDS would halve occupancy)
+    constexpr bool STAGE = sizeof(T) == 2;
     constexpr int RB = D * (int)sizeof(T);            // partial row bytes
     constexpr int RS = RB + 16;                       // staged row stride
-    __shared__ __align__(16) char ostage[STAGE ? kRoutedWaves * 16 * RS : 16];
+    constexpr int SR = D == 64 ? 16 : 8;              // rows staged per pass
+    __shared__ __align__(16) char ostage[STAGE ? kRoutedWaves * SR * RS : 16];
     constexpr int NT = 64 * kRoutedWaves;             // threads
     constexpr int TR = 32 * kRoutedWaves;             // rows per tile
     // the hardware deals workgroups round-robin over the 8 XCDs; give each
@@ -413,7 +417,9 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     // contiguous run of full rows
     const int64_t e0 = st.ebase[s] + (int64_t)h * L * K + it.begin;
     const uint32_t* ent = entries + e0;
-    for (int r = threadIdx.x; r < it.count; r += NT) sent[r] = ent[r];
+    if constexpr (LDS_ENT)
+        for (int r = threadIdx.x; r < it.count; r += NT) sent[r] = ent[r];
+    const uint32_t* esrc = LDS_ENT ? sent : ent;
 
     // gathered query fragments of the first tile are requested before the
     // K / V staging so the two overlap
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
                 for (int ks = 0; ks < W::QREG; ++ks) wt.qf[sb][ks] = qfn[sb][ks];
             }
         }
-        if (base + TR < it.count) fetch_q(base + TR, qn, qfn, sent);
+        if (base + TR < it.count) fetch_q(base + TR, qn, qfn, esrc);
         wt.scores(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
         float m2[2], sum[2];
 #pragma unroll
@@ -484,20 +490,27 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) x[dt][r4] = wt.o[sb][dt][r4] * inv;
             if constexpr (STAGE) {
-                char* st_w = ostage + wave * 16 * RS;
-                store_lane_row<T, NDT>((T*)(st_w + l16 * RS) + g4 * (D / 4), x);
-                // (LDS accesses of one wave complete in order)
+                char* st_w = ostage + wave * SR * RS;
                 constexpr int CPR = RB / 16;                  // 16-byte chunks per row
 #pragma unroll
-                for (int n = 0; n < 16 * CPR / 64; ++n) {
-                    const int qc = 64 * n + lane, r = qc / CPR, c = qc % CPR;
-                    const u32x4_t w = *(const u32x4_t*)(st_w + r * RS + c * 16);
-                    if (row0 + r < it.count)
-                        // whole rows, non-temporal: read back only by the merge
-                        // kernel, much later; kept out of the way in L2 they
-                        // leave room for the gathered query rows other lists
-                        // reuse (routed reads 1.76 -> 1.40 GB at 2 x 64K)
-                        __builtin_nontemporal_store(w, (u32x4_t*)((char*)po + (size_t)(e0 + row0 + r) * RB + c * 16));
+                for (int hp = 0; hp < 16 / SR; ++hp) {
+                    // rows hp*SR .. hp*SR + SR-1 of the sub-tile
+                    if (l16 / SR == hp)
+                        store_lane_row<T, NDT>((T*)(st_w + (l16 % SR) * RS) + g4 * (D / 4), x);
+                    // (LDS accesses of one wave complete in order)
+#pragma unroll
+                    for (int n = 0; n < SR * CPR / 64; ++n) {
+                        const int qc = 64 * n + lane, r = qc / CPR, c = qc % CPR;
+                        const int rr = hp * SR + r;
+                        const u32x4_t w = *(const u32x4_t*)(st_w + r * RS + c * 16);
+                        if (row0 + rr < it.count)
+                            // whole rows, non-temporal: read back only by the
+                            // merge kernel, much later; kept out of the way in
+                            // L2 they leave room for the gathered query rows
+                            // other lists reuse (routed reads 1.76 -> 1.40 GB
+                            // at 2 x 64K)
+                            __builtin_nontemporal_store(w, (u32x4_t*)((char*)po + (size_t)(e0 + row0 + rr) * RB + c * 16));
+                    }
                 }
             } else {
                 // (64-byte pieces of rows: a non-temporal hint would skip the
