@@ -419,7 +419,6 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     const uint32_t* ent = entries + e0;
     if constexpr (LDS_ENT)
         for (int r = threadIdx.x; r < it.count; r += NT) sent[r] = ent[r];
-    const uint32_t* esrc = LDS_ENT ? sent : ent;
 
     // gathered query fragments of the first tile are requested before the
     // K / V staging so the two overlap
@@ -427,13 +426,21 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     u16x8_t qn[2][W::BF ? W::QREG : 1];
     float qfn[2][W::BF ? 1 : W::QREG];
     int base = 32 * wave;
+    // the entries (query, slot) of a tile's two sub-tile rows of this lane
+    auto tile_ent = [&](int b0, const uint32_t* src, uint32_t (&e)[2]) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const int r = b0 + 16 * sb + l16;
+            e[sb] = r < it.count ? src[r] : 0u;
+        }
+    };
     auto fetch_q = [&](int b0, u16x8_t (&qb)[2][W::BF ? W::QREG : 1], float (&qf)[2][W::BF ? 1 : W::QREG],
-                       const uint32_t* src) {
+                       const uint32_t (&ev)[2]) {
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int r = b0 + 16 * sb + l16;
             const bool ok = r < it.count;
-            const uint32_t e = ok ? src[r] : 0u;
+            const uint32_t e = ev[sb];
             const T* qrow = ok ? q + ((size_t)(e >> 5) * H + h) * D : nullptr;
             if constexpr (W::BF) {
 #pragma unroll
@@ -451,7 +458,12 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
             }
         }
     };
-    if (base < it.count) fetch_q(base, qn, qfn, ent);
+    uint32_t en[2];
+    tile_ent(base, ent, en);
+    if (base < it.count) fetch_q(base, qn, qfn, en);
+    // entries from global memory are requested a tile before their rows, so
+    // a row gather never waits for its entry
+    if constexpr (!LDS_ENT) tile_ent(base + TR, ent, en);
     load_kv<T, D, BLK, NT>(sm, k, v, (size_t)(t0 + j * BLK) * H + h, H, BLK);
     __syncthreads();
 
@@ -471,7 +483,11 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
                 for (int ks = 0; ks < W::QREG; ++ks) wt.qf[sb][ks] = qfn[sb][ks];
             }
         }
-        if (base + TR < it.count) fetch_q(base + TR, qn, qfn, esrc);
+        if (base + TR < it.count) {
+            if constexpr (LDS_ENT) tile_ent(base + TR, sent, en);
+            fetch_q(base + TR, qn, qfn, en);
+            if constexpr (!LDS_ENT) tile_ent(base + 2 * TR, ent, en);
+        }
         wt.scores(sm, l16, g4, BLK / 16 - 1, BLK / 16 - 1);
         float m2[2], sum[2];
 #pragma unroll
