@@ -373,15 +373,19 @@ __device__ __forceinline__ void store4(T* p, const float (&x)[4])
 // processed in tiles of 128 queries (4 waves x 2 sub-tiles x 16) while K_j
 // and V_j stay in LDS
 template <typename T, int D, int BLK>
-__global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
+// (bf16 d = 64: at most 128 VGPRs, 4 waves per SIMD)
+__global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void routed_attn_kernel(
     SegTable st, const Item* __restrict__ items, const uint32_t* __restrict__ entries,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float sl2,
     T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
-    // d = 64: the item's entries in LDS; d = 128 reads them from global
-    // memory (L2), so LDS keeps room for the staged rows at 2 workgroups/CU
-    constexpr bool LDS_ENT = D == 64 || sizeof(T) != 2;
+    // bf16: entries are read from global memory (L2) a tile ahead instead of
+    // from an LDS copy, and partial rows are staged 8 at a time, so LDS
+    // allows 4 workgroups per CU at d = 64 (3 with the copy: routed kernel
+    // -10 % at B = 128) and 2 at d = 128 (1 with 16 staged rows).  With
+    // 64-key blocks LDS never limits and the LDS copy is kept.
+    constexpr bool LDS_ENT = sizeof(T) != 2 || (D == 64 && BLK == 64);
     __shared__ uint32_t sent[LDS_ENT ? kItemRows : 1];
     constexpr int NDT = D / 16;
     using W = Wave2<T, D, BLK>;
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(64 * kRoutedWaves) void routed_attn_kernel(
     constexpr bool STAGE = sizeof(T) == 2;
     constexpr int RB = D * (int)sizeof(T);            // partial row bytes
     constexpr int RS = RB + 16;                       // staged row stride
-    constexpr int SR = D == 64 ? 16 : 8;              // rows staged per pass
+    constexpr int SR = LDS_ENT ? 16 : 8;              // rows staged per pass
     __shared__ __align__(16) char ostage[STAGE ? kRoutedWaves * SR * RS : 16];
     constexpr int NT = 64 * kRoutedWaves;             // threads
     constexpr int TR = 32 * kRoutedWaves;             // rows per tile
