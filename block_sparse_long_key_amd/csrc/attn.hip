@@ -31,6 +31,8 @@
 // of the rounded weights, so each output row is a convex combination of V
 // rows with the weights used (fp32 accumulation); the log-sum-exp uses the
 // unrounded fp32 weights.
+#include <type_traits>
+
 #include "moba_internal.h"
 
 namespace moba {
@@ -74,22 +76,42 @@ struct Smem {
     T vt[D * VS];
 };
 
+// The same strides with V^T over K's storage: a kernel loads V^T only after
+// its last read of K (halves the LDS of one key block's stage).
+template <typename T, int D, int BLK>
+struct SmemOne {
+    static constexpr bool BF = sizeof(T) == 2;
+    static constexpr int KS = Smem<T, D, BLK>::KS;
+    static constexpr int VS = Smem<T, D, BLK>::VS;
+    static constexpr int N = BLK * KS > D * VS ? BLK * KS : D * VS;
+    union {
+        T k[N];
+        T vt[N];
+    };
+};
+
 // Load rows [0, nrows) of a key block (rows >= nrows are zero) into LDS:
-// K row-major, V transposed.  row u of the block is global row (row0 + u*H).
-template <typename T, int D, int BLK, int NT>
-__device__ __forceinline__ void load_kv(Smem<T, D, BLK>& sm, const T* __restrict__ k,
-                                        const T* __restrict__ v, size_t row0, int H, int nrows)
+// K row-major (load_k), V transposed (load_vt).  Row u of the block is
+// global row (row0 + u*H).
+template <typename T, int D, int BLK, int NT, typename SM>
+__device__ __forceinline__ void load_k(SM& sm, const T* __restrict__ k, size_t row0, int H, int nrows)
 {
-    using S = Smem<T, D, BLK>;
     constexpr int EPC = 16 / sizeof(T);      // elements per 16-byte chunk
     constexpr int CPR = D / EPC;             // chunks per row
     for (int e = threadIdx.x; e < BLK * CPR; e += NT) {
         const int u = e / CPR, c = e % CPR;
         u32x4_t val = {0u, 0u, 0u, 0u};
         if (u < nrows) val = *(const u32x4_t*)(k + (row0 + (size_t)u * H) * D + c * EPC);
-        *(u32x4_t*)(sm.k + u * S::KS + c * EPC) = val;
+        *(u32x4_t*)(sm.k + u * SM::KS + c * EPC) = val;
     }
-    if constexpr (S::BF) {
+}
+
+template <typename T, int D, int BLK, int NT, typename SM>
+__device__ __forceinline__ void load_vt(SM& sm, const T* __restrict__ v, size_t row0, int H, int nrows)
+{
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr int CPR = D / EPC;
+    if constexpr (SM::BF) {
         // two rows per thread so V^T is written as 32-bit words
         for (int e = threadIdx.x; e < (BLK / 2) * CPR; e += NT) {
             const int p = e % (BLK / 2), c = e / (BLK / 2);
@@ -100,7 +122,7 @@ __device__ __forceinline__ void load_kv(Smem<T, D, BLK>& sm, const T* __restrict
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
                 const uint32_t word = (uint32_t)v0[r] | ((uint32_t)v1[r] << 16);
-                *(uint32_t*)(sm.vt + (c * 8 + r) * S::VS + u) = word;
+                *(uint32_t*)(sm.vt + (c * 8 + r) * SM::VS + u) = word;
             }
         }
     } else {
@@ -108,13 +130,21 @@ __device__ __forceinline__ void load_kv(Smem<T, D, BLK>& sm, const T* __restrict
             const int u = e % BLK, c = e / BLK;
             float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
             if (u < nrows) val = *(const float4*)((const float*)v + (row0 + (size_t)u * H) * D + c * 4);
-            float* dst = (float*)sm.vt + (c * 4) * S::VS + u;
+            float* dst = (float*)sm.vt + (c * 4) * SM::VS + u;
             dst[0] = val.x;
-            dst[S::VS] = val.y;
-            dst[2 * S::VS] = val.z;
-            dst[3 * S::VS] = val.w;
+            dst[SM::VS] = val.y;
+            dst[2 * SM::VS] = val.z;
+            dst[3 * SM::VS] = val.w;
         }
     }
+}
+
+template <typename T, int D, int BLK, int NT>
+__device__ __forceinline__ void load_kv(Smem<T, D, BLK>& sm, const T* __restrict__ k,
+                                        const T* __restrict__ v, size_t row0, int H, int nrows)
+{
+    load_k<T, D, BLK, NT>(sm, k, row0, H, nrows);
+    load_vt<T, D, BLK, NT>(sm, v, row0, H, nrows);
 }
 
 // Per-wave tile state: two sub-tiles of 16 queries each against BLK keys.
@@ -156,9 +186,9 @@ struct Wave2 {
     // The K fragments of tile kt+1 are read from LDS while tile kt's MFMAs
     // run; the scheduling fences keep the compiler from hoisting every
     // fragment load (which would double the register footprint).
-    __device__ __forceinline__ void scores(const Smem<T, D, BLK>& sm, int l16, int g4, int km0, int km1)
+    template <typename S>
+    __device__ __forceinline__ void scores(const S& sm, int l16, int g4, int km0, int km1)
     {
-        using S = Smem<T, D, BLK>;
         const int km = km0 > km1 ? km0 : km1;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt) {
@@ -205,9 +235,9 @@ struct Wave2 {
 
     // O^T = V^T P^T over key tiles kt <= km[sb]; s[] holds P.  One key step
     // (32 keys) at a time, fenced like scores().
-    __device__ __forceinline__ void pv(const Smem<T, D, BLK>& sm, int l16, int g4, int km0, int km1)
+    template <typename S>
+    __device__ __forceinline__ void pv(const S& sm, int l16, int g4, int km0, int km1)
     {
-        using S = Smem<T, D, BLK>;
         const int km = km0 > km1 ? km0 : km1;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -560,14 +590,18 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
     const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
     float sl2, T* __restrict__ o, float* __restrict__ lse)
 {
-    __shared__ __align__(16) Smem<T, D, BLK> sm;
+    // bf16 d = 128: V^T is loaded over K once the scores are done, so the
+    // stage takes half the LDS and 3 workgroups fit a CU (2 otherwise)
+    constexpr bool ONE = sizeof(T) == 2 && D == 128;
+    using SM = std::conditional_t<ONE, SmemOne<T, D, BLK>, Smem<T, D, BLK>>;
+    __shared__ __align__(16) SM sm;
     __shared__ float own_lse[BLK];
     constexpr int NDT = D / 16;
     constexpr int CH = 16 / sizeof(T);        // elements per 16-byte chunk
     constexpr int NCH = D / CH;               // chunks per row
     constexpr int QPP = 64 / NCH;             // queries per wave pass
     constexpr int PF = 8;                     // slots loaded together
-    static_assert(BLK * D <= BLK * Smem<T, D, BLK>::KS, "own rows fit over K");
+    static_assert(BLK * D <= BLK * SM::KS, "own rows fit over K");
     T* own = sm.k;                            // [BLK][D], lane-permuted rows
 
     const int g = blockIdx.x, h = blockIdx.y;
@@ -578,7 +612,8 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
     const int L = seq_len(st, s);
     const int nq = min(BLK, L - i * BLK);
     const size_t row0 = (size_t)(t0 + i * BLK) * H + h;
-    load_kv<T, D, BLK, 2 * BLK>(sm, k, v, row0, H, nq);
+    load_k<T, D, BLK, 2 * BLK>(sm, k, row0, H, nq);
+    if constexpr (!ONE) load_vt<T, D, BLK, 2 * BLK>(sm, v, row0, H, nq);
     __syncthreads();
 
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -600,6 +635,14 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         for (int sb = 0; sb < 2; ++sb)
             wt.template softmax<true>(sb, sl2, g4, sb ? km1 : km0, 32 * wave + 16 * sb + l16,
                                       m2[sb], sum[sb]);
+    }
+    if constexpr (ONE) {
+        __syncthreads();                      // every wave is done with K
+        load_vt<T, D, BLK, 2 * BLK>(sm, v, row0, H, nq);
+        __syncthreads();
+    }
+    if (active) {
+        const int km0 = 2 * wave, km1 = 2 * wave + 1;
         wt.pv(sm, l16, g4, km0, km1);
     }
     __syncthreads();
