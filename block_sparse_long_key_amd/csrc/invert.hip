@@ -5,7 +5,7 @@
 // varlen layout indexed by key block, which the gather-and-densify forward
 // consumes.  This is that step, written as a counting sort with no global
 // atomics:
-//   count   -- one workgroup per (sequence, head, chunk of 32 query blocks):
+//   count   -- one workgroup per (sequence, head, chunk of query blocks):
 //              LDS histogram of the routed past blocks; row of the count
 //              matrix cm[chunk][j] for the lists j this chunk can reach;
 //   scan    -- one workgroup per (sequence, head): list totals, list offsets,
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const 
     const int cl = c - st.cbase[s];
     const int n = seq_nblk(st, s), L = seq_len(st, s), t0 = st.cu[s];
     const int B = st.B, K = st.K, H = st.H;
-    const int ib0 = cl * kInvChunkBlocks, ib1 = min(n, ib0 + kInvChunkBlocks);
+    const int ib0 = cl * st.chunk, ib1 = min(n, ib0 + st.chunk);
     const int nl = ib1;                       // lists reachable: j < ib1
     for (int j = threadIdx.x; j < nl; j += kThreads) hist[j] = 0;
     __syncthreads();
@@ -105,10 +105,10 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
     const int64_t ib = st.ibase[s] + (int64_t)h * seq_item_cap(st, s);
     const int64_t cap = seq_item_cap(st, s);
 
-    // list totals (chunk c reaches list j iff j < (c+1)*kInvChunkBlocks)
+    // list totals (chunk c reaches list j iff j < (c+1)*chunk)
     for (int j = threadIdx.x; j < n; j += kScanThreads) {
         int t = 0;
-        for (int c = j / kInvChunkBlocks; c < nch; ++c) t += cm[(int64_t)c * n + j];
+        for (int c = j / st.chunk; c < nch; ++c) t += cm[(int64_t)c * n + j];
         tot[j] = t;
     }
     __syncthreads();
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
     for (int j = threadIdx.x; j < n; j += kScanThreads) {
         const int beg = tot[j];
         int run = beg;
-        for (int c = j / kInvChunkBlocks; c < nch; ++c) {
+        for (int c = j / st.chunk; c < nch; ++c) {
             const int v = cm[(int64_t)c * n + j];
             cm[(int64_t)c * n + j] = run;
             run += v;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     const int cl = c - st.cbase[s];
     const int n = seq_nblk(st, s), L = seq_len(st, s), t0 = st.cu[s];
     const int B = st.B, K = st.K, H = st.H;
-    const int ib0 = cl * kInvChunkBlocks, ib1 = min(n, ib0 + kInvChunkBlocks);
+    const int ib0 = cl * st.chunk, ib1 = min(n, ib0 + st.chunk);
     const int32_t* pos = cm_base(st, const_cast<int32_t*>(cmat), s, h) + (int64_t)cl * n;
     uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K;
     const int tl0 = ib0 * B, tl1 = min(L, ib1 * B);

@@ -15,7 +15,10 @@ namespace moba {
 constexpr int kMaxSeqs = MOBA_MAX_SEQS;
 // most queries per routed-attention work item (looped in tiles of 128)
 constexpr int kItemRows = 2048;
-// query blocks per inversion chunk (one workgroup of the count/scatter passes)
+// query blocks per inversion chunk (one workgroup of the count/scatter
+// passes): this many, or for sequences of more than 1024 blocks the power of
+// two reaching 1/16 of the longest one's blocks, so a chunk's entries still
+// land in runs of several entries per list when there are thousands of lists
 constexpr int kInvChunkBlocks = 32;
 // largest number of blocks of one sequence (LDS histogram of the inversion)
 constexpr int kMaxBlocksPerSeq = 16384;
@@ -27,6 +30,7 @@ struct SegTable {
     int32_t K;          // top_k (own block included)
     int32_t total_blocks;
     int32_t total_chunks;   // inversion chunks over all sequences (per head)
+    int32_t chunk;          // query blocks per inversion chunk
     int64_t total_items;    // routed-attention item capacity over all (seq, head)
     int32_t cu[kMaxSeqs + 1];     // token start of sequence s
     int32_t boff[kMaxSeqs + 1];   // first global block of sequence s

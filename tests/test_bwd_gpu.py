@@ -58,6 +58,9 @@ CASES = {
     "ragged": _spec("H", seqlens=(1, 127, 129, 700, 0, 300), heads=2),
     "top1": _spec("H", seq=1000, heads=2, top_k=1),
     "top32-B64": _spec("C4", seq=4096, heads=1, top_k=32),
+    # 1094 key blocks: more than 1024, so the index pass takes chunks of 128
+    # query blocks instead of 32
+    "long-B64": _spec("C4", seq=70000, heads=1, top_k=8),
 }
 
 
@@ -103,7 +106,7 @@ def test_bwd_repeatable():
     computed alone and the pieces are added in slot order; the backward's
     index pass places each list's entries in an order that depends only on
     idx, so dK / dV sum the same rows in the same tiles every time."""
-    for name in ("H-2k", "C4-4k"):
+    for name in ("H-2k", "C4-4k", "long-B64"):
         s = CASES[name]
         x, cu, do, idx, a = _run(s)
         _, _, _, _, b = _run(s)
