@@ -219,25 +219,28 @@ __global__ __launch_bounds__(256) void route_kernel(SegTable st, const T* __rest
 //                <= (2^-16 + (2d + 16) 2^-23) * |q| * max_j |c_j|  =: E,
 // and the separation test / fp64 re-scoring work as in the VALU kernel.
 //
-// Workgroup = one query block of one head, B/32 waves of 32 queries (two
-// 16-query sub-tiles); centroid tiles of 64 blocks are staged in LDS as
-// hi / lo rows.  S^T = C Q^T puts 4 blocks x 1 query in each lane.
+// route_prep_kernel splits every centroid once (hi, lo, |c|^2).  Workgroup
+// = one query block of one head, B/32 waves of 32 queries (two 16-query
+// sub-tiles); the hi / lo rows are copied into LDS in tiles of 64 blocks.
+// S^T = C Q^T puts 4 blocks x 1 query in each lane.
 //
 // Selection without branches: a score s of block j becomes a float key whose
 // low LB mantissa bits hold j, |key - s| <= 2^(LB-23) |s|.  Keys are unique
 // and decode back to their block; how they order equal scores does not
 // matter, since two keys within 2E of each other at the selection boundary
 // send the row to the exact fp64 path, and inside the selection order is
-// irrelevant (the output is sorted by block).  A lane keeps its KMAX best keys
+// irrelevant (the output is sorted by block).  A lane keeps its LL best keys
 // in a descending list, and inserting a key x is one v_med3_f32 per slot,
 // a[p] = med3(a[p-1], a[p], x).  The key error is added to E in the
 // separation test.  The 4 lanes of a query merge their lists by shuffles.
 //
-// Near-ties (the separation test fails) are finished by two small kernels
-// that run right after (route_fix_kernel): when the query's K best keys are
-// provably the only blocks that can still be selected, the row carries them
-// (K fp64 re-scorings); otherwise the row is marked for an fp64 re-scoring
-// of every past block.
+// Near-ties (the separation test fails) are finished by route_fix_kernel,
+// which runs right after: when the query's K best keys are provably the only
+// blocks that can still be selected, the row carries them (K fp64
+// re-scorings); otherwise, for k >= 6, it carries its best 2K-4 blocks and a
+// bound on every other block (2K-4 fp64 re-scorings, enough unless one lane
+// held nearly all of the top k); only the rest are re-scored in fp64
+// against every past block.
 __device__ __forceinline__ bool ranks_before64(double sa, int ja, double sb, int jb)
 {
     return sa > sb || (sa == sb && ja < jb);
