@@ -9,7 +9,8 @@
 // The pages' kernel targets another GPU; here the design is CDNA4-first:
 //
 // routed kernel -- one workgroup (4 waves) per work item = one key block j
-//   of one (sequence, head) and up to 128 of the queries that routed to it.
+//   of one (sequence, head) and up to 2048 of the queries that routed to it,
+//   taken in tiles of 128.
 //   K_j goes to LDS row-major, V_j to LDS transposed (so both MFMA operands
 //   are contiguous 16-byte / 8-byte LDS reads).  Each wave gathers 32 query
 //   rows straight from HBM into registers and computes, per 16-query
@@ -21,11 +22,12 @@
 //   Output: one normalised partial o (I/O dtype) and its log2-sum-exp per
 //   (query, slot), stored in list order so each tile's writes are one
 //   contiguous run of full rows (scattered partial-line writes cost far
-//   more than the MFMA work).
+//   more than the MFMA work); bf16 rows are staged in LDS and stored whole.
 // own-block kernel -- one workgroup per (query block i, head): the causal
 //   tile Q_i K_i^T (u <= t), same MFMA scheme, skipping key tiles that are
-//   fully masked, then the merge of that result with the query's routed
-//   partials (log-sum-exp weights, fp32), writing O and LSE.
+//   fully masked (bf16 d = 128: V_i^T staged over K_i after the scores),
+//   then the merge of that result with the query's routed partials
+//   (log-sum-exp weights, fp32), writing O and LSE.
 // fp32 I/O uses v_mfma_f32_16x16x4_f32 on the same skeleton (correctness
 // path); bf16 rounds P to bf16 for the PV product and normalises by the sum
 // of the rounded weights, so each output row is a convex combination of V
