@@ -368,7 +368,8 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                   stream=None):
     """Gradients (dq, dk, dv) of moba_attn_fwd's output for the selection idx.
 
-    o and lse are that forward's outputs; dout is dL/dO.  bf16 only.
+    o and lse are that forward's outputs; dout is dL/dO.  bf16 (fast path) or
+    fp32 (plain recompute path).
     """
     _dev(q, k, v, idx, o, lse, dout)
     if not (q.shape == k.shape == v.shape == o.shape == dout.shape):

@@ -71,16 +71,6 @@ __device__ __forceinline__ u16x8_t pack8(const f32x4_t& lo, const f32x4_t& hi)
     return __builtin_bit_cast(u16x8_t, w);
 }
 
-__device__ __forceinline__ int seq_of_token(const SegTable& st, int t)
-{
-    int lo = 0, hi = st.nseq - 1;
-    while (lo < hi) {                    // last s with cu[s] <= t
-        const int mid = (lo + hi + 1) >> 1;
-        if (st.cu[mid] <= t) lo = mid; else hi = mid - 1;
-    }
-    return lo;
-}
-
 // ------------------------------------------------------------------------
 // D_t = dO_t . O_t and lse2_t = lse_t * log2(e), one row per D/8 lanes
 template <int D>

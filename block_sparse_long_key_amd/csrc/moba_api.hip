@@ -376,7 +376,6 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
-    if (L.dtype != MOBA_BF16) return MOBA_ERR_UNSUPPORTED;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
         !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
         return MOBA_ERR_INVALID_ARG;
@@ -394,8 +393,13 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
     // repeatable list order: dK / dV sum each list's rows in that order
     hipError_t e = run_index(Ll, L, ws, (char*)workspace, idx, true);
     if (e != hipSuccess) return MOBA_ERR_HIP;
-    return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout,
-                                      resolve_scale(softmax_scale, L.D), dq, dk, dv));
+    const float scale = resolve_scale(softmax_scale, L.D);
+    if (L.dtype == MOBA_F32) {
+        const int32_t* ia = expands(Ll) ? (const int32_t*)((char*)workspace + ws.px_off) : idx;
+        return hip_status(launch_attn_bwd_f32(L, ws, (char*)workspace, ia, q, k, v, o, lse, dout, scale,
+                                              dq, dk, dv));
+    }
+    return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout, scale, dq, dk, dv));
 }
 
 }  // extern "C"

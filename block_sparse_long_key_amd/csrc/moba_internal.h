@@ -59,6 +59,16 @@ __device__ inline int seq_of_block(const SegTable& st, int g) {
     while (lo > 0 && st.boff[lo] > g) --lo;
     return lo;
 }
+// sequence holding token t (the last s with cu[s] <= t: with empty
+// sequences sharing a start, the nonempty one that follows them)
+__device__ inline int seq_of_token(const SegTable& st, int t) {
+    int lo = 0, hi = st.nseq - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (st.cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
 __device__ inline int seq_of_chunk(const SegTable& st, int c) {
     int lo = 0, hi = st.nseq - 1;
     while (lo < hi) {
@@ -166,6 +176,11 @@ hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                            const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, float scale, void* dq, void* dk, void* dv);
+// fp32 inputs; idx: the selection in the launch's blocks (expanded for B > 128)
+hipError_t launch_attn_bwd_f32(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
+                               const void* q, const void* k, const void* v, const void* o,
+                               const float* lse, const void* dout, float scale, void* dq, void* dk,
+                               void* dv);
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, float scale, void* o, float* lse);

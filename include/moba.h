@@ -231,13 +231,14 @@ moba_status moba_attn_combine(const moba_shape *shape, const void *q,
  *   P_tu = exp(scale q_t.k_u - lse_t) and D_t = dout_t . o_t:
  *     dv_u = sum_t P_tu dout_t,  dS_tu = P_tu (dout_t . v_u - D_t),
  *     dq_t = scale sum_u dS_tu k_u,  dk_u = scale sum_t dS_tu q_t.
- *   bf16 only (MOBA_ERR_UNSUPPORTED for fp32): P and dS enter the matrix
- *   products as bf16, every sum is fp32, outputs are rounded once.
+ *   bf16: P and dS enter the matrix products as bf16, every sum is fp32,
+ *   outputs are rounded once.  fp32 (a plain recompute path, for exactness
+ *   rather than speed): every product and sum in fp32, in a fixed order.
  *   workspace: at least moba_attn_bwd_workspace_bytes(), 256-byte aligned,
- *   scratch on exit; it holds the inverted lists and one fp32 dq piece per
- *   routed (query, slot) pair.  No atomics on results: dq, dk and dv are
- *   bitwise repeatable (dk / dv for sequences of up to 4096 blocks; longer
- *   ones may differ between runs by fp32 summation order).
+ *   scratch on exit; it holds the inverted lists and (bf16) one fp32 dq
+ *   piece per routed (query, slot) pair.  No atomics on results: dq, dk and
+ *   dv are bitwise repeatable (dk / dv for sequences of up to 4096 blocks;
+ *   longer ones may differ between runs by fp32 summation order).
  *   Same error behaviour as moba_attn_fwd.
  */
 moba_status moba_attn_bwd(const moba_shape *shape, const void *q,

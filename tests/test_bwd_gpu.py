@@ -61,7 +61,14 @@ CASES = {
     # 1094 key blocks: more than 1024, so the index pass takes chunks of 128
     # query blocks instead of 32
     "long-B64": _spec("C4", seq=70000, heads=1, top_k=8),
+    # fp32 inputs (the plain recompute path)
+    "f32-C1": _spec("C1"),
+    "f32-B128": _spec("H", seq=1500, heads=2, dtype="f32"),
+    "f32-varlen-d128": _spec("C5", seqlens=(300, 129, 0, 640), heads=2, block_size=64, top_k=4,
+                             dtype="f32"),
 }
+# fp32: every product and sum in fp32 against the oracle's fp64
+MAX_REL_F32, MEAN_REL_F32 = 1e-4, 1e-5
 
 
 def _run(s):
@@ -80,14 +87,15 @@ def _run(s):
     return x, cu, do, idx, (dq, dk, dv)
 
 
-def _check(name, got, ref, what):
+def _check(name, got, ref, what, dtype="bf16"):
+    bar_max, bar_mean = (MAX_REL, MEAN_REL) if dtype == "bf16" else (MAX_REL_F32, MEAN_REL_F32)
     err = np.abs(got.astype(np.float64) - ref)
     mx_rel = err.max() / max(np.abs(ref).max(), 1e-30)
     mean_rel = err.mean() / max(np.abs(ref).mean(), 1e-30)
     print(f"[{name}] {what}: max|err|/max|ref| {mx_rel:.2e}  mean|err|/mean|ref| {mean_rel:.2e}",
           flush=True)
-    assert mx_rel <= MAX_REL, f"{name} {what}: max rel {mx_rel:.3e}"
-    assert mean_rel <= MEAN_REL, f"{name} {what}: mean rel {mean_rel:.3e}"
+    assert mx_rel <= bar_max, f"{name} {what}: max rel {mx_rel:.3e}"
+    assert mean_rel <= bar_mean, f"{name} {what}: mean rel {mean_rel:.3e}"
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -98,7 +106,7 @@ def test_bwd_matches_oracle(name):
     H, d = s.heads, s.head_dim
     ref = oracle.attend_bwd(x["q"], x["k"], x["v"], idx, do, s.block_size, s.top_k, cu)
     for g, r, w in zip(got, ref, ("dq", "dk", "dv")):
-        _check(name, _np(g).reshape(-1, H, d), r, w)
+        _check(name, _np(g).reshape(-1, H, d), r, w, s.dtype)
 
 
 def test_bwd_repeatable():
@@ -106,7 +114,7 @@ def test_bwd_repeatable():
     computed alone and the pieces are added in slot order; the backward's
     index pass places each list's entries in an order that depends only on
     idx, so dK / dV sum the same rows in the same tiles every time."""
-    for name in ("H-2k", "C4-4k", "long-B64"):
+    for name in ("H-2k", "C4-4k", "long-B64", "f32-varlen-d128"):
         s = CASES[name]
         x, cu, do, idx, a = _run(s)
         _, _, _, _, b = _run(s)
