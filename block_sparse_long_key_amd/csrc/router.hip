@@ -477,9 +477,10 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                     acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
             }
             // keys: the scores with their low LB mantissa bits replaced by j.
-            // A key at or below the lane's last kept key changes nothing, so
-            // each insertion runs only where some lane's key passes the
-            // threshold of the group's start (the wave skips it otherwise)
+            // A key at or below the lane's last kept key changes nothing;
+            // each insertion is masked to the lanes whose key passes the
+            // threshold of the group's start (straight-line code: at these
+            // list lengths nearly every wave has such a lane for every key)
             const float thr = key[sb][LL - 1];
             float x[4];
             bool pass[4];
