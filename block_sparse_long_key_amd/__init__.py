@@ -169,6 +169,42 @@ def _rows(x: torch.Tensor) -> Tuple[int, ...]:
     return tuple(x.shape[:-1])
 
 
+# The C ABI takes plain pointers, so every buffer size is checked here: a
+# wrong-sized tensor raises instead of reaching a kernel.
+def _expect(t: Optional[torch.Tensor], shape, dtype, name: str):
+    if t is None:
+        return
+    _dev(t)
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise MobaError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
+def _like(t: Optional[torch.Tensor], ref: torch.Tensor, name: str):
+    _expect(t, ref.shape, ref.dtype, name)
+
+
+def _ws(t: torch.Tensor, need: int):
+    _dev(t)
+    if t.dtype != torch.uint8 or t.dim() != 1:
+        raise MobaError("workspace must be a 1-D uint8 tensor")
+    if t.numel() < need:
+        raise MobaError(f"workspace has {t.numel()} bytes, {need} needed")
+
+
+def _qkv(q, k, v):
+    _dev(q, k, v)
+    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
+        raise MobaError("q, k, v must share shape and dtype")
+
+
+def _idx(idx, q, top_k):
+    _expect(idx, _rows(q) + (top_k,), torch.int32, "idx")
+
+
+def _cent_shape(k, block_size, cu_seqlens):
+    return (moba_total_blocks(k, block_size, cu_seqlens), k.shape[-2], k.shape[-1])
+
+
 def moba_total_blocks(x: torch.Tensor, block_size: int, cu_seqlens=None) -> int:
     sh, keep = _make_shape(x, block_size, 1, cu_seqlens)
     n = _load().moba_total_blocks(ctypes.byref(sh))
@@ -209,9 +245,14 @@ def moba_key_conv(k: torch.Tensor, w: torch.Tensor, block_size: int,
         raise MobaError("w must be fp32 [heads, head_dim, width]")
     if out is None:
         out = torch.empty_like(k)
-    if with_centroids and cent is None:
-        nb = moba_total_blocks(k, block_size, cu_seqlens)
-        cent = torch.empty((nb, k.shape[-2], k.shape[-1]), dtype=torch.float32, device=k.device)
+    _like(out, k, "out")
+    if out.data_ptr() == k.data_ptr():
+        raise MobaError("out must not alias k")
+    if with_centroids:
+        if cent is None:
+            cent = torch.empty(_cent_shape(k, block_size, cu_seqlens), dtype=torch.float32,
+                               device=k.device)
+        _expect(cent, _cent_shape(k, block_size, cu_seqlens), torch.float32, "cent")
     rc = _load().moba_key_conv(ctypes.byref(sh), _p(k), _p(w), w.shape[2],
                                _CONV_MODES[mode], _p(out),
                                _p(cent if with_centroids else None), _stream(stream))
@@ -236,9 +277,10 @@ def moba_key_conv_bwd(k: torch.Tensor, w: torch.Tensor, dk_out: torch.Tensor, bl
         raise MobaError("w must be fp32 [heads, head_dim, width]")
     sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
     W = int(w.shape[2])
+    need = moba_key_conv_bwd_workspace_bytes(k, block_size, W, cu_seqlens)
     if workspace is None:
-        need = moba_key_conv_bwd_workspace_bytes(k, block_size, W, cu_seqlens)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=k.device)
+    _ws(workspace, need)
     dk = torch.empty_like(k)
     dw = torch.empty_like(w)
     rc = _load().moba_key_conv_bwd(ctypes.byref(sh), _p(k), _p(w), W, _CONV_MODES[mode],
@@ -254,8 +296,9 @@ def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,
     _dev(k)
     sh, keep = _make_shape(k, block_size, 1, cu_seqlens)
     if out is None:
-        nb = moba_total_blocks(k, block_size, cu_seqlens)
-        out = torch.empty((nb, k.shape[-2], k.shape[-1]), dtype=torch.float32, device=k.device)
+        out = torch.empty(_cent_shape(k, block_size, cu_seqlens), dtype=torch.float32,
+                          device=k.device)
+    _expect(out, _cent_shape(k, block_size, cu_seqlens), torch.float32, "out")
     _check(_load().moba_centroids(ctypes.byref(sh), _p(k), _p(out), _stream(stream)),
            "moba_centroids")
     return out
@@ -271,11 +314,14 @@ def moba_route_topk(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k:
     when None."""
     _dev(q, cent)
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _expect(cent, _cent_shape(q, block_size, cu_seqlens), torch.float32, "cent")
     if out is None:
         out = torch.empty(_rows(q) + (top_k,), dtype=torch.int32, device=q.device)
+    _idx(out, q, top_k)
     need = int(_load().moba_route_topk_workspace_bytes(ctypes.byref(sh)))
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _ws(workspace, need)
     _check(_load().moba_route_topk(ctypes.byref(sh), _p(q), _p(cent), _p(out), _p(workspace),
                                    workspace.numel(), _stream(stream)),
            "moba_route_topk")
@@ -286,18 +332,24 @@ def _workspace(q, block_size, top_k, cu_seqlens, workspace):
     need = moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _ws(workspace, need)
     return workspace
 
 
 def moba_attn_index(idx, q, block_size, top_k, workspace, cu_seqlens=None, stream=None):
+    _dev(q)
+    _idx(idx, q, top_k)
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _ws(workspace, moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens))
     _check(_load().moba_attn_index(ctypes.byref(sh), _p(idx), _p(workspace),
                                    workspace.numel(), _stream(stream)), "moba_attn_index")
 
 
 def moba_attn_routed(q, k, v, block_size, top_k, workspace, scale=None, cu_seqlens=None,
                      stream=None):
+    _qkv(q, k, v)
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _ws(workspace, moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens))
     _check(_load().moba_attn_routed(ctypes.byref(sh), _p(q), _p(k), _p(v),
                                     float(scale or 0.0), _p(workspace), workspace.numel(),
                                     _stream(stream)), "moba_attn_routed")
@@ -305,7 +357,12 @@ def moba_attn_routed(q, k, v, block_size, top_k, workspace, scale=None, cu_seqle
 
 def moba_attn_combine(q, k, v, idx, block_size, top_k, workspace, o, lse=None, scale=None,
                       cu_seqlens=None, stream=None):
+    _qkv(q, k, v)
+    _idx(idx, q, top_k)
+    _like(o, q, "o")
+    _expect(lse, _rows(q), torch.float32, "lse")
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _ws(workspace, moba_attn_fwd_workspace_bytes(q, block_size, top_k, cu_seqlens))
     _check(_load().moba_attn_combine(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
                                      float(scale or 0.0), _p(o), _p(lse), _p(workspace),
                                      workspace.numel(), _stream(stream)), "moba_attn_combine")
@@ -320,14 +377,12 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
 
     Returns (o, lse) with lse fp32 [..., heads] (None if not requested).
     """
-    _dev(q, k, v, idx)
-    if not (q.shape == k.shape == v.shape) or not (q.dtype == k.dtype == v.dtype):
-        raise MobaError("q, k, v must share shape and dtype")
-    if idx.dtype != torch.int32 or tuple(idx.shape) != _rows(q) + (top_k,):
-        raise MobaError("idx must be int32 [..., heads, top_k]")
+    _qkv(q, k, v)
+    _idx(idx, q, top_k)
     sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
     if out is None:
         out = torch.empty_like(q)
+    _like(out, q, "out")
     lse = torch.empty(_rows(q), dtype=torch.float32, device=q.device) if return_lse else None
     workspace = _workspace(q, block_size, top_k, cu_seqlens, workspace)
     rc = _load().moba_attn_fwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
@@ -384,10 +439,12 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = out
-    _dev(dq, dk, dv)
+    for g, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _like(g, q, n)
+    need = moba_attn_bwd_workspace_bytes(q, block_size, top_k, cu_seqlens)
     if workspace is None:
-        need = moba_attn_bwd_workspace_bytes(q, block_size, top_k, cu_seqlens)
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _ws(workspace, need)
     rc = _load().moba_attn_bwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
                                float(scale or 0.0), _p(o), _p(lse), _p(dout), _p(dq),
                                _p(dk), _p(dv), _p(workspace), workspace.numel(),

@@ -368,3 +368,36 @@ def test_full_size_sampled(name):
     go = _np(o).reshape(-1, s.head_dim)[rows]
     gl = _np(lse).reshape(-1)[rows]
     _check_o(go[same], gl[same], ro[same], rl[same], "bf16", rows=True, what=f"{name} full")
+
+
+def test_binding_rejects_wrong_buffers():
+    """Wrong-sized or wrong-typed buffers raise MobaError before any launch."""
+    m = moba()
+    T, H, d, B, K = 512, 2, 64, 64, 3
+    q = torch.zeros(T, H, d, dtype=torch.bfloat16, device=DEV)
+    cu = [0, T]
+    nb = m.moba_total_blocks(q, B, cu)
+    cent = torch.zeros(nb, H, d, dtype=torch.float32, device=DEV)
+    idx = torch.zeros(T, H, K, dtype=torch.int32, device=DEV)
+    need = m.moba_attn_fwd_workspace_bytes(q, B, K, cu)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=DEV)
+    bad = [
+        lambda: m.moba_centroids(q, B, cu_seqlens=cu, out=cent[:-1]),
+        lambda: m.moba_centroids(q, B, cu_seqlens=cu, out=cent.double()),
+        lambda: m.moba_route_topk(q, cent[:, :1], B, K, cu_seqlens=cu),
+        lambda: m.moba_route_topk(q, cent, B, K, cu_seqlens=cu, out=idx[:, :, :2]),
+        lambda: m.moba_route_topk(q, cent, B, K, cu_seqlens=cu, workspace=ws[:8]),
+        lambda: m.moba_attn_fwd(q, q, q, idx.long(), B, K, cu_seqlens=cu),
+        lambda: m.moba_attn_fwd(q, q[:-1], q[:-1], idx, B, K, cu_seqlens=cu),
+        lambda: m.moba_attn_fwd(q, q, q, idx, B, K, cu_seqlens=cu, out=q.float()),
+        lambda: m.moba_attn_fwd(q, q, q, idx, B, K, cu_seqlens=cu, workspace=ws[: need - 1]),
+        lambda: m.moba_attn_index(idx[1:], q, B, K, ws, cu_seqlens=cu),
+        lambda: m.moba_attn_combine(q, q, q, idx, B, K, ws, q[:-1], cu_seqlens=cu),
+        lambda: m.moba_key_conv(q, torch.zeros(H, d, 3, device=DEV), B, cu_seqlens=cu,
+                                out=q),
+    ]
+    for i, f in enumerate(bad):
+        with pytest.raises(m.MobaError):
+            f()
+            pytest.fail(f"case {i} did not raise")
+    torch.cuda.synchronize()
