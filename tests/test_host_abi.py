@@ -144,3 +144,45 @@ def test_python_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 64, 1, 64, dtype=torch.bfloat16)
     with pytest.raises(moba.MobaError):
         moba.moba_centroids(q, 64)
+
+
+C_CALLER = r"""
+#include "moba.h"
+#include <stdio.h>
+int main(void) {
+    int32_t cu[3] = {0, 1000, 1300};
+    moba_shape sh = {0};
+    sh.batch = 1; sh.seq = 1300; sh.heads = 2; sh.head_dim = 64;
+    sh.cu_seqlens = cu; sh.num_seqs = 2; sh.block_size = 128; sh.top_k = 4;
+    sh.dtype = MOBA_BF16;
+    /* a null q is refused on the host, before any device work */
+    moba_status st = moba_centroids(&sh, NULL, (float *)256, NULL);
+    printf("%d %lld %d %s\n", moba_abi_version(), (long long)moba_total_blocks(&sh),
+           moba_attn_fwd_workspace_bytes(&sh) > 0, moba_status_string(st));
+    return 0;
+}
+"""
+
+
+def test_header_compiles_as_c_and_links(lib, tmp_path):
+    """A plain C99 program includes moba.h, links the library and calls the
+    host-only entry points (no torch, no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    src = tmp_path / "caller.c"
+    src.write_text(C_CALLER)
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(moba.library_path())
+    libname = os.path.basename(moba.library_path())[3:-3]
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror=implicit-function-declaration",
+                    "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"),
+                    "-I", "/opt/rocm/include", str(src), "-L", libdir, f"-l{libname}",
+                    f"-Wl,-rpath,{libdir}", "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split(None, 3)
+    assert int(out[0]) == lib.moba_abi_version()
+    assert int(out[1]) == 11                  # ceil(1000/128) + ceil(300/128)
+    assert out[2] == "1"
+    assert out[3].strip() == lib.moba_status_string(INVALID).decode()
