@@ -59,3 +59,52 @@ def test_forward_and_backward_replay_from_a_graph():
         got = [idx, o, state["lse"], *grads]
         for a, b, name in zip(got, ref, ("idx", "o", "lse", "dq", "dk", "dv")):
             assert torch.equal(a, b), f"replay {rep}: {name} differs from the eager run"
+
+
+def test_concurrent_streams_match_sequential():
+    """Calls keep no state between them: two problems run at the same time on
+    two streams, each with its own workspace, give the sequential results
+    bitwise (forward and backward)."""
+    import block_sparse_long_key_amd as moba
+    probs = []
+    for name, n in (("H", 4096), ("C5", 6144)):      # C5: 4 sequences, d = 128
+        s = workloads.spec(name).scaled(n, "-streams")
+        x = workloads.make(s)
+        q, k, v = (x[t].to(DEV) for t in ("q", "k", "v"))
+        cu = None
+        if s.seqlens is not None:
+            cu = [0]
+            for ln in s.seqlens:
+                cu.append(cu[-1] + ln)
+        do = workloads.grad_output(s).to(DEV)
+        B, K = s.block_size, s.top_k
+        wsf = torch.empty(max(moba.moba_attn_fwd_workspace_bytes(q, B, K, cu),
+                              moba.moba_route_topk_workspace_bytes(q, B, K, cu), 256),
+                          dtype=torch.uint8, device=DEV)
+        wsb = torch.empty(moba.moba_attn_bwd_workspace_bytes(q, B, K, cu), dtype=torch.uint8, device=DEV)
+        probs.append(dict(q=q, k=k, v=v, do=do, B=B, K=K, cu=cu, wsf=wsf, wsb=wsb))
+
+    def run(p):
+        cent = moba.moba_centroids(p["k"], p["B"], cu_seqlens=p["cu"])
+        idx = moba.moba_route_topk(p["q"], cent, p["B"], p["K"], cu_seqlens=p["cu"], workspace=p["wsf"])
+        o, lse = moba.moba_attn_fwd(p["q"], p["k"], p["v"], idx, p["B"], p["K"], cu_seqlens=p["cu"],
+                                    workspace=p["wsf"])
+        g = moba.moba_attn_bwd(p["q"], p["k"], p["v"], idx, o, lse, p["do"], p["B"], p["K"],
+                               cu_seqlens=p["cu"], workspace=p["wsb"])
+        return (idx, o, lse, *g)
+
+    ref = [run(p) for p in probs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in probs]
+    for rep in range(3):
+        outs = [None] * len(probs)
+        for i, (p, st) in enumerate(zip(probs, streams)):
+            st.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(st):
+                outs[i] = run(p)
+        for st in streams:
+            torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        for i in range(len(probs)):
+            for a, b, name in zip(outs[i], ref[i], ("idx", "o", "lse", "dq", "dk", "dv")):
+                assert torch.equal(a, b), f"problem {i} replay {rep}: {name} differs"
