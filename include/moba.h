@@ -45,7 +45,8 @@
  * "Configurazione MoBA"); top_k 1..32; conv width 1..8; dtype bf16 (fast
  * path) or fp32 (correctness path; block_size * head_dim <= 8192 counting
  * blocks above 128 as 128, block_size <= 256); num_seqs <= MOBA_MAX_SEQS
- * (varlen); tokens * heads < 2^27 per call.
+ * (varlen); at most 16384 blocks per sequence; tokens * heads < 2^27 per
+ * call.
  * Blocks of 256 / 512 keys: routing (centroids, scores, top-k) works on the
  * blocks as given; the attention calls attend a selected block as its 2 / 4
  * sub-blocks of 128 keys (the same key set, so the same result), with the

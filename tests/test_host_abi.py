@@ -87,6 +87,9 @@ def test_large_blocks_attend_as_128_key_blocks(lib):
     (dict(heads=0), INVALID), (dict(batch=65), UNSUPPORTED),
     (dict(dtype=0, d=128, B=128), UNSUPPORTED),
     (dict(cu=[0, 10, 5]), INVALID), (dict(cu=[1, 10]), INVALID),
+    (dict(cu=list(range(0, 660, 10))), UNSUPPORTED),        # 65 sequences
+    (dict(seq=1 << 26, heads=2), UNSUPPORTED),              # tokens x heads = 2^27
+    (dict(seq=16384 * 64 + 1, B=64), UNSUPPORTED),          # 16385 blocks in a sequence
 ])
 def test_bad_shapes_rejected_on_host(lib, kw, code):
     sh = _shape(**kw)
@@ -95,6 +98,16 @@ def test_bad_shapes_rejected_on_host(lib, kw, code):
     assert rc == code
     assert lib.moba_total_blocks(ctypes.byref(sh)) == -1
     assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def test_largest_accepted_shapes(lib):
+    # 64 sequences (the most a varlen batch may hold), 16384 blocks in one
+    # sequence and 63 * 2^21 < 2^27 token-heads are accepted on the host
+    sh = _shape(cu=list(range(0, 650, 10)), B=64)
+    assert lib.moba_total_blocks(ctypes.byref(sh)) == 64
+    sh = _shape(seq=16384 * 128, heads=63, B=128, K=8)
+    assert lib.moba_total_blocks(ctypes.byref(sh)) == 16384
+    assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) > 0
 
 
 def test_route_workspace(lib):

@@ -280,6 +280,7 @@ def test_route_long_scan_every_row(seq, B, K):
     ([640], 2, 64, 64, 32, "f32"),            # fp32, k > blocks
     ([1000], 1, 128, 64, 5, "f32"),           # fp32, d = 128, ragged
     ([4096], 1, 64, 64, 32, "bf16"),          # maximum k
+    ([(53 * i) % 257 for i in range(64)], 2, 64, 64, 4, "bf16"),  # 64 sequences (the maximum), ragged, one empty
 ])
 def test_edge_cases(seqlens, H, d, B, K, dtype):
     print(f"[edge {seqlens} H{H} d{d} B{B} K{K} {dtype}]", flush=True)
