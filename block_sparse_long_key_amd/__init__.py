@@ -11,7 +11,8 @@ the calls raise -- there is no CPU fallback.
 Names follow the C ABI: ``moba_key_conv``, ``moba_centroids``,
 ``moba_route_topk``, ``moba_attn_fwd`` (plus its three stages
 ``moba_attn_index``, ``moba_attn_routed``, ``moba_attn_combine``), the
-convenience ``moba_fwd`` that chains them, ``moba_attn_bwd`` and
+convenience ``moba_fwd`` that chains them (``fwd``: the same, returning
+(o, lse, idx)), ``moba_attn_bwd`` and
 ``moba_key_conv_bwd``, and ``moba_attention``: the whole layer as a
 differentiable op (torch autograd glue around the same calls).
 
@@ -29,7 +30,7 @@ import torch
 
 __all__ = [
     "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
-    "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd",
+    "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd", "fwd",
     "moba_attn_fwd_workspace_bytes", "moba_route_topk_workspace_bytes", "moba_total_blocks",
     "library_path",
     "moba_attn_bwd", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
@@ -413,6 +414,15 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
     idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens, workspace=workspace)
     o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
     return o, lse, idx, kk
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, top_k: int,
+        conv_w: Optional[torch.Tensor] = None, conv_mode: str = "plain", cu_seqlens=None,
+        scale: Optional[float] = None):
+    """``moba_fwd`` without the convolved keys: returns (o, lse, idx)."""
+    o, lse, idx, _ = moba_fwd(q, k, v, block_size, top_k, conv_w=conv_w, conv_mode=conv_mode,
+                              cu_seqlens=cu_seqlens, scale=scale)
+    return o, lse, idx
 
 
 def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,

@@ -164,9 +164,13 @@ def test_deterministic_bitwise(cases):
     q, k, v, w, cus = _gpu_inputs(s, x)
     a = moba().moba_fwd(q, k, v, s.block_size, s.top_k)
     b = moba().moba_fwd(q, k, v, s.block_size, s.top_k)
+    c = moba().fwd(q, k, v, s.block_size, s.top_k)         # (o, lse, idx)
     torch.cuda.synchronize()
     for x1, x2 in zip(a, b):
         assert torch.equal(x1, x2)
+    assert len(c) == 3
+    for x1, x3 in zip(a, c):
+        assert torch.equal(x1, x3)
 
 
 # ------------------------------------------------------------ edge cases --
