@@ -674,7 +674,7 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
 {
     constexpr int RPW = 64 / KMAX;               // rows per pass
     const int H = st.H, K = st.K;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int grp = lane / KMAX, p = lane % KMAX;
     {
         uint64_t cm = __ballot(s0 != kPending && s0 != kHint && s0 <= -2);
@@ -745,7 +745,7 @@ __device__ __forceinline__ uint64_t fix_hint_rows(const SegTable& st, const uint
     constexpr int FP = 2 * KMAX;                 // lanes per row (F <= FP)
     constexpr int RPW = 64 / FP;                 // rows per pass
     const int H = st.H, K = st.K, F = 2 * K - 4;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const int grp = lane / FP, p = lane % FP;
     uint64_t failed = 0;
     uint64_t cm = __ballot(s0 == kHint);
@@ -821,6 +821,14 @@ __device__ __forceinline__ uint64_t fix_hint_rows(const SegTable& st, const uint
     return failed;
 }
 
+// orders one wave's LDS writes before its later reads by other lanes
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Marked rows (slot 0 = kPending), rare: lanes score past blocks j = lane,
 // lane + 64, ... and keep their best KMAX by (score desc, index asc) in a
 // sorted list; K-1 rounds of a wave-wide argmax over the list heads then
@@ -832,7 +840,7 @@ __device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16
                                                 uint64_t more)
 {
     const int H = st.H, K = st.K;
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     {
         // rows marked by the MFMA kernel, and hint rows whose bound failed
         uint64_t fm = __ballot(s0 == kPending) | more;
@@ -842,7 +850,7 @@ __device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16
             const int tq = i * BLK + r0 + src;
             const uint16_t* qp = q + ((size_t)(st.cu[s] + tq) * H + h) * D;
             for (int c = lane; c < D; c += 64) qstage[c] = bf16_to_f32(qp[c]);
-            __syncthreads();
+            wave_lds_sync();
             double sc[KMAX];
             int jx[KMAX];
 #pragma unroll
@@ -892,20 +900,22 @@ __device__ __forceinline__ void fix_marked_rows(const SegTable& st, const uint16
                     if (p < K - 1) out[p] = rsel[p];
                 out[K - 1] = i;
             }
-            __syncthreads();
+            wave_lds_sync();
         }
     }
 }
 
-// One wave per (query block, head), in the MFMA kernel's order: one look at
-// its rows, then the candidate rows and the (rare) marked rows of each
-// 64-row chunk.
+// One workgroup per (query block, head), in the MFMA kernel's order, and one
+// wave per 64-row chunk of the block: one look at its rows, then its
+// candidate, hint and (rare) marked rows.  The waves share nothing (each has
+// its own LDS staging row) and never wait for one another.
 template <int D, int BLK, int KMAX>
-__global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_fix_kernel(SegTable st, const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(BLK) void route_fix_kernel(SegTable st, const uint16_t* __restrict__ q,
                                                                       const float* __restrict__ cent,
                                                                       int32_t* __restrict__ idx)
 {
-    __shared__ __align__(16) float qstage[D];
+    // one wave per 64-row chunk of the query block; the waves share nothing
+    __shared__ __align__(16) float qstage[BLK / 64][D];
     int g, h;
     route_item(st, g, h);
     const int H = st.H, K = st.K;
@@ -913,16 +923,16 @@ __global__ __launch_bounds__(64, (KMAX > 16 ? 2 : 4)) void route_fix_kernel(SegT
     const int i = g - st.boff[s];
     if (K == 1 || i <= K - 1) return;                  // no scoring happened here
     const int L = seq_len(st, s);
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     const float* cbase = cent + (size_t)st.boff[s] * H * D + (size_t)h * D;
-    for (int r0 = 0; r0 < BLK; r0 += 64) {
-        const int tl = i * BLK + r0 + lane;
-        int32_t s0 = 0;
-        if (r0 + lane < BLK && tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
-        fix_candidate_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
-        const uint64_t failed = fix_hint_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
-        fix_marked_rows<D, BLK, KMAX>(st, q, cbase, idx, qstage, s, i, h, r0, s0, failed);
-    }
+    const int wave = threadIdx.x >> 6;
+    const int r0 = 64 * wave;
+    const int tl = i * BLK + r0 + lane;
+    int32_t s0 = 0;
+    if (tl < L) s0 = idx[((size_t)(st.cu[s] + tl) * H + h) * K];
+    fix_candidate_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
+    const uint64_t failed = fix_hint_rows<D, BLK, KMAX>(st, q, cbase, idx, s, i, h, r0, s0);
+    fix_marked_rows<D, BLK, KMAX>(st, q, cbase, idx, qstage[wave], s, i, h, r0, s0, failed);
 }
 
 template <typename T, int D>
@@ -954,7 +964,7 @@ hipError_t launch_mfma_k(const Launch& L, const uint16_t* q, const float* cent, 
                        w.lo, w.n2, idx);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((route_fix_kernel<D, BLK, KMAX>), grid, dim3(64), 0, L.stream, L.st, q, cent, idx);
+    hipLaunchKernelGGL((route_fix_kernel<D, BLK, KMAX>), grid, dim3(BLK), 0, L.stream, L.st, q, cent, idx);
     return hipGetLastError();
 }
 
