@@ -96,7 +96,9 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     }
 
     double sum[kVec] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
+    // (8 tokens in flight: plain conv / pooling 4-14 % faster than 4; the
+    // SiLU mode is VALU-bound and keeps 4)
+#pragma unroll (MODE == 1 ? 4 : 8)
     for (int tl = a; tl < b; ++tl) {
         const size_t row = (size_t)(t0 + tl) * HD + ch;
         float x[4];
@@ -113,7 +115,13 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
                 for (int l = kMaxW - 1; l >= 0; --l)
                     if (l < W) acc = __builtin_fmaf(wr[v][l], win[v][l], acc);
                 float r = acc;
-                if constexpr (MODE == 1) r = x[v] + acc / (1.0f + expf(-acc));
+                // SiLU(acc) = acc / (1 + e^-acc) on the hardware exp2 and
+                // reciprocal (a few ulp in fp32; the accurate expf and
+                // IEEE quotient made this mode VALU-bound, 1.5x slower).
+                // Below acc = -87 the reciprocal's result is denormal and the
+                // term (|.| < 1e-36) may come out as zero.
+                if constexpr (MODE == 1)
+                    r = x[v] + acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * 1.4426950408889634f));
                 y[v] = IO<T>::round(r);
             }
             Vec4<T>::store(kout + row, y);

@@ -100,7 +100,9 @@ typedef struct {
  *      channel (h, c) (l = 0 is the current token).  Zero before each
  *      sequence start.
  *   The tap sum is fp32 fmaf from the oldest tap to the newest, started at
- *   +0; MOBA_CONV_SILU_RESIDUAL then adds k_t + conv/(1+exp(-conv)) in fp32.
+ *   +0; MOBA_CONV_SILU_RESIDUAL then adds k_t + conv/(1+exp(-conv)) in fp32
+ *   on the hardware exp2 and reciprocal (a few ulp; a SiLU term below 1e-36
+ *   in magnitude, conv < -87, may be taken as zero).
  *   k_out (same layout and dtype as k) is rounded to the dtype (bf16:
  *   round-to-nearest-even).  k_out must not alias k.
  *   If `cent` is not NULL, the block centroids of k_out are also written to
