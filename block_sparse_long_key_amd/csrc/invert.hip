@@ -70,6 +70,30 @@ __global__ __launch_bounds__(kThreads) void inv_count_kernel(SegTable st, const 
     const int nent = (tl1 - tl0) * K;
     const int32_t* src = idx + ((size_t)(t0 + tl0) * H + h) * K;
     const Div div(K, B);
+    if ((K & 3) == 0) {
+        // k a multiple of 4: four slots of one row per 16-byte load (a
+        // row's K words start 16-byte aligned), kBatch / 4 loads in flight
+        constexpr int QB = kBatch / 4;
+        const int nq4 = nent >> 2;
+        for (int q0 = threadIdx.x; q0 < nq4; q0 += kThreads * QB) {
+            int4 jv[QB];
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int e = 4 * (q0 + u * kThreads);
+                const int r = div.row(e), slot = e - r * K;
+                jv[u] = e < nent ? *(const int4*)(src + (size_t)r * H * K + slot) : make_int4(-1, -1, -1, -1);
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int e = 4 * (q0 + u * kThreads);
+                const int i = div.block(tl0 + div.row(e));
+                if (jv[u].x >= 0 && jv[u].x < i) atomicAdd(&hist[jv[u].x], 1);
+                if (jv[u].y >= 0 && jv[u].y < i) atomicAdd(&hist[jv[u].y], 1);
+                if (jv[u].z >= 0 && jv[u].z < i) atomicAdd(&hist[jv[u].z], 1);
+                if (jv[u].w >= 0 && jv[u].w < i) atomicAdd(&hist[jv[u].w], 1);
+            }
+        }
+    } else
     // kBatch loads in flight per thread before their LDS updates
     for (int e0 = threadIdx.x; e0 < nent; e0 += kThreads * kBatch) {
         int jv[kBatch];
@@ -239,6 +263,44 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
         for (int j = threadIdx.x; j < ib1; j += kThreads) cur[j] = pos[j];
     }
     __syncthreads();
+    if (!DET && (K & 3) == 0) {
+        // k a multiple of 4: four slots of one row per 16-byte load and per
+        // 16-byte reverse-map store
+        constexpr int QB = kBatch / 4;
+        const int nq4 = e_hi >> 2;
+        for (int q0 = threadIdx.x; q0 < nq4; q0 += kThreads * QB) {
+            int4 jv[QB];
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int e = 4 * (q0 + u * kThreads);
+                const int r = div.row(e), slot = e - r * K;
+                jv[u] = e < e_hi ? *(const int4*)(src + (size_t)r * H * K + slot) : make_int4(-1, -1, -1, -1);
+            }
+            int4 pv[QB];
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int e = 4 * (q0 + u * kThreads);
+                const int i = div.block(tl0 + div.row(e));
+                pv[u].x = (jv[u].x >= 0 && jv[u].x < i) ? atomicAdd(&wc[jv[u].x], 1) : -1;
+                pv[u].y = (jv[u].y >= 0 && jv[u].y < i) ? atomicAdd(&wc[jv[u].y], 1) : -1;
+                pv[u].z = (jv[u].z >= 0 && jv[u].z < i) ? atomicAdd(&wc[jv[u].z], 1) : -1;
+                pv[u].w = (jv[u].w >= 0 && jv[u].w < i) ? atomicAdd(&wc[jv[u].w], 1) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < QB; ++u) {
+                const int e = 4 * (q0 + u * kThreads);
+                if (e >= e_hi) continue;
+                const int r = div.row(e), slot = e - r * K;
+                const uint32_t tok = (uint32_t)(t0 + tl0 + r) << 5;
+                if (pv[u].x >= 0) ent[pv[u].x] = tok | (uint32_t)slot;
+                if (pv[u].y >= 0) ent[pv[u].y] = tok | (uint32_t)(slot + 1);
+                if (pv[u].z >= 0) ent[pv[u].z] = tok | (uint32_t)(slot + 2);
+                if (pv[u].w >= 0) ent[pv[u].w] = tok | (uint32_t)(slot + 3);
+                *(int4*)(rv + e) = pv[u];
+            }
+        }
+        return;
+    }
     for (int e0 = first; e0 < e_hi; e0 += STEP * kBatch) {
         int jv[kBatch];
 #pragma unroll
