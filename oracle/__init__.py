@@ -57,6 +57,8 @@ def _load():
         lib.moba_oracle_total_blocks.argtypes = [_P, _I, _I]
         lib.moba_oracle_route_rows.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P]
         lib.moba_oracle_attend_rows.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _I, _P, _P]
+        lib.moba_oracle_route_scores.argtypes = [_P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P]
+        lib.moba_oracle_route_scores.restype = _I
         lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
                                                _P, _P, _P, _P, _P, _I]
         lib.moba_oracle_attend_bwd.restype = _I
@@ -207,6 +209,25 @@ def route_rows(q, cent, B: int, K: int, cu, rows):
                                         _ptr(ga), _ptr(gb), _ptr(ex))
     assert rc == 0
     return idx[rows], ga[rows], gb[rows], ex[rows].astype(bool)
+
+
+def route_scores(q, cent, B: int, cu, rows) -> np.ndarray:
+    """fp64 router scores of the listed rows against every past block.
+
+    Returns f64 [nrows, nmax] (nmax = the longest sequence's block count);
+    entry j of a row is NaN for j >= its own block.
+    """
+    q = _f32(q)
+    cent = np.ascontiguousarray(cent, dtype=np.float32)
+    T, H, d = q.shape
+    c = _cu(cu)
+    nmax = max(1, max((int(c[s + 1] - c[s]) + B - 1) // B for s in range(len(c) - 1)))
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    out = np.empty((len(rows), nmax), dtype=np.float64)
+    rc = _load().moba_oracle_route_scores(_ptr(q), _ptr(cent), H, d, B, _ptr(c), len(c) - 1,
+                                          _ptr(rows), len(rows), nmax, _ptr(out))
+    assert rc == 0
+    return out
 
 
 def attend_rows(q, k, v, idx, B: int, K: int, cu, rows, scale: float = 0.0):

@@ -263,21 +263,29 @@ static int cmp_int(const void *a, const void *b)
     return (x > y) - (x < y);
 }
 
-/* one query: token t_local `tl` of sequence s, head h; sc/order scratch of
- * n doubles/ints, row scratch of K ints */
-static void route_one(route_ctx *c, int s, int h, int tl, double *sc, int *order, int *row)
+/* router scores of one query (token t_local `tl` of sequence s, head h)
+ * against its i past blocks, written to sc[0..i-1]; returns i */
+static int score_past(const route_ctx *c, int s, int h, int tl, double *sc)
 {
-    int t0 = c->cu[s];
-    size_t t = (size_t)(t0 + tl);
+    size_t t = (size_t)(c->cu[s] + tl);
     int i = tl / c->B;
     const float *qv = c->q + (t * c->H + h) * c->d;
-    /* scores of the past blocks */
     for (int j = 0; j < i; ++j) {
         const float *cv = c->cent + ((size_t)(c->boff[s] + j) * c->H + h) * c->d;
         double acc = 0.0;
         for (int ch = 0; ch < c->d; ++ch) acc = acc + (double)qv[ch] * (double)cv[ch];
         sc[j] = acc;
     }
+    return i;
+}
+
+/* one query: token t_local `tl` of sequence s, head h; sc/order scratch of
+ * n doubles/ints, row scratch of K ints */
+static void route_one(route_ctx *c, int s, int h, int tl, double *sc, int *order, int *row)
+{
+    int t0 = c->cu[s];
+    size_t t = (size_t)(t0 + tl);
+    int i = score_past(c, s, h, tl, sc);
     /* selection sort of the first m+1 places in the total order */
     int m = (c->K - 1) < i ? (c->K - 1) : i;
     int need = (m + 1) < i ? (m + 1) : i;
@@ -456,6 +464,31 @@ int moba_oracle_route_rows(const float *q, const float *cent, int H, int d, int 
     free(sc);
     free(order);
     free(row);
+    free(boff);
+    return 0;
+}
+
+/* Step 3 alone for the listed rows: the fp64 router score of every past
+ * block, scores[r * nmax + j] for j < i (the row's own block index), NaN
+ * for j >= i.  nmax must be at least the longest sequence's block count.
+ * Lets a test check that a selection differing from this oracle's is still
+ * a valid tolerant top-(k-1) of the same scores. */
+int moba_oracle_route_scores(const float *q, const float *cent, int H, int d, int B,
+                             const int *cu, int nseq, const long long *rows, int nrows,
+                             int nmax, double *scores)
+{
+    if (B < 1) return 1;
+    int *boff = block_offsets(cu, nseq, B);
+    route_ctx c = {q, cent, NULL, NULL, NULL, NULL, cu, boff, H, d, B, 1};
+    for (int s = 0; s < nseq; ++s)
+        if (ceil_div(cu[s + 1] - cu[s], B) > nmax) { free(boff); return 2; }
+    for (int r = 0; r < nrows; ++r) {
+        int t = (int)(rows[r] / H), h = (int)(rows[r] % H);
+        int s = seq_of_token(cu, nseq, t);
+        double *out = scores + (size_t)r * (size_t)nmax;
+        int i = score_past(&c, s, h, t - cu[s], out);
+        for (int j = i; j < nmax; ++j) out[j] = NAN;
+    }
     free(boff);
     return 0;
 }

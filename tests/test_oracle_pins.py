@@ -226,6 +226,66 @@ def test_route_ties_go_to_lower_index():
     assert idx[6, 0].tolist() == [0, 1, 3]
 
 
+def _route_one_query(scores, K):
+    """The oracle's routing of one query whose past-block scores are exactly
+    ``scores`` (B = 1, q = e_0 and centroid j = (scores[j], 0): every score is
+    one exact product)."""
+    n = len(scores)
+    T = n + 1
+    q = np.zeros((T, 1, 2), np.float32)
+    q[:, 0, 0] = 1.0
+    cent = np.zeros((T, 1, 2), np.float32)
+    cent[:n, 0, 0] = np.asarray(scores, np.float32)
+    assert np.array_equal(cent[:n, 0, 0].astype(np.float64), np.asarray(scores, np.float64))
+    idx, ga, gb, ex = oracle.route(q, cent, 1, K, [0, T])
+    return idx[n, 0].tolist(), float(ga[n, 0]), float(gb[n, 0]), bool(ex[n, 0])
+
+
+# (k-1)-th best a = 100000 (or -100000) against the k-th best b: the near-tie
+# record is |a - b| <= 1e-5 max(|a|, |b|) on those two ranks only
+@pytest.mark.parametrize("a,b,exempt", [
+    (100000.0, 99999.5, True),        # 0.5e-5 relative
+    (100000.0, 99999.125, True),      # 0.875e-5
+    (100000.0, 99998.875, False),     # 1.125e-5
+    (100000.0, 99998.0, False),       # 2e-5
+    (-100000.0, -100000.5, True),     # negative scores, 0.5e-5 of |b|
+    (-100000.0, -100002.0, False),    # 2e-5
+    (3.0, 3.0, True),                 # an exact tie
+])
+def test_route_near_tie_gap_threshold(a, b, exempt):
+    K = 4                              # k-1 = 3 routed slots: ranks 3 and 4
+    # past scores in scrambled block order: two clear winners, a, b, a clear loser
+    top = abs(a) * 3
+    scores = [b, top, a - 50000 if a > 0 else a - 50000, top * 2, a]
+    order = sorted(range(5), key=lambda j: (-scores[j], j))
+    assert [scores[j] for j in order[2:4]] == [a, b]
+    row, ga, gb, ex = _route_one_query(scores, K)
+    assert row == sorted(order[:3]) + [5]
+    assert ga == a and gb == b
+    assert ex == exempt
+
+
+def test_route_near_tie_uses_ranks_k_minus_1_and_k():
+    """Only the gap between the (k-1)-th and k-th best past scores counts:
+    a near-equal pair at ranks (k-2, k-1) or (k, k+1) is no near-tie."""
+    K = 4
+    # ranks: 1st 300000, 2nd 100000.5, 3rd (k-1) 100000, 4th (k) 90000, 5th 89999.5
+    scores = [89999.5, 100000.0, 300000.0, 90000.0, 100000.5]
+    row, ga, gb, ex = _route_one_query(scores, K)
+    assert row == [1, 2, 4, 5]
+    assert (ga, gb) == (100000.0, 90000.0)
+    assert not ex
+    # moving the near-equal pair onto ranks (k-1, k) makes it one
+    scores = [89999.5, 100000.5, 300000.0, 100000.0, 200000.0]
+    row, ga, gb, ex = _route_one_query(scores, K)
+    assert row == [1, 2, 4, 5]
+    assert (ga, gb) == (100000.5, 100000.0)
+    assert ex
+    # and with k = 2 the pair is the best and second-best score (2.2e-6 apart)
+    row, ga, gb, ex = _route_one_query([7.0, 7.0 + 2.0 ** -16, 1.0], 2)
+    assert row == [1, 3] and (ga, gb) == (7.0 + 2.0 ** -16, 7.0) and ex
+
+
 def test_route_top_k_at_least_blocks_selects_all_past():
     H, d, B = 1, 4, 4
     T = 32
