@@ -23,6 +23,7 @@ int tensor of num_seqs + 1 offsets).
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
 from typing import Optional, Sequence, Tuple
 
@@ -162,6 +163,22 @@ def _stream(stream=None) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Runs a call whose ``stream`` (keyword) is given with that stream as
+    torch's current one, so the outputs and workspaces the call allocates
+    belong to the stream its kernels run on: torch's caching allocator then
+    hands a dropped workspace only to later work on that same stream, never
+    to another stream while the kernels may still read it.  Outputs are
+    ready on ``stream``; another stream must wait for it before using them."""
+    @functools.wraps(fn)
+    def call(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kw)
+    return call
+
+
 def _p(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -232,6 +249,7 @@ def moba_attn_bwd_workspace_bytes(q: torch.Tensor, block_size: int, top_k: int,
     return int(_load().moba_attn_bwd_workspace_bytes(ctypes.byref(sh)))
 
 
+@_on_stream
 def moba_key_conv(k: torch.Tensor, w: torch.Tensor, block_size: int,
                   mode: str = "plain", cu_seqlens=None, with_centroids: bool = False,
                   out: Optional[torch.Tensor] = None, cent: Optional[torch.Tensor] = None,
@@ -267,6 +285,7 @@ def moba_key_conv_bwd_workspace_bytes(k: torch.Tensor, block_size: int, width: i
     return int(_load().moba_key_conv_bwd_workspace_bytes(ctypes.byref(sh), int(width)))
 
 
+@_on_stream
 def moba_key_conv_bwd(k: torch.Tensor, w: torch.Tensor, dk_out: torch.Tensor, block_size: int,
                       mode: str = "plain", cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
                       stream=None):
@@ -291,6 +310,7 @@ def moba_key_conv_bwd(k: torch.Tensor, w: torch.Tensor, dk_out: torch.Tensor, bl
     return dk, dw
 
 
+@_on_stream
 def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,
                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Block means of k: fp32 [total_blocks, heads, head_dim]."""
@@ -305,6 +325,7 @@ def moba_centroids(k: torch.Tensor, block_size: int, cu_seqlens=None,
     return out
 
 
+@_on_stream
 def moba_route_topk(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k: int,
                     cu_seqlens=None, out: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
@@ -337,6 +358,7 @@ def _workspace(q, block_size, top_k, cu_seqlens, workspace):
     return workspace
 
 
+@_on_stream
 def moba_attn_index(idx, q, block_size, top_k, workspace, cu_seqlens=None, stream=None):
     _dev(q)
     _idx(idx, q, top_k)
@@ -346,6 +368,7 @@ def moba_attn_index(idx, q, block_size, top_k, workspace, cu_seqlens=None, strea
                                    workspace.numel(), _stream(stream)), "moba_attn_index")
 
 
+@_on_stream
 def moba_attn_routed(q, k, v, block_size, top_k, workspace, scale=None, cu_seqlens=None,
                      stream=None):
     _qkv(q, k, v)
@@ -356,6 +379,7 @@ def moba_attn_routed(q, k, v, block_size, top_k, workspace, scale=None, cu_seqle
                                     _stream(stream)), "moba_attn_routed")
 
 
+@_on_stream
 def moba_attn_combine(q, k, v, idx, block_size, top_k, workspace, o, lse=None, scale=None,
                       cu_seqlens=None, stream=None):
     _qkv(q, k, v)
@@ -369,6 +393,7 @@ def moba_attn_combine(q, k, v, idx, block_size, top_k, workspace, o, lse=None, s
                                      workspace.numel(), _stream(stream)), "moba_attn_combine")
 
 
+@_on_stream
 def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                   block_size: int, top_k: int, scale: Optional[float] = None,
                   cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
@@ -393,13 +418,15 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     return out, lse
 
 
+@_on_stream
 def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, top_k: int,
              conv_w: Optional[torch.Tensor] = None, conv_mode: str = "plain",
              cu_seqlens=None, scale: Optional[float] = None,
-             workspace: Optional[torch.Tensor] = None):
+             workspace: Optional[torch.Tensor] = None, stream=None):
     """The whole MoBA forward: [key conv] -> centroids -> route -> attention.
 
-    Returns (o, lse, idx, k_used) where k_used is k' when a conv ran.
+    Returns (o, lse, idx, k_used) where k_used is k' when a conv ran.  With
+    ``stream`` every step runs (and every buffer is allocated) on it.
     """
     if conv_w is not None:
         kk, cent = moba_key_conv(k, conv_w, block_size, conv_mode, cu_seqlens,
@@ -418,13 +445,14 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, top_k: int,
         conv_w: Optional[torch.Tensor] = None, conv_mode: str = "plain", cu_seqlens=None,
-        scale: Optional[float] = None):
+        scale: Optional[float] = None, stream=None):
     """``moba_fwd`` without the convolved keys: returns (o, lse, idx)."""
     o, lse, idx, _ = moba_fwd(q, k, v, block_size, top_k, conv_w=conv_w, conv_mode=conv_mode,
-                              cu_seqlens=cu_seqlens, scale=scale)
+                              cu_seqlens=cu_seqlens, scale=scale, stream=stream)
     return o, lse, idx
 
 
+@_on_stream
 def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                   o: torch.Tensor, lse: torch.Tensor, dout: torch.Tensor,
                   block_size: int, top_k: int, scale: Optional[float] = None,

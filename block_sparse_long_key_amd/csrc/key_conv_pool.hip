@@ -51,6 +51,40 @@ template <> struct Vec4<uint16_t> {
     }
 };
 
+// k + SiLU(acc) rounded to T, equal to the exact formula's result: the
+// fp64 value k + acc / (1 + e^-acc), rounded to fp32 and then to T.
+// bf16: the value comes from the hardware exp2 and reciprocal in fp32;
+// |r - v| <= |silu| (|acc| + 8) 2^-23 + |r| 2^-24 (the exp2 argument's
+// rounding costs |acc| 2^-23 relative, exp2, the reciprocal and the three
+// roundings a few 2^-24 more) and fp32(v) is another |r| 2^-24 away.  When
+// r is farther than twice that from the bf16 rounding midpoint next to it,
+// every value in reach rounds to the same bf16 and the fast result stands;
+// otherwise (about 1 element in 10^3) the fp64 formula decides.  fp32 I/O
+// (the correctness path) always takes the fp64 formula.
+template <typename T>
+__device__ __forceinline__ float silu_residual(float x, float acc)
+{
+    if constexpr (sizeof(T) == 2) {
+        const float silu = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * 1.4426950408889634f));
+        const float r = x + silu;
+        const float rb = IO<T>::round(r);
+        const uint32_t ex = __float_as_uint(r) & 0x7f800000u;
+        // half a bf16 ulp in r's binade
+        const float hu = __uint_as_float(ex - (8u << 23));
+        const float delta = __builtin_fmaf(fabsf(silu), (fabsf(acc) + 8.0f) * 1.1920929e-07f,
+                                           fabsf(r) * 5.9604645e-08f) + 1e-35f;
+        const bool safe = ex > (9u << 23) && hu - fabsf(r - rb) > 2.0f * delta;
+        if (__builtin_expect(safe, 1)) return rb;
+    }
+    const double a = (double)acc;
+    float f = (float)((double)x + a / (1.0 + exp(-a)));
+    // the fp32 rounding stays a step of its own: folded into the dtype
+    // conversion it would become one fp64 -> bf16 rounding, which differs
+    // where the fp32 value is a bf16 tie
+    asm volatile("" : "+v"(f));
+    return IO<T>::round(f);
+}
+
 // CONV: apply the key convolution (MODE 0 plain, 1 SiLU + residual) and
 //       write k'.  POOL: write the block centroid of the (convolved) keys.
 template <typename T, bool CONV, bool POOL, int MODE>
@@ -114,15 +148,10 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
 #pragma unroll
                 for (int l = kMaxW - 1; l >= 0; --l)
                     if (l < W) acc = __builtin_fmaf(wr[v][l], win[v][l], acc);
-                float r = acc;
-                // SiLU(acc) = acc / (1 + e^-acc) on the hardware exp2 and
-                // reciprocal (a few ulp in fp32; the accurate expf and
-                // IEEE quotient made this mode VALU-bound, 1.5x slower).
-                // Below acc = -87 the reciprocal's result is denormal and the
-                // term (|.| < 1e-36) may come out as zero.
                 if constexpr (MODE == 1)
-                    r = x[v] + acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * 1.4426950408889634f));
-                y[v] = IO<T>::round(r);
+                    y[v] = silu_residual<T>(x[v], acc);
+                else
+                    y[v] = IO<T>::round(acc);
             }
             Vec4<T>::store(kout + row, y);
         } else {

@@ -441,7 +441,11 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int p = 0; p < KMAX; ++p) key[sb][p] = -INFINITY;
-    const int LB = 32 - __builtin_clz((unsigned)(i - 1) | 1u);
+    // the last, partial group of 16 writes ids up to the next multiple of
+    // 16 (its blocks j >= i carry the lowest finite score), so the id field
+    // has at least 4 bits: every id then decodes to itself, and a masked
+    // block's id stays >= i wherever keys are turned back into block ids
+    const int LB = max(4, 32 - __builtin_clz((unsigned)(i - 1) | 1u));
     const uint32_t lmask = (1u << LB) - 1u;
     float cmax2 = 0.f;                      // max |c|^2 over the past blocks
 

@@ -100,9 +100,10 @@ typedef struct {
  *      channel (h, c) (l = 0 is the current token).  Zero before each
  *      sequence start.
  *   The tap sum is fp32 fmaf from the oldest tap to the newest, started at
- *   +0; MOBA_CONV_SILU_RESIDUAL then adds k_t + conv/(1+exp(-conv)) in fp32
- *   on the hardware exp2 and reciprocal (a few ulp; a SiLU term below 1e-36
- *   in magnitude, conv < -87, may be taken as zero).
+ *   +0; MOBA_CONV_SILU_RESIDUAL then forms k_t + conv/(1+exp(-conv)) as if
+ *   in fp64 and rounds it to fp32 (bf16 output: a fast fp32 evaluation is
+ *   used wherever its error bound proves the same bf16 result, the fp64
+ *   formula elsewhere).
  *   k_out (same layout and dtype as k) is rounded to the dtype (bf16:
  *   round-to-nearest-even).  k_out must not alias k.
  *   If `cent` is not NULL, the block centroids of k_out are also written to

@@ -228,9 +228,9 @@ def test_attention_sink_long_lists(name):
     cent = m.moba_centroids(k, B, cus)
     idx = m.moba_route_topk(q, cent, B, K, cus)
     torch.cuda.synchronize()
-    from test_parity_gpu import _check_idx, _check_o
-    _check_idx(idx.cpu().numpy().reshape(-1, H, K), ref["idx"], ref["gap_a"], ref["gap_b"],
-               ref["exempt"], name)
+    from test_parity_gpu import _assert_exact, _check_o, _check_sel
+    _assert_exact(_check_sel(idx.cpu().numpy(), ref["idx"], ref["exempt"], x["q"], ref["cent"], B,
+                             K, cu, what=name), name)
     idx_ref = torch.from_numpy(ref["idx"]).reshape(tuple(q.shape[:-1]) + (K,)).to(DEV)
     o, lse = m.moba_attn_fwd(q, k, v, idx_ref, B, K, cu_seqlens=cus)
     do = workloads.grad_output(s)

@@ -108,3 +108,29 @@ def test_concurrent_streams_match_sequential():
         for i in range(len(probs)):
             for a, b, name in zip(outs[i], ref[i], ("idx", "o", "lse", "dq", "dk", "dv")):
                 assert torch.equal(a, b), f"problem {i} replay {rep}: {name} differs"
+
+
+def test_explicit_stream_owns_its_buffers():
+    """A call given ``stream=`` (not inside ``torch.cuda.stream``) allocates
+    its outputs and workspace on that stream: right after it returns, the
+    current stream allocates and overwrites the same amount of memory while
+    the call's kernels may still run, and the results must not change."""
+    import block_sparse_long_key_amd as moba
+    s = workloads.spec("H").scaled(8192, "-explicit-stream")
+    x = workloads.make(s)
+    B, K = s.block_size, s.top_k
+    q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
+    ref = moba.moba_fwd(q, k, v, B, K)
+    torch.cuda.synchronize()
+    need = moba.moba_attn_fwd_workspace_bytes(q, B, K) + 2 * q.numel() * 2
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        got = moba.moba_fwd(q, k, v, B, K, stream=side)
+        junk = torch.empty(need, dtype=torch.uint8, device=DEV)
+        junk.fill_(0xA5)                     # on the current stream, racing the side stream
+        del junk
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for a, b, name in zip(got, ref, ("o", "lse", "idx", "k")):
+            assert torch.equal(a, b), f"rep {rep}: {name} differs with stream="

@@ -7,8 +7,8 @@ its 128-key sub-blocks (the own block split into the sub-blocks before the
 query's own sub-block, plus that sub-block token-causally).  The oracle
 knows nothing of sub-blocks, so agreement checks that re-expression as well
 as the kernels.  Bars are those of the B=128 tests: identical selections
-(near-tie rows must stay valid), O / LSE within the forward bar, dq / dk / dv
-within the backward bar.
+(a differing near-tie row would also have to be valid), O / LSE within the
+forward bar, dq / dk / dv within the backward bar.
 """
 import dataclasses
 
@@ -19,7 +19,7 @@ import torch
 import oracle
 import workloads
 from test_bwd_gpu import _check as _check_grad
-from test_parity_gpu import _check_idx, _check_o
+from test_parity_gpu import _check_o, _verify_forward
 
 pytestmark = pytest.mark.gpu
 
@@ -67,13 +67,12 @@ def test_large_block_forward_and_backward(name):
     q, k, v = (x[n].to(DEV) for n in ("q", "k", "v"))
     w = None if x["conv_w"] is None else x["conv_w"].to(DEV)
     cus = x["cu_seqlens"]
-    # whole forward on the GPU: routing must equal the oracle's
+    # whole forward on the GPU: selection (every row equal to the oracle's)
+    # and output against the oracle on the same selection
     o, lse, idx, kk = m.moba_fwd(q, k, v, B, K, conv_w=w, cu_seqlens=cus)
     torch.cuda.synchronize()
     H, d = s.heads, s.head_dim
-    nd = _check_idx(idx.cpu().numpy().reshape(-1, H, K), ref["idx"], ref["gap_a"],
-                    ref["gap_b"], ref["exempt"], name)
-    print(f"[large {name}] rows differing at near-ties: {nd}", flush=True)
+    _verify_forward(o, lse, idx, ref, x["q"], ref["k_conv"], x["v"], B, K, cu, s.dtype, name)
     # attention on the oracle's selection (so near-tie rows cannot matter)
     idx_ref = torch.from_numpy(ref["idx"]).reshape(tuple(q.shape[:-1]) + (K,)).to(DEV)
     o2, lse2 = m.moba_attn_fwd(q, kk, v, idx_ref, B, K, cu_seqlens=cus)
