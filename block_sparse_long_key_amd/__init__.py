@@ -30,7 +30,8 @@ from typing import Optional, Sequence, Tuple
 import torch
 
 __all__ = [
-    "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_attn_fwd",
+    "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_route_topk_noalloc",
+    "moba_attn_fwd",
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd", "fwd",
     "moba_attn_fwd_workspace_bytes", "moba_route_topk_workspace_bytes", "moba_total_blocks",
     "library_path",
@@ -81,6 +82,7 @@ def _load():
         "moba_key_conv": [SH, P, P, I32, I32, P, P, P],
         "moba_centroids": [SH, P, P, P],
         "moba_route_topk": [SH, P, P, P, P, SZ, P],
+        "moba_route_topk_noalloc": [SH, P, P, P, P],
         "moba_attn_fwd": [SH, P, P, P, P, F32, P, P, P, SZ, P],
         "moba_attn_index": [SH, P, P, SZ, P],
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
@@ -347,6 +349,24 @@ def moba_route_topk(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k:
     _check(_load().moba_route_topk(ctypes.byref(sh), _p(q), _p(cent), _p(out), _p(workspace),
                                    workspace.numel(), _stream(stream)),
            "moba_route_topk")
+    return out
+
+
+@_on_stream
+def moba_route_topk_noalloc(q: torch.Tensor, cent: torch.Tensor, block_size: int, top_k: int,
+                            cu_seqlens=None, out: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """moba_route_topk on the library's fixed per-GPU routing scratch (the C
+    call allocates nothing; pass ``out`` to allocate nothing here either).
+    Calls that overlap on one GPU race on that scratch."""
+    _dev(q, cent)
+    sh, keep = _make_shape(q, block_size, top_k, cu_seqlens)
+    _expect(cent, _cent_shape(q, block_size, cu_seqlens), torch.float32, "cent")
+    if out is None:
+        out = torch.empty(_rows(q) + (top_k,), dtype=torch.int32, device=q.device)
+    _idx(out, q, top_k)
+    _check(_load().moba_route_topk_noalloc(ctypes.byref(sh), _p(q), _p(cent), _p(out),
+                                           _stream(stream)), "moba_route_topk_noalloc")
     return out
 
 

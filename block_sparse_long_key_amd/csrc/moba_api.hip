@@ -295,6 +295,22 @@ moba_status moba_route_topk(const moba_shape* shape, const void* q, const float*
     return hip_status(launch_route(L, q, cent, workspace, idx));
 }
 
+moba_status moba_route_topk_noalloc(const moba_shape* shape, const void* q, const float* cent,
+                                    int32_t* idx, hipStream_t stream)
+{
+    Launch L;
+    moba_status st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
+    if (!ptr_ok(q) || !ptr_ok(cent) || !ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (L.dtype == MOBA_BF16 && route_ws_bytes(L) > (size_t)MOBA_ROUTE_SCRATCH_BYTES)
+        return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    if (L.tokens == 0) return MOBA_OK;
+    void* ws = nullptr;
+    hipError_t e = route_scratch(&ws);
+    if (e != hipSuccess) return MOBA_ERR_HIP;
+    return hip_status(launch_route(L, q, cent, ws, idx));
+}
+
 // the index pass on the (possibly expanded) selection
 hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, char* wsp,
                      const int32_t* idx, bool det = false)

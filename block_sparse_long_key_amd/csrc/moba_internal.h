@@ -163,6 +163,8 @@ struct RouteWs {
 };
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t route_ws_bytes(const Launch& L);
+// address of this device's fixed routing scratch (MOBA_ROUTE_SCRATCH_BYTES)
+hipError_t route_scratch(void** out);
 RouteWs route_ws(const Launch& L, void* workspace);
 // bf16 queries use the workspace; fp32 queries do not read it
 hipError_t launch_route(const Launch& L, const void* q, const float* cent, void* workspace,

@@ -22,6 +22,7 @@
 // one query each) of one head; the centroids of the past blocks stream
 // through LDS in tiles of 32 and are read by all threads as broadcasts.
 // bf16 queries use the MFMA kernel below.
+#include <mutex>
 #include <type_traits>
 
 #include "moba_internal.h"
@@ -1027,6 +1028,40 @@ hipError_t launch_route(const Launch& L, const void* q, const float* cent, void*
     }
     return L.D == 64 ? launch_d<float, 64>(L, q, cent, idx)
                      : launch_d<float, 128>(L, q, cent, idx);
+}
+
+// ------------------------------------------------------------------------
+// The fixed routing scratch of moba_route_topk_noalloc: one copy per GPU,
+// held while the process runs.  Host code never passes `scratch` itself (a
+// host-side stand-in for the device symbol): it asks for the symbol's
+// address on the current device once, and passes that.
+}  // namespace moba
+
+static __device__ __align__(256) char scratch[MOBA_ROUTE_SCRATCH_BYTES];
+
+namespace moba {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t route_scratch(void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 }  // namespace moba

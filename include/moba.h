@@ -176,6 +176,30 @@ moba_status moba_route_topk(const moba_shape *shape, const void *q,
 size_t moba_route_topk_workspace_bytes(const moba_shape *shape);
 
 /*
+ * moba_route_topk_noalloc -- moba_route_topk for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation): the same selection, with the routing
+ * workspace taken from a fixed buffer of MOBA_ROUTE_SCRATCH_BYTES inside
+ * the library (one per GPU, held until the process ends) instead of a
+ * caller's workspace.  It makes no allocation of its own.
+ *   bf16 queries need 4 * head_dim + 4 bytes per (block, head) centroid
+ *   row, so the buffer covers about 129 000 rows at head_dim 64 and 65 000
+ *   at 128 (one 512K-token sequence of 16 heads at B = 128 takes 16 MiB);
+ *   a larger shape (moba_route_topk_workspace_bytes() above
+ *   MOBA_ROUTE_SCRATCH_BYTES) returns MOBA_ERR_WORKSPACE_TOO_SMALL before
+ *   any launch.  fp32 queries do not use the buffer.
+ *   Every call on one GPU uses that GPU's one buffer: calls that may
+ *   overlap on a GPU (several streams, several host threads) race and must
+ *   be ordered by the caller.  Nothing in the buffer needs to start at zero;
+ *   each call rewrites what it reads.  Other arguments and errors as
+ *   moba_route_topk.
+ */
+#define MOBA_ROUTE_SCRATCH_BYTES (32u << 20)
+moba_status moba_route_topk_noalloc(const moba_shape *shape, const void *q,
+                                    const float *cent, int32_t *idx,
+                                    hipStream_t stream);
+
+/*
  * moba_attn_fwd -- attention over the selected blocks (task definition).
  *   For query t in block i: keys = all keys of each listed past block
  *   (0 <= idx < i) plus the keys u <= t of block i.  -1 entries are padding;

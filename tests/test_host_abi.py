@@ -199,3 +199,17 @@ def test_header_compiles_as_c_and_links(lib, tmp_path):
     assert int(out[1]) == 11                  # ceil(1000/128) + ceil(300/128)
     assert out[2] == "1"
     assert out[3].strip() == lib.moba_status_string(INVALID).decode()
+
+
+def test_route_noalloc_refuses_shapes_beyond_its_scratch(lib):
+    """The no-allocation routing call checks its fixed scratch size on the
+    host, before any launch (bf16: 4 d + 4 bytes per (block, head) row)."""
+    fake = ctypes.c_void_p(1 << 20)            # never dereferenced: refused first
+    # 2 x 262144 tokens, 64 heads, B = 64: 8192 blocks x 64 heads = 524288 rows
+    big = _shape(batch=2, seq=262144, heads=64, d=64, B=64, K=8)
+    need = lib.moba_route_topk_workspace_bytes(ctypes.byref(big))
+    assert need > 32 << 20
+    assert lib.moba_route_topk_noalloc(ctypes.byref(big), fake, fake, fake, None) == WS_SMALL
+    # invalid arguments are still refused as such
+    assert lib.moba_route_topk_noalloc(ctypes.byref(_shape()), None, fake, fake, None) == INVALID
+    assert lib.moba_route_topk_noalloc(ctypes.byref(_shape(d=96)), fake, fake, fake, None) == UNSUPPORTED
