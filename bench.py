@@ -54,56 +54,63 @@ def _traffic(per_launch_algo_bytes):
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(spec, x, nthreads=None, max_slices=32):
-    """The CPU oracle (as it stands) on a bounded sample: the first
-    `max_slices` (sequence, head) slices of the workload (all 32 at the
-    default workload, i.e. the whole forward), each a full forward of one
-    head of one sequence, on up to 16 threads (one slice per thread at a
-    time)."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
+
+def cpu_baseline(spec, x, nthreads=None):
+    """The CPU oracle (as it stands) on a bounded sample of the workload: the
+    whole forward (key conv when the workload has one, centroids, routing,
+    attention) of every head, on up to 16 threads (one (sequence, head) at a
+    time per thread).  The sample is the whole workload, except for the
+    512K-token sequence, whose first 131072 tokens are taken (its full
+    routing alone would take minutes).  C1 (one head, 1024 tokens) is also
+    timed on one thread."""
     import oracle
 
     avail = len(os.sched_getaffinity(0))
     threads = nthreads or min(16, avail)
-    n = max(1, min(max_slices, spec.batch * spec.heads))
-    b_sl = []
     H = spec.heads
-    q = x["q"].float().numpy()
-    k = x["k"].float().numpy()
-    v = x["v"].float().numpy()
-    for r in range(n):
-        b, h = divmod(r, H)
-        b_sl.append((b, h))
-    # stack the sampled slices as one "batch" of n sequences with one head
-    qs = np.ascontiguousarray(np.stack([q[b, :, h] for b, h in b_sl])[:, :, None, :])
-    ks = np.ascontiguousarray(np.stack([k[b, :, h] for b, h in b_sl])[:, :, None, :])
-    vs = np.ascontiguousarray(np.stack([v[b, :, h] for b, h in b_sl])[:, :, None, :])
-    w = None
-    if x["conv_w"] is not None:
-        raise NotImplementedError("cpu baseline sample covers conv-free workloads")
-    cu = [i * spec.seq for i in range(n + 1)]
-    t0 = time.perf_counter()
-    oracle.forward(qs.reshape(-1, 1, spec.head_dim), ks.reshape(-1, 1, spec.head_dim),
-                   vs.reshape(-1, 1, spec.head_dim), spec.block_size, spec.top_k, cu,
-                   conv_w=w, nthreads=threads)
-    dt = time.perf_counter() - t0
-    f_sample = workloads.eff_flops(spec)["total"] * n / (spec.batch * spec.heads)
-    model = ""
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
-    except OSError:
-        pass
-    return {
+    sample = spec
+    if spec.seqlens is None and spec.seq > 131072:
+        sample = spec.scaled(131072, "-prefix")
+        x = {n: (x[n][:, :131072] if n in ("q", "k", "v") else x[n]) for n in x}
+    q, k, v = (x[n].float().contiguous() for n in ("q", "k", "v"))
+    w = x["conv_w"]
+    cu = x["cu_seqlens"] or workloads.segments(sample)
+    mode = 0 if spec.conv_mode == "plain" else 1
+    rb = spec.dtype == "bf16"
+
+    def run(th):
+        t0 = time.perf_counter()
+        oracle.forward(q, k, v, spec.block_size, spec.top_k, cu, conv_w=w, conv_mode=mode,
+                       round_bf16=rb, nthreads=th)
+        return time.perf_counter() - t0
+
+    # the oracle runs one (sequence, head) per thread at a time
+    threads = min(threads, (len(cu) - 1) * H)
+    dt = run(threads)
+    f_sample = workloads.eff_flops(sample)["total"]
+    steps = ("key conv, " if w is not None else "") + "centroids, routing, attention"
+    what = ("the whole workload" if sample is spec else
+            f"the first {sample.seq} tokens of each of the {sample.batch} sequence(s)")
+    out = {
         "value": f_sample / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-        "sample": f"{n} of {spec.batch * spec.heads} (sequence, head) slices, full forward "
-                  f"(centroids, routing, attention) in fp64 C on {threads} threads; "
-                  f"{dt:.1f} s; cpu: {model}",
+        "sample": f"{what}, all {H} heads: full forward ({steps}) in fp64 C on {threads} "
+                  f"threads; {dt:.1f} s; cpu: {_cpu_model()}",
         "seconds": dt,
     }
+    if spec.name == "C1":
+        dt1 = run(1)
+        out["single_thread"] = {"value": f_sample / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
+                                "seconds": dt1}
+    return out
 
 
 def _calib_copy(args, dev):
@@ -208,6 +215,15 @@ def main():
     routed_tflops = fl["routed"] / (routed_ms * 1e-3) / 1e12
     pairs = workloads.routed_pairs(spec)
     traffic = _traffic(pairs) if args.config == "H" else None
+    # the routing stages against the HBM roofline: algorithmic bytes (every
+    # tensor moved once) over the event-timed stage time
+    rbytes = workloads.routing_bytes(spec)
+    routing = {}
+    for n, b in rbytes.items():
+        t = stage_ms[n] * 1e-3
+        routing[n] = {"ms": round(stage_ms[n], 4), "alg_bytes": b,
+                      "GBps": round(b / t / 1e9, 1),
+                      "pct_of_hbm_peak": round(100 * b / t / 1e9 / PEAK_HBM_GBS, 1)}
 
     out = {
         "metric": METRIC,
@@ -229,6 +245,7 @@ def main():
                    "F_eff": fl["total"]},
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "stage_ms": {n: round(t, 4) for n, t in stage_ms.items()},
+        "routing_hbm": routing,
         "event_ms_per_step": round(sum(ms_steps) / len(ms_steps), 4),
         "event_ms_median": round(sorted(ms_steps)[len(ms_steps) // 2], 4),
         "event_ms_min": round(min(ms_steps), 4),
@@ -249,10 +266,7 @@ def main():
                              if traffic else None),
         },
     }
-    if not args.no_cpu_baseline and spec.conv_width == 0:
-        out["cpu_baseline"] = cpu_baseline(spec, x)
-    else:
-        out["cpu_baseline"] = None
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(spec, x)
     print(json.dumps(out), flush=True)
 
 

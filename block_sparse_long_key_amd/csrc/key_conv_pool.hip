@@ -52,30 +52,10 @@ template <> struct Vec4<uint16_t> {
 };
 
 // k + SiLU(acc) rounded to T, equal to the exact formula's result: the
-// fp64 value k + acc / (1 + e^-acc), rounded to fp32 and then to T.
-// bf16: the value comes from the hardware exp2 and reciprocal in fp32;
-// |r - v| <= |silu| (|acc| + 8) 2^-23 + |r| 2^-24 (the exp2 argument's
-// rounding costs |acc| 2^-23 relative, exp2, the reciprocal and the three
-// roundings a few 2^-24 more) and fp32(v) is another |r| 2^-24 away.  When
-// r is farther than twice that from the bf16 rounding midpoint next to it,
-// every value in reach rounds to the same bf16 and the fast result stands;
-// otherwise (about 1 element in 10^3) the fp64 formula decides.  fp32 I/O
-// (the correctness path) always takes the fp64 formula.
+// fp64 value v = k + acc / (1 + e^-acc), rounded to fp32 and then to T.
 template <typename T>
-__device__ __forceinline__ float silu_residual(float x, float acc)
+__device__ __forceinline__ float silu_exact(float x, float acc)
 {
-    if constexpr (sizeof(T) == 2) {
-        const float silu = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * 1.4426950408889634f));
-        const float r = x + silu;
-        const float rb = IO<T>::round(r);
-        const uint32_t ex = __float_as_uint(r) & 0x7f800000u;
-        // half a bf16 ulp in r's binade
-        const float hu = __uint_as_float(ex - (8u << 23));
-        const float delta = __builtin_fmaf(fabsf(silu), (fabsf(acc) + 8.0f) * 1.1920929e-07f,
-                                           fabsf(r) * 5.9604645e-08f) + 1e-35f;
-        const bool safe = ex > (9u << 23) && hu - fabsf(r - rb) > 2.0f * delta;
-        if (__builtin_expect(safe, 1)) return rb;
-    }
     const double a = (double)acc;
     float f = (float)((double)x + a / (1.0 + exp(-a)));
     // the fp32 rounding stays a step of its own: folded into the dtype
@@ -83,6 +63,27 @@ __device__ __forceinline__ float silu_residual(float x, float acc)
     // where the fp32 value is a bf16 tie
     asm volatile("" : "+v"(f));
     return IO<T>::round(f);
+}
+
+// The same for bf16 output from the hardware exp2 and reciprocal in fp32:
+// |r - v| <= |silu| (|acc| + 8) 2^-23 + |r| 2^-24 (the exp2 argument's
+// rounding costs |acc| 2^-23 relative, exp2, the reciprocal and the three
+// roundings a few 2^-24 more) and fp32(v) is another |r| 2^-24 away.  When
+// r is farther than twice that from the bf16 rounding midpoint next to it,
+// every value in reach rounds to the same bf16: `safe`, and the result is
+// exact; otherwise (about 1 element in 700) silu_exact decides.
+__device__ __forceinline__ float silu_fast_bf16(float x, float acc, bool& safe)
+{
+    const float silu = acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc * 1.4426950408889634f));
+    const float r = x + silu;
+    const float rb = IO<uint16_t>::round(r);
+    const uint32_t ex = __float_as_uint(r) & 0x7f800000u;
+    // half a bf16 ulp in r's binade
+    const float hu = __uint_as_float(ex - (8u << 23));
+    const float delta = __builtin_fmaf(fabsf(silu), (fabsf(acc) + 8.0f) * 1.1920929e-07f,
+                                       fabsf(r) * 5.9604645e-08f) + 1e-35f;
+    safe = ex > (9u << 23) && hu - fabsf(r - rb) > 2.0f * delta;
+    return rb;
 }
 
 // CONV: apply the key convolution (MODE 0 plain, 1 SiLU + residual) and
@@ -129,6 +130,16 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
         }
     }
 
+    // bf16 k + SiLU(conv): elements whose fast result is not proven are
+    // queued (x, acc, fast result, position) and finished after the block
+    // in fp64, so a wave runs the fp64 formula a few times per block instead
+    // of at every token where one lane needs it; a full queue finishes an
+    // element on the spot
+    constexpr bool DEFER = CONV && MODE == 1 && sizeof(T) == 2;
+    constexpr int kQ = 6;
+    __shared__ float4 fq[DEFER ? kQ : 1][kThreads];
+    int nq = 0;
+
     double sum[kVec] = {0.0, 0.0, 0.0, 0.0};
     // (8 tokens in flight: plain conv / pooling 4-14 % faster than 4; the
     // SiLU mode is VALU-bound and keeps 4)
@@ -148,10 +159,23 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
 #pragma unroll
                 for (int l = kMaxW - 1; l >= 0; --l)
                     if (l < W) acc = __builtin_fmaf(wr[v][l], win[v][l], acc);
-                if constexpr (MODE == 1)
-                    y[v] = silu_residual<T>(x[v], acc);
-                else
+                if constexpr (DEFER) {
+                    bool safe;
+                    y[v] = silu_fast_bf16(x[v], acc, safe);
+                    if (!safe) {
+                        if (nq < kQ) {
+                            fq[nq][threadIdx.x] = make_float4(x[v], acc, y[v],
+                                                              __int_as_float(((tl - a) << 2) | v));
+                            ++nq;
+                        } else {
+                            y[v] = silu_exact<T>(x[v], acc);
+                        }
+                    }
+                } else if constexpr (MODE == 1) {
+                    y[v] = silu_exact<T>(x[v], acc);
+                } else {
                     y[v] = IO<T>::round(acc);
+                }
             }
             Vec4<T>::store(kout + row, y);
         } else {
@@ -161,6 +185,24 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
         if constexpr (POOL) {
 #pragma unroll
             for (int v = 0; v < kVec; ++v) sum[v] += (double)y[v];
+        }
+    }
+    if constexpr (DEFER) {
+        // finish the queued elements: the exact k' replaces the fast one in
+        // k_out (this thread stored it) and in the block sum (an fp64 sum of
+        // bf16 keys is exact, so the order of its terms does not matter)
+        for (int e = 0; e < nq; ++e) {
+            const float4 f = fq[e][threadIdx.x];
+            const int pos = __float_as_int(f.w);
+            const int tl = a + (pos >> 2), v = pos & 3;
+            const float yx = silu_exact<T>(f.x, f.y);
+            if (yx != f.z) {
+                kout[(size_t)(t0 + tl) * HD + ch + v] = f32_to_bf16(yx);
+                const double dlt = (double)yx - (double)f.z;
+#pragma unroll
+                for (int u = 0; u < kVec; ++u)
+                    if (u == v) sum[u] += dlt;
+            }
         }
     }
     if constexpr (POOL) {

@@ -28,7 +28,7 @@ from typing import List, Optional
 import torch
 
 __all__ = ["Spec", "CONFIGS", "spec", "make", "segments", "eff_flops",
-           "routed_pairs", "grad_output", "eff_flops_bwd"]
+           "routed_pairs", "grad_output", "eff_flops_bwd", "routing_bytes"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -251,3 +251,26 @@ def eff_flops_bwd(s: Spec) -> dict:
     i.e. 2.5 times the forward's 4*d."""
     f = eff_flops(s)
     return {n: v * 5 // 2 for n, v in f.items()}
+
+
+def routing_bytes(s: Spec) -> dict:
+    """Algorithmic HBM bytes of the routing stages of one forward (every
+    tensor moved once): key conv + pooling (k read, k' written, centroids
+    written) or pooling alone (k read, centroids written); the router (q
+    read, the centroids read once per (sequence, head), idx written); the
+    index inversion (idx read, one 4-byte entry written per (query, routed
+    block) pair)."""
+    esz = 4 if s.dtype == "f32" else 2
+    d, H, K = s.head_dim, s.heads, s.top_k
+    tokens = sum(s.seqlens) if s.seqlens is not None else s.batch * s.seq
+    lens = s.seqlens if s.seqlens is not None else (s.seq,) * s.batch
+    blocks = sum((L + s.block_size - 1) // s.block_size for L in lens)
+    kv = tokens * H * d * esz
+    cent = blocks * H * d * 4
+    idx = tokens * H * K * 4
+    out = {"pool": kv + cent}
+    if s.conv_width > 0:
+        out = {"conv_pool": 2 * kv + cent}
+    out["route"] = kv + cent + idx
+    out["index"] = idx + routed_pairs(s) * 4
+    return out
