@@ -220,7 +220,7 @@ __global__ __launch_bounds__(64 * kRedWaves) void conv_dw_reduce_kernel(int nblk
 
 template <typename T, int MODE>
 hipError_t conv_bwd_t(const Launch& L, const void* k, const float* w, int W, const void* gk,
-                      void* dk, float* dw, float* dwp)
+                      void* dk, float* dwp)
 {
     const int HD = L.st.H * L.D;
     const int nblk = L.st.total_blocks;
@@ -228,25 +228,29 @@ hipError_t conv_bwd_t(const Launch& L, const void* k, const float* w, int W, con
         dim3 grid(nblk, (HD + kThreads * kVec - 1) / (kThreads * kVec));
         hipLaunchKernelGGL((conv_bwd_kernel<T, MODE>), grid, dim3(kThreads), 0, L.stream, L.st, HD,
                            (const T*)k, w, W, (const T*)gk, (T*)dk, dwp);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
-    const int n = HD * W;
-    hipLaunchKernelGGL(conv_dw_reduce_kernel, dim3((n + 63) / 64), dim3(64 * kRedWaves), 0,
-                       L.stream, nblk, n, dwp, dw);
     return hipGetLastError();
 }
 
 }  // namespace
 
+// dk and the per-block dw partials (at dwp + block * H*d*W) of one launch
 hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W, int mode,
-                           const void* gk, void* dk, float* dw, float* dwp)
+                           const void* gk, void* dk, float* dwp)
 {
     if (L.dtype == MOBA_BF16)
-        return mode == 0 ? conv_bwd_t<uint16_t, 0>(L, k, w, W, gk, dk, dw, dwp)
-                         : conv_bwd_t<uint16_t, 1>(L, k, w, W, gk, dk, dw, dwp);
-    return mode == 0 ? conv_bwd_t<float, 0>(L, k, w, W, gk, dk, dw, dwp)
-                     : conv_bwd_t<float, 1>(L, k, w, W, gk, dk, dw, dwp);
+        return mode == 0 ? conv_bwd_t<uint16_t, 0>(L, k, w, W, gk, dk, dwp)
+                         : conv_bwd_t<uint16_t, 1>(L, k, w, W, gk, dk, dwp);
+    return mode == 0 ? conv_bwd_t<float, 0>(L, k, w, W, gk, dk, dwp)
+                     : conv_bwd_t<float, 1>(L, k, w, W, gk, dk, dwp);
+}
+
+// dw = the sum over nblk blocks of the partials (n = H*d*W values each)
+hipError_t launch_conv_dw_reduce(hipStream_t stream, int nblk, int n, const float* dwp, float* dw)
+{
+    hipLaunchKernelGGL(conv_dw_reduce_kernel, dim3((n + 63) / 64), dim3(64 * kRedWaves), 0, stream,
+                       nblk, n, dwp, dw);
+    return hipGetLastError();
 }
 
 }  // namespace moba

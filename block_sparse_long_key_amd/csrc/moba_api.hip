@@ -148,6 +148,10 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
 moba_status hip_status(hipError_t e) { return e == hipSuccess ? MOBA_OK : MOBA_ERR_HIP; }
 
 bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
+// idx and lse of a later sequence group start at a row offset: 4-byte
+// aligned (the caller's own pointers are checked for 16 bytes)
+bool idx_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+
 
 // The attention entry points work on 128-key blocks when the shape's blocks
 // are larger: Ll is the shape's own launch (routing granularity), La the
@@ -184,46 +188,122 @@ float resolve_scale(float scale, int D)
     return scale > 0.f ? scale : (float)(1.0 / sqrt((double)D));
 }
 
-}  // namespace
+// ---------------------------------------------------------------------
+// Calls over more sequences than one launch table holds (kMaxSeqs) run as
+// consecutive groups of at most kMaxSeqs sequences, each a shape of its own
+// with every pointer advanced to its first token or block: sequences are
+// independent, so the results are those of one call.  Workspaces hold one
+// region per group (the stages of one call find their group's lists in
+// place); the routing workspace is reused group after group.
+struct Groups {
+    int n = 0;                     // number of groups
+    int nseq = 0;                  // sequences over all groups
+    moba_shape base;               // the caller's shape
+    const int32_t* cu = nullptr;   // caller's cu_seqlens (null: uniform batch)
+};
 
-extern "C" {
+struct Group {
+    moba_shape sh;
+    int32_t cu[kMaxSeqs + 1];
+    int64_t tok0 = 0;              // first token of the group (over the call)
+    int64_t blk0 = 0;              // first block of the group (shape's block size)
+};
 
-int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-const char* moba_status_string(moba_status s)
+// validates what spans groups (cu_seqlens as a whole, the token x head
+// limit); everything else is checked per group by make_launch
+moba_status split(const moba_shape* sh, Groups* G)
 {
-    switch (s) {
-        case MOBA_OK: return "ok";
-        case MOBA_ERR_INVALID_ARG: return "invalid argument";
-        case MOBA_ERR_UNSUPPORTED: return "unsupported shape or parameter";
-        case MOBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
-        case MOBA_ERR_HIP: return "HIP launch error";
+    if (!sh) return MOBA_ERR_INVALID_ARG;
+    if (sh->heads < 1 || sh->seq < 0 || sh->batch < 1 || sh->block_size < 1)
+        return MOBA_ERR_INVALID_ARG;
+    G->base = *sh;
+    if (sh->cu_seqlens) {
+        if (sh->batch != 1 || sh->num_seqs < 1) return MOBA_ERR_INVALID_ARG;
+        const int32_t* cu = sh->cu_seqlens;
+        if (cu[0] != 0 || cu[sh->num_seqs] != sh->seq) return MOBA_ERR_INVALID_ARG;
+        for (int q = 0; q < sh->num_seqs; ++q)
+            if (cu[q + 1] < cu[q]) return MOBA_ERR_INVALID_ARG;
+        G->cu = cu;
+        G->nseq = sh->num_seqs;
+    } else {
+        G->nseq = sh->batch;
     }
-    return "unknown status";
+    const int64_t tokens = sh->cu_seqlens ? (int64_t)sh->seq : (int64_t)sh->batch * sh->seq;
+    if (tokens * sh->heads >= kMaxRows) return MOBA_ERR_UNSUPPORTED;
+    G->n = (G->nseq + kMaxSeqs - 1) / kMaxSeqs;
+    return MOBA_OK;
 }
 
-int64_t moba_total_blocks(const moba_shape* shape)
+void group(const Groups& G, int g, Group* out)
+{
+    const int s0 = g * kMaxSeqs;
+    const int n = std::min(kMaxSeqs, G.nseq - s0);
+    out->sh = G.base;
+    if (G.cu) {
+        const int32_t c0 = G.cu[s0];
+        for (int q = 0; q <= n; ++q) out->cu[q] = G.cu[s0 + q] - c0;
+        out->sh.cu_seqlens = out->cu;
+        out->sh.num_seqs = n;
+        out->sh.seq = G.cu[s0 + n] - c0;
+        out->tok0 = c0;
+        int64_t b = 0;
+        for (int q = 0; q < s0; ++q) b += ceil_div64(G.cu[q + 1] - G.cu[q], G.base.block_size);
+        out->blk0 = b;
+    } else {
+        out->sh.batch = n;
+        out->tok0 = (int64_t)s0 * G.base.seq;
+        out->blk0 = (int64_t)s0 * ceil_div64(G.base.seq, G.base.block_size);
+    }
+}
+
+moba_status check_groups(const Groups& G)
+{
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        Launch L;
+        const moba_status st = make_launch(&gr.sh, &L, nullptr);
+        if (st != MOBA_OK) return st;
+    }
+    return MOBA_OK;
+}
+
+size_t esize(const moba_shape* sh) { return sh->dtype == MOBA_BF16 ? 2 : 4; }
+
+// element offsets of a group: token rows of q/k/v/o, idx rows, lse, centroids
+template <typename P>
+P* at(P* p, int64_t rows, size_t bytes_per_row)
+{
+    return p ? (P*)((char*)const_cast<void*>((const void*)p) + rows * (int64_t)bytes_per_row) : p;
+}
+
+}  // namespace
+
+namespace one {
+int64_t total_blocks_one(const moba_shape* shape)
 {
     Launch L;
     if (make_launch(shape, &L, nullptr) != MOBA_OK) return -1;
     return L.st.total_blocks;
 }
 
-size_t moba_attn_fwd_workspace_bytes(const moba_shape* shape)
+size_t attn_fwd_workspace_bytes_one(const moba_shape* shape)
 {
     Launch Ll, La;
     if (attn_launch(shape, nullptr, &Ll, &La) != MOBA_OK) return 0;
     return layout(La, false, expands(Ll)).total;
 }
 
-size_t moba_attn_bwd_workspace_bytes(const moba_shape* shape)
+size_t attn_bwd_workspace_bytes_one(const moba_shape* shape)
 {
     Launch Ll, La;
     if (attn_launch(shape, nullptr, &Ll, &La) != MOBA_OK) return 0;
     return layout(La, true, expands(Ll)).total;
 }
 
-moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w, int32_t width,
+moba_status key_conv_one(const moba_shape* shape, const void* k, const float* w, int32_t width,
                           int32_t mode, void* k_out, float* cent, hipStream_t stream)
 {
     Launch L;
@@ -239,14 +319,14 @@ moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w
     return hip_status(launch_conv_pool(L, k, w, width, mode, k_out, cent));
 }
 
-size_t moba_key_conv_bwd_workspace_bytes(const moba_shape* shape, int32_t width)
+size_t key_conv_bwd_workspace_bytes_one(const moba_shape* shape, int32_t width)
 {
     Launch L;
     if (make_launch(shape, &L, nullptr) != MOBA_OK || width < 1 || width > 8) return 0;
     return align256((size_t)L.st.total_blocks * L.st.H * L.D * width * 4);
 }
 
-moba_status moba_key_conv_bwd(const moba_shape* shape, const void* k, const float* w, int32_t width,
+moba_status key_conv_bwd_one(const moba_shape* shape, const void* k, const float* w, int32_t width,
                               int32_t mode, const void* dk_out, void* dk, float* dw, void* workspace,
                               size_t workspace_bytes, hipStream_t stream)
 {
@@ -259,13 +339,13 @@ moba_status moba_key_conv_bwd(const moba_shape* shape, const void* k, const floa
     if (!ptr_ok(k) || !ptr_ok(w) || !ptr_ok(dk_out) || !ptr_ok(dk) || !ptr_ok(dw))
         return MOBA_ERR_INVALID_ARG;
     if (dk == k || dk == dk_out) return MOBA_ERR_INVALID_ARG;
-    const size_t need = moba_key_conv_bwd_workspace_bytes(shape, width);
+    const size_t need = key_conv_bwd_workspace_bytes_one(shape, width);
     if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
     if (workspace_bytes < need) return MOBA_ERR_WORKSPACE_TOO_SMALL;
-    return hip_status(launch_conv_bwd(L, k, w, width, mode, dk_out, dk, dw, (float*)workspace));
+    return hip_status(launch_conv_bwd(L, k, w, width, mode, dk_out, dk, (float*)workspace));
 }
 
-moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, hipStream_t stream)
+moba_status centroids_one(const moba_shape* shape, const void* k, float* cent, hipStream_t stream)
 {
     Launch L;
     moba_status st = make_launch(shape, &L, stream);
@@ -275,33 +355,33 @@ moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, 
     return hip_status(launch_conv_pool(L, k, nullptr, 0, 0, nullptr, cent));
 }
 
-size_t moba_route_topk_workspace_bytes(const moba_shape* shape)
+size_t route_topk_workspace_bytes_one(const moba_shape* shape)
 {
     Launch L;
     if (make_launch(shape, &L, nullptr) != MOBA_OK) return 0;
     return std::max(route_ws_bytes(L), (size_t)256);
 }
 
-moba_status moba_route_topk(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
+moba_status route_topk_one(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
                             void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     Launch L;
     moba_status st = make_launch(shape, &L, stream);
     if (st != MOBA_OK) return st;
-    if (!ptr_ok(q) || !ptr_ok(cent) || !ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (!ptr_ok(q) || !ptr_ok(cent) || !idx_ok(idx)) return MOBA_ERR_INVALID_ARG;
     if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
     if (workspace_bytes < std::max(route_ws_bytes(L), (size_t)256)) return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (L.tokens == 0) return MOBA_OK;
     return hip_status(launch_route(L, q, cent, workspace, idx));
 }
 
-moba_status moba_route_topk_noalloc(const moba_shape* shape, const void* q, const float* cent,
+moba_status route_topk_noalloc_one(const moba_shape* shape, const void* q, const float* cent,
                                     int32_t* idx, hipStream_t stream)
 {
     Launch L;
     moba_status st = make_launch(shape, &L, stream);
     if (st != MOBA_OK) return st;
-    if (!ptr_ok(q) || !ptr_ok(cent) || !ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (!ptr_ok(q) || !ptr_ok(cent) || !idx_ok(idx)) return MOBA_ERR_INVALID_ARG;
     if (L.dtype == MOBA_BF16 && route_ws_bytes(L) > (size_t)MOBA_ROUTE_SCRATCH_BYTES)
         return MOBA_ERR_WORKSPACE_TOO_SMALL;
     if (L.tokens == 0) return MOBA_OK;
@@ -324,13 +404,13 @@ hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, cha
     return launch_inv(La, ws, wsp, idx, det);
 }
 
-moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* workspace,
+moba_status attn_index_one(const moba_shape* shape, const int32_t* idx, void* workspace,
                             size_t workspace_bytes, hipStream_t stream)
 {
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
-    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (!idx_ok(idx)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
     st = check_ws(L, workspace, workspace_bytes, &ws, false, expands(Ll));
     if (st != MOBA_OK) return st;
@@ -338,7 +418,7 @@ moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* w
     return hip_status(run_index(Ll, L, ws, (char*)workspace, idx));
 }
 
-moba_status moba_attn_routed(const moba_shape* shape, const void* q, const void* k, const void* v,
+moba_status attn_routed_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                              float softmax_scale, void* workspace, size_t workspace_bytes,
                              hipStream_t stream)
 {
@@ -354,16 +434,16 @@ moba_status moba_attn_routed(const moba_shape* shape, const void* q, const void*
                                          resolve_scale(softmax_scale, L.D)));
 }
 
-moba_status moba_attn_combine(const moba_shape* shape, const void* q, const void* k, const void* v,
+moba_status attn_combine_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                               const int32_t* idx, float softmax_scale, void* o, float* lse,
                               void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
-    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o))
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !idx_ok(idx) || !ptr_ok(o))
         return MOBA_ERR_INVALID_ARG;
-    if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3u)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
     st = check_ws(L, workspace, workspace_bytes, &ws, false, expands(Ll));
     if (st != MOBA_OK) return st;
@@ -372,19 +452,19 @@ moba_status moba_attn_combine(const moba_shape* shape, const void* q, const void
                                           resolve_scale(softmax_scale, L.D), o, lse));
 }
 
-moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+moba_status attn_fwd_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                           const int32_t* idx, float softmax_scale, void* o, float* lse,
                           void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
-    moba_status st = moba_attn_index(shape, idx, workspace, workspace_bytes, stream);
+    moba_status st = attn_index_one(shape, idx, workspace, workspace_bytes, stream);
     if (st != MOBA_OK) return st;
-    st = moba_attn_routed(shape, q, k, v, softmax_scale, workspace, workspace_bytes, stream);
+    st = attn_routed_one(shape, q, k, v, softmax_scale, workspace, workspace_bytes, stream);
     if (st != MOBA_OK) return st;
-    return moba_attn_combine(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
+    return attn_combine_one(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
                              workspace_bytes, stream);
 }
 
-moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+moba_status attn_bwd_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                           const int32_t* idx, float softmax_scale, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, hipStream_t stream)
@@ -392,7 +472,7 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
-    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !ptr_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !idx_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
         !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
         return MOBA_ERR_INVALID_ARG;
     const void* ins[] = {q, k, v, o, dout, (const void*)lse, (const void*)idx};
@@ -416,6 +496,307 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
                                               dq, dk, dv));
     }
     return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout, scale, dq, dk, dv));
+}
+
+}  // namespace one
+
+extern "C" {
+
+int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
+
+const char* moba_status_string(moba_status s)
+{
+    switch (s) {
+        case MOBA_OK: return "ok";
+        case MOBA_ERR_INVALID_ARG: return "invalid argument";
+        case MOBA_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+        case MOBA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOBA_ERR_HIP: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+// ---------------------------------------------------------------- groups --
+#define MOBA_GROUPS(shape)                      \
+    Groups G;                                   \
+    {                                           \
+        moba_status st_ = split(shape, &G);     \
+        if (st_ == MOBA_OK) st_ = check_groups(G); \
+        if (st_ != MOBA_OK) return st_;         \
+    }
+
+int64_t moba_total_blocks(const moba_shape* shape)
+{
+    Groups G;
+    if (split(shape, &G) != MOBA_OK) return -1;
+    int64_t n = 0;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const int64_t b = one::total_blocks_one(&gr.sh);
+        if (b < 0) return -1;
+        n += b;
+    }
+    return n;
+}
+
+size_t moba_attn_fwd_workspace_bytes(const moba_shape* shape)
+{
+    Groups G;
+    if (split(shape, &G) != MOBA_OK) return 0;
+    size_t n = 0;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        Launch Ll, La;
+        if (attn_launch(&gr.sh, nullptr, &Ll, &La) != MOBA_OK) return 0;
+        n += one::attn_fwd_workspace_bytes_one(&gr.sh);
+    }
+    return n;
+}
+
+size_t moba_attn_bwd_workspace_bytes(const moba_shape* shape)
+{
+    Groups G;
+    if (split(shape, &G) != MOBA_OK) return 0;
+    size_t n = 0;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        Launch Ll, La;
+        if (attn_launch(&gr.sh, nullptr, &Ll, &La) != MOBA_OK) return 0;
+        n += one::attn_bwd_workspace_bytes_one(&gr.sh);
+    }
+    return n;
+}
+
+moba_status moba_key_conv(const moba_shape* shape, const void* k, const float* w, int32_t width,
+                          int32_t mode, void* k_out, float* cent, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    const size_t row = (size_t)shape->heads * shape->head_dim;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        moba_status st = one::key_conv_one(&gr.sh, at(k, gr.tok0, row * esize(shape)), w, width, mode,
+                                           at(k_out, gr.tok0, row * esize(shape)),
+                                           at(cent, gr.blk0, row * 4), stream);
+        if (st != MOBA_OK) return st;
+    }
+    return MOBA_OK;
+}
+
+size_t moba_key_conv_bwd_workspace_bytes(const moba_shape* shape, int32_t width)
+{
+    const int64_t nb = moba_total_blocks(shape);
+    if (nb < 0 || width < 1 || width > 8) return 0;
+    return align256((size_t)nb * shape->heads * shape->head_dim * width * 4);
+}
+
+moba_status moba_key_conv_bwd(const moba_shape* shape, const void* k, const float* w, int32_t width,
+                              int32_t mode, const void* dk_out, void* dk, float* dw, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (mode != MOBA_CONV_PLAIN && mode != MOBA_CONV_SILU_RESIDUAL) return MOBA_ERR_INVALID_ARG;
+    if (width < 1) return MOBA_ERR_INVALID_ARG;
+    if (width > 8) return MOBA_ERR_UNSUPPORTED;
+    if (!ptr_ok(k) || !ptr_ok(w) || !ptr_ok(dk_out) || !ptr_ok(dk) || !ptr_ok(dw))
+        return MOBA_ERR_INVALID_ARG;
+    if (dk == k || dk == dk_out) return MOBA_ERR_INVALID_ARG;
+    const size_t need = moba_key_conv_bwd_workspace_bytes(shape, width);
+    if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
+    if (workspace_bytes < need) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    const size_t row = (size_t)shape->heads * shape->head_dim;
+    const size_t part = row * (size_t)width;            // dw partial floats per block
+    // every group's pass first (dk and per-block dw partials), then one fixed-order sum
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        moba_status st = one::key_conv_bwd_one(&gr.sh, at(k, gr.tok0, row * esize(shape)), w, width, mode,
+                                               at(dk_out, gr.tok0, row * esize(shape)),
+                                               at(dk, gr.tok0, row * esize(shape)), dw,
+                                               at(workspace, gr.blk0, part * 4),
+                                               workspace_bytes - (size_t)gr.blk0 * part * 4, stream);
+        if (st != MOBA_OK) return st;
+    }
+    return hip_status(launch_conv_dw_reduce(stream, (int)moba_total_blocks(shape), (int)part,
+                                            (const float*)workspace, dw));
+}
+
+moba_status moba_centroids(const moba_shape* shape, const void* k, float* cent, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    const size_t row = (size_t)shape->heads * shape->head_dim;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        moba_status st = one::centroids_one(&gr.sh, at(k, gr.tok0, row * esize(shape)),
+                                            at(cent, gr.blk0, row * 4), stream);
+        if (st != MOBA_OK) return st;
+    }
+    return MOBA_OK;
+}
+
+size_t moba_route_topk_workspace_bytes(const moba_shape* shape)
+{
+    Groups G;
+    if (split(shape, &G) != MOBA_OK) return 0;
+    size_t n = 0;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t b = one::route_topk_workspace_bytes_one(&gr.sh);
+        if (b == 0) return 0;
+        n = std::max(n, b);
+    }
+    return n;
+}
+
+moba_status moba_route_topk(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    const size_t row = (size_t)shape->heads * shape->head_dim;
+    const size_t irow = (size_t)shape->heads * (shape->top_k > 0 ? shape->top_k : 0) * 4;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        moba_status st = one::route_topk_one(&gr.sh, at(q, gr.tok0, row * esize(shape)),
+                                             at(cent, gr.blk0, row * 4), at(idx, gr.tok0, irow),
+                                             workspace, workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+    }
+    return MOBA_OK;
+}
+
+moba_status moba_route_topk_noalloc(const moba_shape* shape, const void* q, const float* cent,
+                                    int32_t* idx, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    const size_t row = (size_t)shape->heads * shape->head_dim;
+    const size_t irow = (size_t)shape->heads * (shape->top_k > 0 ? shape->top_k : 0) * 4;
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        moba_status st = one::route_topk_noalloc_one(&gr.sh, at(q, gr.tok0, row * esize(shape)),
+                                                     at(cent, gr.blk0, row * 4), at(idx, gr.tok0, irow),
+                                                     stream);
+        if (st != MOBA_OK) return st;
+    }
+    return MOBA_OK;
+}
+
+#define MOBA_ATTN_GROUPS(bwd_)                                                           \
+    const size_t row = (size_t)shape->heads * shape->head_dim;                          \
+    const size_t irow = (size_t)shape->heads * (shape->top_k > 0 ? shape->top_k : 0) * 4; \
+    const size_t lrow = (size_t)shape->heads * 4;                                       \
+    (void)row; (void)irow; (void)lrow;                                                  \
+    const size_t need_ = (bwd_) ? moba_attn_bwd_workspace_bytes(shape)                   \
+                                : moba_attn_fwd_workspace_bytes(shape);                  \
+    if (G.n > 1 && workspace_bytes < need_) return MOBA_ERR_WORKSPACE_TOO_SMALL;        \
+    size_t wsoff = 0;
+
+moba_status moba_attn_index(const moba_shape* shape, const int32_t* idx, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    MOBA_ATTN_GROUPS(false);
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t wsz = one::attn_fwd_workspace_bytes_one(&gr.sh);
+        moba_status st = one::attn_index_one(&gr.sh, at(idx, gr.tok0, irow), at(workspace, (int64_t)wsoff, 1),
+                                             G.n > 1 ? wsz : workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+        wsoff += wsz;
+    }
+    return MOBA_OK;
+}
+
+moba_status moba_attn_routed(const moba_shape* shape, const void* q, const void* k, const void* v,
+                             float softmax_scale, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    MOBA_ATTN_GROUPS(false);
+    const size_t er = row * esize(shape);
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t wsz = one::attn_fwd_workspace_bytes_one(&gr.sh);
+        moba_status st = one::attn_routed_one(&gr.sh, at(q, gr.tok0, er), at(k, gr.tok0, er),
+                                              at(v, gr.tok0, er), softmax_scale,
+                                              at(workspace, (int64_t)wsoff, 1),
+                                              G.n > 1 ? wsz : workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+        wsoff += wsz;
+    }
+    return MOBA_OK;
+}
+
+moba_status moba_attn_combine(const moba_shape* shape, const void* q, const void* k, const void* v,
+                              const int32_t* idx, float softmax_scale, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
+    MOBA_ATTN_GROUPS(false);
+    const size_t er = row * esize(shape);
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t wsz = one::attn_fwd_workspace_bytes_one(&gr.sh);
+        moba_status st = one::attn_combine_one(&gr.sh, at(q, gr.tok0, er), at(k, gr.tok0, er),
+                                               at(v, gr.tok0, er), at(idx, gr.tok0, irow), softmax_scale,
+                                               at(o, gr.tok0, er), at(lse, gr.tok0, lrow),
+                                               at(workspace, (int64_t)wsoff, 1),
+                                               G.n > 1 ? wsz : workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+        wsoff += wsz;
+    }
+    return MOBA_OK;
+}
+
+moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+                          const int32_t* idx, float softmax_scale, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    moba_status st = moba_attn_index(shape, idx, workspace, workspace_bytes, stream);
+    if (st != MOBA_OK) return st;
+    st = moba_attn_routed(shape, q, k, v, softmax_scale, workspace, workspace_bytes, stream);
+    if (st != MOBA_OK) return st;
+    return moba_attn_combine(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
+                             workspace_bytes, stream);
+}
+
+moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+                          const int32_t* idx, float softmax_scale, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx) || !ptr_ok(lse)) return MOBA_ERR_INVALID_ARG;
+    MOBA_ATTN_GROUPS(true);
+    const size_t er = row * esize(shape);
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t wsz = one::attn_bwd_workspace_bytes_one(&gr.sh);
+        moba_status st = one::attn_bwd_one(&gr.sh, at(q, gr.tok0, er), at(k, gr.tok0, er), at(v, gr.tok0, er),
+                                           at(idx, gr.tok0, irow), softmax_scale, at(o, gr.tok0, er),
+                                           at(lse, gr.tok0, lrow), at(dout, gr.tok0, er), at(dq, gr.tok0, er),
+                                           at(dk, gr.tok0, er), at(dv, gr.tok0, er),
+                                           at(workspace, (int64_t)wsoff, 1),
+                                           G.n > 1 ? wsz : workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+        wsoff += wsz;
+    }
+    return MOBA_OK;
 }
 
 }  // extern "C"

@@ -152,7 +152,8 @@ struct Launch {
 hipError_t launch_conv_pool(const Launch& L, const void* k, const float* w, int W,
                             int mode, void* k_out, float* cent);
 hipError_t launch_conv_bwd(const Launch& L, const void* k, const float* w, int W, int mode,
-                           const void* gk, void* dk, float* dw, float* dwp);
+                           const void* gk, void* dk, float* dwp);
+hipError_t launch_conv_dw_reduce(hipStream_t stream, int nblk, int n, const float* dwp, float* dw);
 // The router's workspace: the centroids split for the MFMA scores (bf16 high
 // and low parts, [block][head][d] like the centroids) and their squared
 // norms ([block][head]).

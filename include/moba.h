@@ -39,14 +39,19 @@
  *     returns MOBA_ERR_HIP.  Device faults surface at the caller's next sync.
  *     Nothing is printed, nothing throws.
  *   - Calls are stateless and may be issued from several host threads.
+ *   - A call over more sequences than one launch table holds
+ *     (MOBA_MAX_SEQS, a varlen batch or a uniform batch of more rows) runs
+ *     them as consecutive groups of MOBA_MAX_SEQS sequences, each with its
+ *     pointers advanced to its first token / block (sequences are
+ *     independent): the results are those of one call.  The attention
+ *     workspaces then hold one region per group, back to back.
  *
  * Support matrix: head_dim 64 or 128; block_size 64, 128, 256 or 512
  * (256 / 512: top_k <= 8, the summary page's MoBA-256 / MoBA-512 variants,
  * "Configurazione MoBA"); top_k 1..32; conv width 1..8; dtype bf16 (fast
  * path) or fp32 (correctness path; block_size * head_dim <= 8192 counting
- * blocks above 128 as 128, block_size <= 256); num_seqs <= MOBA_MAX_SEQS
- * (varlen); at most 16384 blocks per sequence; tokens * heads < 2^27 per
- * call.
+ * blocks above 128 as 128, block_size <= 256); any number of sequences;
+ * at most 16384 blocks per sequence; tokens * heads < 2^27 per call.
  * Blocks of 256 / 512 keys: routing (centroids, scores, top-k) works on the
  * blocks as given; the attention calls attend a selected block as its 2 / 4
  * sub-blocks of 128 keys (the same key set, so the same result), with the
@@ -65,6 +70,7 @@ extern "C" {
 #endif
 
 #define MOBA_ABI_VERSION 2
+/* sequences per launch group (a call with more runs several groups) */
 #define MOBA_MAX_SEQS 64
 
 typedef enum {

@@ -61,6 +61,10 @@ CASES = {
     # 1094 key blocks: more than 1024, so the index pass takes chunks of 128
     # query blocks instead of 32
     "long-B64": _spec("C4", seq=70000, heads=1, top_k=8),
+    # 150 ragged sequences (some empty): more than one launch table holds,
+    # so the call runs as groups of 64 with one workspace region each
+    "many-seqs": _spec("H", seqlens=tuple((41 * i) % 300 for i in range(150)), heads=2,
+                       block_size=64, top_k=4),
     # fp32 inputs (the plain recompute path)
     "f32-C1": _spec("C1"),
     "f32-B128": _spec("H", seq=1500, heads=2, dtype="f32"),
@@ -168,6 +172,9 @@ CONV_CASES = {
     "W8-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 8),
     "f32-W4": (_spec("C1"), "plain", 4),
     "C3-full-W3": (dataclasses.replace(workloads.spec("C3"), plant=False), "plain", 3),
+    # 150 ragged sequences: dw sums every group's block partials in one pass
+    "many-seqs-W4": (_spec("H", seqlens=tuple((41 * i) % 300 for i in range(150)), heads=2,
+                           block_size=64, top_k=4), "plain", 4),
 }
 
 

@@ -84,10 +84,11 @@ def test_large_blocks_attend_as_128_key_blocks(lib):
     (dict(d=96), UNSUPPORTED), (dict(B=32), UNSUPPORTED), (dict(B=1024), UNSUPPORTED),
     (dict(B=256, K=9), UNSUPPORTED), (dict(dtype=0, B=512), UNSUPPORTED),
     (dict(K=0), INVALID), (dict(K=33), UNSUPPORTED), (dict(dtype=7), INVALID),
-    (dict(heads=0), INVALID), (dict(batch=65), UNSUPPORTED),
+    (dict(heads=0), INVALID),
     (dict(dtype=0, d=128, B=128), UNSUPPORTED),
     (dict(cu=[0, 10, 5]), INVALID), (dict(cu=[1, 10]), INVALID),
-    (dict(cu=list(range(0, 660, 10))), UNSUPPORTED),        # 65 sequences
+    (dict(cu=list(range(0, 2000, 10)) + [1990 + 16385 * 64], B=64), UNSUPPORTED),  # 16385 blocks in the last group
+    (dict(cu=list(range(0, 2000, 10)) + [1995, 1990]), INVALID),  # decreasing past group 0
     (dict(seq=1 << 26, heads=2), UNSUPPORTED),              # tokens x heads = 2^27
     (dict(seq=16384 * 64 + 1, B=64), UNSUPPORTED),          # 16385 blocks in a sequence
 ])
@@ -101,13 +102,59 @@ def test_bad_shapes_rejected_on_host(lib, kw, code):
 
 
 def test_largest_accepted_shapes(lib):
-    # 64 sequences (the most a varlen batch may hold), 16384 blocks in one
-    # sequence and 63 * 2^21 < 2^27 token-heads are accepted on the host
-    sh = _shape(cu=list(range(0, 650, 10)), B=64)
-    assert lib.moba_total_blocks(ctypes.byref(sh)) == 64
+    # 16384 blocks in one sequence and 63 * 2^21 < 2^27 token-heads are
+    # accepted on the host
     sh = _shape(seq=16384 * 128, heads=63, B=128, K=8)
     assert lib.moba_total_blocks(ctypes.byref(sh)) == 16384
     assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) > 0
+
+
+def _one_group_sums(lib, lens, B=64, K=4, heads=2, d=64):
+    """Workspace of a many-sequence call vs the calls of its groups of 64."""
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    sh = _shape(cu=cu, B=B, K=K, heads=heads, d=d)
+    parts = []
+    for g in range(0, len(lens), 64):
+        sub = lens[g:g + 64]
+        c = [0]
+        for L in sub:
+            c.append(c[-1] + L)
+        parts.append(_shape(cu=c, B=B, K=K, heads=heads, d=d))
+    return sh, parts
+
+
+@pytest.mark.parametrize("nseq", [64, 65, 200])
+def test_many_sequences_run_in_groups_of_64(lib, nseq):
+    """More varlen sequences than one launch table holds (MOBA_MAX_SEQS) are
+    accepted: the call runs them as groups of 64, so block counts add up, the
+    attention workspaces hold one region per group and the routing
+    workspace is the largest group's."""
+    lens = [(37 * i) % 300 for i in range(nseq)]
+    sh, parts = _one_group_sums(lib, lens)
+    nb = sum((L + 63) // 64 for L in lens)
+    assert lib.moba_total_blocks(ctypes.byref(sh)) == nb
+    for f in (lib.moba_attn_fwd_workspace_bytes, lib.moba_attn_bwd_workspace_bytes):
+        assert f(ctypes.byref(sh)) == sum(f(ctypes.byref(p)) for p in parts)
+    r = lib.moba_route_topk_workspace_bytes
+    assert r(ctypes.byref(sh)) == max(r(ctypes.byref(p)) for p in parts)
+    assert lib.moba_key_conv_bwd_workspace_bytes(ctypes.byref(sh), 3) >= nb * 2 * 64 * 3 * 4
+    # a uniform batch of more than 64 rows too
+    assert lib.moba_total_blocks(ctypes.byref(_shape(batch=130, seq=100, B=64))) == 260
+
+
+def test_many_sequence_attention_workspace_is_checked_whole(lib):
+    lens = [100] * 130
+    sh, parts = _one_group_sums(lib, lens)
+    need = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh))
+    p = ctypes.c_void_p(1 << 20)
+    assert lib.moba_attn_index(ctypes.byref(sh), p, p, need - 256, None) == WS_SMALL
+    assert lib.moba_attn_bwd(ctypes.byref(sh), p, p, p, p, ctypes.c_float(0.0), p, p, p,
+                             ctypes.c_void_p(2 << 20), ctypes.c_void_p(3 << 20),
+                             ctypes.c_void_p(4 << 20), p,
+                             lib.moba_attn_bwd_workspace_bytes(ctypes.byref(sh)) - 256,
+                             None) == WS_SMALL
 
 
 def test_route_workspace(lib):

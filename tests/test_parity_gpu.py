@@ -217,6 +217,8 @@ def _run_case(seqlens, H, d, B, K, dtype, seed, conv_w_width=0, scale=None, v_on
     gw = None if w is None else w.to(DEV)
     o, lse, idx, kk = moba().moba_fwd(gq, gk, gv, B, K, conv_w=gw, cu_seqlens=cu, scale=scale)
     torch.cuda.synchronize()
+    if conv_w_width:
+        assert np.array_equal(_np(kk), ref["k_conv"]), "k' differs from the oracle's"
     _verify_forward(o, lse, idx, ref, q, ref["k_conv"], v, B, K, cu, dtype,
                     f"edge {seqlens[:8]} B{B} K{K} {dtype}", scale=scale or 0.0)
     return o, lse, idx, ref
@@ -332,11 +334,22 @@ def test_route_all_scores_tied_in_the_first_blocks(K):
     ([640], 2, 64, 64, 32, "f32"),            # fp32, k > blocks
     ([1000], 1, 128, 64, 5, "f32"),           # fp32, d = 128, ragged
     ([4096], 1, 64, 64, 32, "bf16"),          # maximum k
-    ([(53 * i) % 257 for i in range(64)], 2, 64, 64, 4, "bf16"),  # 64 sequences (the maximum), ragged, one empty
+    ([(53 * i) % 257 for i in range(64)], 2, 64, 64, 4, "bf16"),  # 64 sequences (one launch table), one empty
+    ([(53 * i) % 257 for i in range(200)], 2, 64, 64, 4, "bf16"),  # 200 sequences: 4 groups of <= 64
+    ([(29 * i) % 150 for i in range(70)], 1, 128, 64, 3, "f32"),    # 70 sequences, fp32, d = 128
 ])
 def test_edge_cases(seqlens, H, d, B, K, dtype):
     print(f"[edge {seqlens} H{H} d{d} B{B} K{K} {dtype}]", flush=True)
     _run_case(seqlens, H, d, B, K, dtype, seed=sum(seqlens) + K)
+
+
+def test_many_sequences_with_key_conv():
+    """130 varlen sequences with the key conv: k', centroids, selection and
+    output of the whole forward equal the oracle's (the call runs as groups
+    of at most 64 sequences)."""
+    seqlens = [(71 * i) % 400 for i in range(130)]
+    print(f"[many seqs conv] {len(seqlens)} sequences", flush=True)
+    _run_case(seqlens, 2, 64, 64, 5, "bf16", seed=77, conv_w_width=3)
 
 
 def test_v_ones_gives_ones():
@@ -450,6 +463,55 @@ def test_full_size_sampled_long_context():
     gl = _np(lse).reshape(-1)[rows]
     _check_o(go, gl, ro, rl, "bf16", rows=True, what="L sampled")
     _assert_exact(drows, "L sampled")
+
+
+def test_longest_sequence_sampled():
+    """One sequence of 16384 blocks of 64 keys (the most a sequence may
+    hold; 1M tokens, one head, top-8): block ids take 14 key bits, the index
+    pass stages 16384 counters per workgroup, the backward takes the
+    placement for long lists.  Invariants on every row; selection, output
+    and the attention gradients (dq of sampled rows, dk / dv of sampled key
+    blocks) against the oracle's row and key-block subsets."""
+    B, K, d, H = 64, 8, 64, 1
+    T = 16384 * B
+    print(f"[longest sequence {T} tokens]", flush=True)
+    g = torch.Generator().manual_seed(16384)
+    q, k, v, do = (torch.randn((T, H, d), generator=g).to(torch.bfloat16) for _ in range(4))
+    cu = [0, T]
+    m = moba()
+    gq, gk, gv, gdo = (t.to(DEV) for t in (q, k, v, do))
+    o, lse, idx, _ = m.moba_fwd(gq, gk, gv, B, K, cu_seqlens=cu)
+    dq, dk, dv = m.moba_attn_bwd(gq, gk, gv, idx, o, lse, gdo, B, K, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    gi = idx.reshape(T, K)
+    own = (torch.arange(T, device=DEV) // B).to(torch.int32)[:, None]
+    assert torch.all((gi == own).any(-1))
+    full = (gi >= 0).all(-1)
+    assert torch.all(gi[full][:, 1:] > gi[full][:, :-1])
+    assert torch.all(torch.where(gi >= 0, gi, torch.zeros_like(gi)) <= own)
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.integers(0, T, 1000), T - 1 - np.arange(64)]))
+    cent = oracle.centroids(k, B, cu)
+    ri, ga, gb, ex = oracle.route_rows(q, cent, B, K, cu, rows)
+    gidx = idx.cpu().numpy().reshape(-1, K)
+    drows = _check_sel(gidx[rows], ri, ex, q, cent, B, K, cu, rows=rows, what="16384 blocks")
+    ro, rl = parity.outputs_on_gpu_selection(q, k, v, gidx.reshape(T, H, K), B, K, cu, rows)
+    _check_o(_np(o).reshape(-1, d)[rows], _np(lse).reshape(-1)[rows], ro, rl, "bf16", rows=True,
+             what="16384 blocks")
+    _assert_exact(drows, "16384 blocks")
+    # gradients on the GPU's own selection: dq of the sampled rows, dk / dv
+    # of sampled key blocks (block 0 holds the longest list)
+    qsel = np.zeros((T, H), bool)
+    qsel[rows, 0] = True
+    kb = np.zeros((16384, H), bool)
+    kb[[0, 1, 5000, 16382, 16383], 0] = True
+    rq, rk, rv = oracle.attend_bwd(q, k, v, gidx.reshape(T, H, K), do, B, K, cu, qsel=qsel,
+                                   kbsel=kb, nthreads=16)
+    from test_bwd_gpu import _check as _check_grad
+    _check_grad("16384 blocks", _np(dq).reshape(T, H, d)[rows], rq[rows], "dq")
+    keys = np.concatenate([np.arange(j * B, (j + 1) * B) for j in np.nonzero(kb[:, 0])[0]])
+    _check_grad("16384 blocks", _np(dk).reshape(T, H, d)[keys], rk[keys], "dk")
+    _check_grad("16384 blocks", _np(dv).reshape(T, H, d)[keys], rv[keys], "dv")
 
 
 def test_binding_rejects_wrong_buffers():
