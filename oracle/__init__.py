@@ -58,6 +58,9 @@ def _load():
         lib.moba_oracle_route_rows.argtypes = [_P, _P, _I, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P, _P]
         lib.moba_oracle_attend_rows.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _I, _P, _P]
         lib.moba_oracle_route_scores.argtypes = [_P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P]
+        lib.moba_oracle_attend_blasst.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _D,
+                                                  _P, _P, _D, _P, _P, _P, _I]
+        lib.moba_oracle_attend_blasst.restype = _I
         lib.moba_oracle_route_scores.restype = _I
         lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
                                                _P, _P, _P, _P, _P, _I]
@@ -188,6 +191,43 @@ def forward(q, k, v, B: int, K: int, cu, conv_w=None, conv_mode: int = 0,
     o, lse = attend(q, kk, v, idx, B, K, cu, scale, nthreads)
     return {"k_conv": kk, "cent": cent, "idx": idx, "gap_a": ga, "gap_b": gb,
             "exempt": ex, "o": o, "lse": lse}
+
+
+def attend_blasst(q, k, v, idx, B: int, K: int, cu, lam: float, scale: float = 0.0,
+                  keep=None, flip=None, tau: float = 1e-4, nthreads: Optional[int] = None):
+    """Step 5 with the BLASST block skip (blocks visited in ascending order,
+    own block last; a block whose maximum score is below the running maximum
+    of the attended scores + ln(lam) is skipped).  lam = 0 keeps every block.
+
+    keep (bool [T, H, K], optional) replaces the rule by an explicit choice
+    per idx slot.  flip (uint64 [T, H], optional) takes the near decisions
+    whose bit is set the other way.  Returns (o f64 [T,H,d], lse f64 [T,H],
+    near uint64 [T,H]): bit b of near marks a decision on the b-th visited
+    block within tau * max(1, |M|) of the threshold.
+    """
+    import math
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    T, H, d = q.shape
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, H, K)
+    c = _cu(cu)
+    o = np.empty((T, H, d), dtype=np.float64)
+    lse = np.empty((T, H), dtype=np.float64)
+    near = np.zeros((T, H), dtype=np.uint64)
+    kp = None
+    if keep is not None:
+        kp = np.ascontiguousarray(np.asarray(keep, dtype=np.uint8).reshape(T, H, K))
+    fl = None
+    if flip is not None:
+        fl = np.ascontiguousarray(np.asarray(flip, dtype=np.uint64).reshape(T, H))
+    ll = math.log(lam) if lam > 0 else -math.inf
+    rc = _load().moba_oracle_attend_blasst(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), H, d, B, K,
+                                           _ptr(c), len(c) - 1, float(scale), float(ll),
+                                           None if kp is None else _ptr(kp),
+                                           None if fl is None else _ptr(fl), float(tau),
+                                           _ptr(o), _ptr(lse), _ptr(near),
+                                           nthreads or default_threads())
+    assert rc == 0
+    return o, lse, near
 
 
 def route_rows(q, cent, B: int, K: int, cu, rows):

@@ -428,6 +428,145 @@ int moba_oracle_attend(const float *q, const float *k, const float *v,
 }
 
 /* =====================================================================
+ * Step 5, BLASST variant ("BLASST: Dynamic BLocked Attention Sparsity via
+ * Softmax Thresholding", section "Meccanismo di Pruning"): the query's
+ * blocks are visited in ascending order, as an online softmax visits its
+ * key blocks, with a running maximum M of the attended scores; a block
+ * whose own maximum m~ satisfies m~ - M < ln(lambda), 0 <= lambda <= 1, is
+ * skipped -- its keys take no part in the softmax.  The first block is
+ * never skipped.  Blocks: the listed past blocks (0 <= j < i, ascending, as in
+ * step 5), then the own block i with its causal keys u <= t.
+ *   log_lambda = -inf keeps every block (step 5 exactly).
+ *   keep (optional, uint8 [rows][K]): instead of the rule, block of slot p
+ *   is attended iff keep[row][p] != 0; the own block is slot p with
+ *   idx == i, or kept when no slot lists it.
+ *   near (optional, uint64 per row): bit b set where the decision on the
+ *   b-th visited block lies within tau * max(1, |M|) of the threshold (a
+ *   decision that a different rounding of the scores may take the other
+ *   way); flip (optional, uint64 per row): such near decisions whose bit is
+ *   set are taken the other way (the later ones still follow the rule).
+ * ===================================================================== */
+typedef struct {
+    attn_ctx a;
+    double log_lambda, tau;
+    const unsigned char *keep;
+    const unsigned long long *flip;
+    unsigned long long *near;
+} blasst_ctx;
+
+static void blasst_one(blasst_ctx *c, int s, int h, int tl, double *z, int *keys,
+                       int *kept, int *bstart, int *bslot)
+{
+    attn_ctx *a = &c->a;
+    int t0 = a->cu[s], L = a->cu[s + 1] - a->cu[s];
+    size_t t = (size_t)(t0 + tl);
+    size_t r = t * a->H + h;
+    int i = tl / a->B;
+    const int *row = a->idx + r * a->K;
+    /* blocks in visiting order with their key ranges in keys[] */
+    int nb = 0, nk = 0, own_slot = -1;
+    for (int p = 0; p < a->K; ++p) {
+        int j = row[p];
+        if (j == i) own_slot = p;
+        if (j < 0 || j >= i) continue;
+        bstart[nb] = nk;
+        bslot[nb++] = p;
+        for (int u = j * a->B; u < (j + 1) * a->B && u < L; ++u) keys[nk++] = u;
+    }
+    bstart[nb] = nk;
+    bslot[nb++] = own_slot;
+    for (int u = i * a->B; u <= tl; ++u) keys[nk++] = u;
+    bstart[nb] = nk;
+    const float *qv = a->q + r * a->d;
+    for (int e = 0; e < nk; ++e) {
+        const float *kv = a->k + ((size_t)(t0 + keys[e]) * a->H + h) * a->d;
+        double acc = 0.0;
+        for (int ch = 0; ch < a->d; ++ch) acc = acc + (double)qv[ch] * (double)kv[ch];
+        z[e] = a->scale * acc;
+    }
+    /* block maxima and the skip decisions, in visiting order */
+    double M = -INFINITY;
+    unsigned long long near = 0;
+    const unsigned long long flip = c->flip ? c->flip[r] : 0;
+    for (int b = 0; b < nb; ++b) {
+        double m = -INFINITY;
+        for (int e = bstart[b]; e < bstart[b + 1]; ++e) if (z[e] > m) m = z[e];
+        int kb;
+        if (c->keep) {
+            kb = bslot[b] < 0 ? 1 : c->keep[r * a->K + bslot[b]] != 0;
+        } else {
+            kb = 1;
+            if (M > -INFINITY && m - M < c->log_lambda) kb = 0;
+            if (M > -INFINITY && c->log_lambda > -INFINITY) {
+                double mx = fabs(M) > 1.0 ? fabs(M) : 1.0;
+                if (fabs(m - M - c->log_lambda) <= c->tau * mx) {
+                    near |= 1ull << b;
+                    if ((flip >> b) & 1ull) kb = !kb;
+                }
+            }
+        }
+        /* the running maximum is that of the attended scores */
+        if (kb && m > M) M = m;
+        kept[b] = kb;
+    }
+    if (c->near) c->near[r] = near;
+    /* softmax over the kept blocks' keys */
+    double Mk = -INFINITY;
+    for (int b = 0; b < nb; ++b) {
+        if (!kept[b]) continue;
+        for (int e = bstart[b]; e < bstart[b + 1]; ++e) if (z[e] > Mk) Mk = z[e];
+    }
+    double l = 0.0;
+    double *ov = a->o + r * a->d;
+    for (int ch = 0; ch < a->d; ++ch) ov[ch] = 0.0;
+    for (int b = 0; b < nb; ++b) {
+        if (!kept[b]) continue;
+        for (int e = bstart[b]; e < bstart[b + 1]; ++e) {
+            double p = exp(z[e] - Mk);
+            l += p;
+            const float *vv = a->v + ((size_t)(t0 + keys[e]) * a->H + h) * a->d;
+            for (int ch = 0; ch < a->d; ++ch) ov[ch] += p * (double)vv[ch];
+        }
+    }
+    for (int ch = 0; ch < a->d; ++ch) ov[ch] /= l;
+    if (a->lse) a->lse[r] = Mk + log(l);
+}
+
+static void blasst_job(void *vctx, int job)
+{
+    blasst_ctx *c = (blasst_ctx *)vctx;
+    int s = job / c->a.H, h = job % c->a.H;
+    int L = c->a.cu[s + 1] - c->a.cu[s];
+    int maxkeys = c->a.K * c->a.B + c->a.B;
+    double *z = (double *)malloc(sizeof(double) * (size_t)maxkeys);
+    int *keys = (int *)malloc(sizeof(int) * (size_t)maxkeys);
+    int *kept = (int *)malloc(sizeof(int) * (size_t)(c->a.K + 2));
+    int *bstart = (int *)malloc(sizeof(int) * (size_t)(c->a.K + 3));
+    int *bslot = (int *)malloc(sizeof(int) * (size_t)(c->a.K + 2));
+    for (int tl = 0; tl < L; ++tl) blasst_one(c, s, h, tl, z, keys, kept, bstart, bslot);
+    free(z);
+    free(keys);
+    free(kept);
+    free(bstart);
+    free(bslot);
+}
+
+int moba_oracle_attend_blasst(const float *q, const float *k, const float *v,
+                              const int *idx, int H, int d, int B, int K,
+                              const int *cu, int nseq, double scale, double log_lambda,
+                              const unsigned char *keep, const unsigned long long *flip,
+                              double tau, double *o, double *lse, unsigned long long *near,
+                              int nthreads)
+{
+    if (B < 1 || K < 1 || K > 63) return 1;
+    if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
+    blasst_ctx c = {{q, k, v, idx, o, lse, cu, H, d, B, K, scale}, log_lambda, tau, keep, flip,
+                    near};
+    run_jobs(blasst_job, &c, nseq * H, nthreads);
+    return 0;
+}
+
+/* =====================================================================
  * Row subsets (for sampled checks at sizes where the full oracle is too
  * slow): the same steps 3-4 / 5 for the listed (token, head) rows only.
  * rows[r] = token * H + head (global token index).  Outputs are written at

@@ -644,3 +644,113 @@ def test_conv_bwd_identity_filter_passes_gradient_through():
         for l in range(W):
             ref[:, :, l] += (g[a + l:b].astype(np.float64) * k[a:b - l]).sum(0)
     assert np.allclose(dw, ref, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- BLASST ----
+# "BLASST: Dynamic BLocked Attention Sparsity via Softmax Thresholding",
+# section "Meccanismo di Pruning": blocks visited in order with a running
+# maximum M; a block whose maximum m~ has m~ - M < ln(lambda) is skipped.
+def _blasst_case(seed, T=48, H=2, d=8, B=4, K=4):
+    q, k, v = (_bf16(_rand((T, H, d), seed + i)) for i in range(3))
+    cu = [0, 20, T]
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    return q, k, v, idx, cu, B, K
+
+
+def test_blasst_with_lambda_zero_is_plain_attention():
+    q, k, v, idx, cu, B, K = _blasst_case(60)
+    o, lse = oracle.attend(q, k, v, idx, B, K, cu)
+    ob, lb, near = oracle.attend_blasst(q, k, v, idx, B, K, cu, 0.0)
+    assert np.array_equal(o, ob) and np.array_equal(lse, lb) and not near.any()
+
+
+def test_blasst_keep_mask_matches_masked_sdpa():
+    """Explicit per-slot keep choices: the attention over the kept blocks
+    equals the library's SDPA with that boolean mask (fp64)."""
+    q, k, v, idx, cu, B, K = _blasst_case(61)
+    T, H, d = q.shape
+    g = np.random.default_rng(5)
+    keep = g.random(idx.shape) < 0.6
+    ob, lb, _ = oracle.attend_blasst(q, k, v, idx, B, K, cu, 0.0, keep=keep)
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        L = s1 - s0
+        for h in range(H):
+            m = np.zeros((L, L), bool)
+            for tl in range(L):
+                i = tl // B
+                row, kp = idx[s0 + tl, h], keep[s0 + tl, h]
+                own_kept = True
+                for p in range(K):
+                    j = row[p]
+                    if j == i:
+                        own_kept = bool(kp[p])
+                    elif 0 <= j < i and kp[p]:
+                        m[tl, j * B:min((j + 1) * B, L)] = True
+                if own_kept:
+                    m[tl, i * B:tl + 1] = True
+            qq, kk, vv = (torch.from_numpy(x[s0:s1, h]).double()[None] for x in (q, k, v))
+            ref = F.scaled_dot_product_attention(qq, kk, vv, attn_mask=torch.from_numpy(m)[None])
+            rows = m.any(1)
+            assert np.allclose(ob[s0:s1, h][rows], ref[0].numpy()[rows], atol=1e-12)
+
+
+def test_blasst_crafted_skips():
+    """One head, blocks of 2 keys, d = 2, q = (1, 0) and scale 1: a key's
+    score is its first coordinate.  Block maxima, in visiting order, are
+    1, 3, 2.5, 0.5 (past) and the own block's; with lambda = e^-1 a block is
+    skipped when its maximum is more than 1 below the running maximum."""
+    B, K = 2, 5
+    firsts = [[1.0, 0.0], [3.0, -1.0], [2.5, 2.0], [0.5, 0.0], [2.2, 9.0]]   # block 4 = own
+    T = 10
+    q = np.zeros((T, 1, 2), np.float32)
+    q[:, 0, 0] = 1.0
+    k = np.zeros((T, 1, 2), np.float32)
+    for j, (a, b) in enumerate(firsts):
+        k[2 * j, 0, 0], k[2 * j + 1, 0, 0] = a, b
+    v = _rand((T, 1, 2), 62)
+    idx = np.full((T, 1, K), -1, np.int32)
+    idx[8] = [[0, 1, 2, 3, 4]]                   # query t = 8 (own block 4, keys u <= 8)
+    idx[:8] = [[0, -1, -1, -1, -1]]
+    idx[9] = idx[8]
+    o, lse, near = oracle.attend_blasst(q, k, v, idx, B, K, [0, T], math.exp(-1.0), scale=1.0)
+    # t = 8: block 0 (max 1) kept, M = 1; block 1 (3) kept, M = 3; block 2
+    # (2.5) kept; block 3 (0.5 < 3 - 1) skipped; own block: key 8 only
+    # (score 2.2 >= 2) kept
+    keys = [0, 1, 2, 3, 4, 5, 8]
+    z = k[keys, 0, 0].astype(np.float64)
+    p = np.exp(z - z.max())
+    assert np.allclose(o[8, 0], (p[:, None] * v[keys, 0]).sum(0) / p.sum(), atol=1e-14)
+    assert abs(lse[8, 0] - (z.max() + math.log(p.sum()))) < 1e-14
+    # t = 9: own block keys 8, 9 (max 9) raise the maximum: still kept, block 3 still skipped
+    keys9 = keys + [9]
+    z9 = k[keys9, 0, 0].astype(np.float64)
+    p9 = np.exp(z9 - z9.max())
+    assert np.allclose(o[9, 0], (p9[:, None] * v[keys9, 0]).sum(0) / p9.sum(), atol=1e-14)
+    # a threshold exactly at a decision is flagged as near (block 3 is the
+    # 4th visited: bit 3), and the flipped decision keeps it
+    o2, _, near2 = oracle.attend_blasst(q, k, v, idx, B, K, [0, T], math.exp(-2.5), scale=1.0)
+    assert near2[8, 0] == 1 << 3 and near[8, 0] == 0      # block 3: 0.5 - 3 = -2.5
+    flip = np.zeros((T, 1), np.uint64)
+    flip[8, 0] = 1 << 3
+    o3, _, _ = oracle.attend_blasst(q, k, v, idx, B, K, [0, T], math.exp(-2.5), scale=1.0,
+                                    flip=flip)
+    kept = [keys, keys[:6] + [6, 7, 8]]
+    z3 = k[kept[1], 0, 0].astype(np.float64)
+    p3 = np.exp(z3 - z3.max())
+    ref2 = (p3[:, None] * v[kept[1], 0]).sum(0) / p3.sum()
+    # at exactly -2.5 the rule keeps block 3 (not below the threshold): the
+    # flip skips it
+    assert np.allclose(o2[8, 0], ref2, atol=1e-14) and np.allclose(o3[8, 0], o[8, 0], atol=1e-14)
+
+
+def test_blasst_first_block_kept_and_v_ones():
+    q, k, v, idx, cu, B, K = _blasst_case(63)
+    ones = np.ones_like(v)
+    for lam in (0.3, 0.9, 1.0):
+        o, lse, _ = oracle.attend_blasst(q, k, ones, idx, B, K, cu, lam)
+        assert np.allclose(o, 1.0, atol=1e-12)
+    # lambda = 1: every attended block after the first raises the running max
+    o1, l1, _ = oracle.attend_blasst(q, k, v, idx, B, K, cu, 1.0)
+    o0, l0 = oracle.attend(q, k, v, idx, B, K, cu)
+    assert not np.allclose(o1, o0)             # something was skipped
+    assert np.all(l1 <= l0 + 1e-12)            # dropping keys only lowers the LSE
