@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--pass", dest="which", default="fwd", choices=["fwd", "bwd"],
                     help="fwd (default): the forward pass; bwd: the attention "
                          "backward (moba_attn_bwd) for the forward's selection")
+    ap.add_argument("--blasst-lambda", type=float, default=None,
+                    help="time the forward with the BLASST block skip at this lambda "
+                         "(moba_attn_fwd_blasst as one stage after routing)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB first (a "
                          "known-size kernel for scaling HBM byte counters)")
@@ -168,6 +171,9 @@ def main():
     stream = torch.cuda.current_stream()
     names = (["conv_pool"] if w is not None else ["pool"]) + ["route", "index", "routed_attn",
                                                             "diag_combine"]
+    blasst = args.blasst_lambda is not None
+    if blasst:
+        names = names[:2] + ["attn_blasst"]
 
     def step(ev=None):
         def mark(i):
@@ -183,6 +189,11 @@ def main():
         mark(1)
         moba.moba_route_topk(q, cent, B, K, cu, out=idx, workspace=ws)
         mark(2)
+        if blasst:
+            moba.moba_attn_fwd_blasst(q, kk, v, idx, B, K, args.blasst_lambda, cu_seqlens=cu,
+                                      workspace=ws, out=o)
+            mark(3)
+            return
         moba.moba_attn_index(idx, q, B, K, ws, cu)
         mark(3)
         moba.moba_attn_routed(q, kk, v, B, K, ws, None, cu)
@@ -197,27 +208,31 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: whole steps, bracketed by syncs
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    nev = len(names) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    ms_steps = [e[0].elapsed_time(e[5]) for e in evs]
+    ms_steps = [e[0].elapsed_time(e[nev - 1]) for e in evs]
     ms_step = wall * 1e3 / args.steps
     stage_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps
                 for j, n in enumerate(names)}
 
     fl = workloads.eff_flops(spec)
     value = fl["total"] / (ms_step * 1e-3) / 1e12
-    routed_ms = stage_ms["routed_attn"]
-    routed_tflops = fl["routed"] / (routed_ms * 1e-3) / 1e12
+    routed_ms = stage_ms["attn_blasst" if blasst else "routed_attn"]
+    routed_flops = fl["total"] if blasst else fl["routed"]
+    routed_tflops = routed_flops / (routed_ms * 1e-3) / 1e12
     pairs = workloads.routed_pairs(spec)
-    traffic = _traffic(pairs) if args.config == "H" else None
+    traffic = _traffic(pairs) if args.config == "H" and not blasst else None
     # the routing stages against the HBM roofline: algorithmic bytes (every
     # tensor moved once) over the event-timed stage time
     rbytes = workloads.routing_bytes(spec)
+    if blasst:
+        rbytes.pop("index")
     routing = {}
     for n, b in rbytes.items():
         t = stage_ms[n] * 1e-3
@@ -238,7 +253,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. N(0,1) q/k/v, CPU torch.Generator)",
-        "config": {"workload": f"moba_fwd {spec.name}: {spec.desc}",
+        "config": {"workload": f"moba_fwd {spec.name}: {spec.desc}"
+                               + (f", BLASST lambda={args.blasst_lambda}" if blasst else ""),
                    "batch": spec.batch, "seq_len": spec.seq, "heads": spec.heads,
                    "head_dim": spec.head_dim, "block_size": B, "top_k": K,
                    "key_conv_width": spec.conv_width, "key_conv_mode": spec.conv_mode,
@@ -251,14 +267,15 @@ def main():
         "event_ms_min": round(min(ms_steps), 4),
         "event_ms_max": round(max(ms_steps), 4),
         "roofline": {
-            "kernel": "routed_attn_kernel (moba_attn_routed)",
+            "kernel": ("moba_attn_fwd_blasst (index + routed + own block and merge)" if blasst
+                       else "routed_attn_kernel (moba_attn_routed)"),
             "bound": "mfma",
             "achieved": round(routed_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(routed_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "algorithmic_flops_per_launch": fl["routed"],
+            "algorithmic_flops_per_launch": routed_flops,
             "avg_launch_ms": round(routed_ms, 4),
             # the kernel is bound by its HBM traffic in practice: the same
             # bytes over the same time

@@ -31,7 +31,7 @@ import torch
 
 __all__ = [
     "moba_key_conv", "moba_centroids", "moba_route_topk", "moba_route_topk_noalloc",
-    "moba_attn_fwd",
+    "moba_attn_fwd", "moba_attn_fwd_blasst",
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd", "fwd",
     "moba_attn_fwd_workspace_bytes", "moba_route_topk_workspace_bytes", "moba_total_blocks",
     "library_path",
@@ -84,6 +84,7 @@ def _load():
         "moba_route_topk": [SH, P, P, P, P, SZ, P],
         "moba_route_topk_noalloc": [SH, P, P, P, P],
         "moba_attn_fwd": [SH, P, P, P, P, F32, P, P, P, SZ, P],
+        "moba_attn_fwd_blasst": [SH, P, P, P, P, F32, F32, P, P, P, SZ, P],
         "moba_attn_index": [SH, P, P, SZ, P],
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
         "moba_attn_combine": [SH, P, P, P, P, F32, P, P, P, SZ, P],
@@ -418,9 +419,12 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                   block_size: int, top_k: int, scale: Optional[float] = None,
                   cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
                   return_lse: bool = True, out: Optional[torch.Tensor] = None,
-                  stream=None):
+                  blasst_lambda: Optional[float] = None, stream=None):
     """Attention over the listed blocks + the causal own block.
 
+    blasst_lambda (0..1): skip, per query, the selected blocks whose
+    maximum score is below the running maximum + ln(lambda) (BLASST, blocks
+    in ascending order, the own block last; moba_attn_fwd_blasst).
     Returns (o, lse) with lse fp32 [..., heads] (None if not requested).
     """
     _qkv(q, k, v)
@@ -431,6 +435,13 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     _like(out, q, "out")
     lse = torch.empty(_rows(q), dtype=torch.float32, device=q.device) if return_lse else None
     workspace = _workspace(q, block_size, top_k, cu_seqlens, workspace)
+    if blasst_lambda is not None:
+        rc = _load().moba_attn_fwd_blasst(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
+                                          float(scale or 0.0), float(blasst_lambda), _p(out),
+                                          _p(lse), _p(workspace), workspace.numel(),
+                                          _stream(stream))
+        _check(rc, "moba_attn_fwd_blasst")
+        return out, lse
     rc = _load().moba_attn_fwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
                                float(scale or 0.0), _p(out), _p(lse), _p(workspace),
                                workspace.numel(), _stream(stream))
@@ -438,12 +449,20 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     return out, lse
 
 
+def moba_attn_fwd_blasst(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                         block_size: int, top_k: int, blasst_lambda: float, **kw):
+    """moba_attn_fwd with the BLASST block skip (see moba_attn_fwd)."""
+    return moba_attn_fwd(q, k, v, idx, block_size, top_k, blasst_lambda=blasst_lambda, **kw)
+
+
 @_on_stream
 def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int, top_k: int,
              conv_w: Optional[torch.Tensor] = None, conv_mode: str = "plain",
              cu_seqlens=None, scale: Optional[float] = None,
-             workspace: Optional[torch.Tensor] = None, stream=None):
-    """The whole MoBA forward: [key conv] -> centroids -> route -> attention.
+             workspace: Optional[torch.Tensor] = None, blasst_lambda: Optional[float] = None,
+             stream=None):
+    """The whole MoBA forward: [key conv] -> centroids -> route -> attention
+    (with the BLASST block skip when blasst_lambda is given).
 
     Returns (o, lse, idx, k_used) where k_used is k' when a conv ran.  With
     ``stream`` every step runs (and every buffer is allocated) on it.
@@ -459,7 +478,8 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
                    moba_route_topk_workspace_bytes(q, block_size, top_k, cu_seqlens), 256)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens, workspace=workspace)
-    o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
+    o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace,
+                           blasst_lambda=blasst_lambda)
     return o, lse, idx, kk
 
 

@@ -32,7 +32,10 @@
 // path); bf16 rounds P to bf16 for the PV product and normalises by the sum
 // of the rounded weights, so each output row is a convex combination of V
 // rows with the weights used (fp32 accumulation); the log-sum-exp uses the
-// unrounded fp32 weights.
+// unrounded fp32 weights.  Normalisations multiply by the hardware
+// reciprocal (1 ulp: far below the bf16 rounding that follows; x * rcp(x)
+// stays within 2^-23 of 1, so V = 1 still gives exactly 1).
+#include <math.h>
 #include <type_traits>
 
 #include "moba_internal.h"
@@ -409,7 +412,8 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void routed_attn_kernel(
     SegTable st, const Item* __restrict__ items, const uint32_t* __restrict__ entries,
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float sl2,
-    T* __restrict__ po, float* __restrict__ pl, int64_t nitems, int64_t per_xcd)
+    T* __restrict__ po, float* __restrict__ pl, float* __restrict__ pm, int64_t nitems,
+    int64_t per_xcd)
 {
     __shared__ __align__(16) Smem<T, D, BLK> sm;
     // bf16: entries are read from global memory (L2) a tile ahead instead of
@@ -534,7 +538,7 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
         for (int sb = 0; sb < 2; ++sb) {
             const int row0 = base + 16 * sb;                  // first row of the sub-tile
             if (row0 >= it.count) continue;                   // wave-uniform
-            const float inv = 1.0f / wt.used_sum(sb, sum[sb]);
+            const float inv = __builtin_amdgcn_rcpf(wt.used_sum(sb, sum[sb]));
             const size_t prow = (size_t)(e0 + row0 + l16);
             float x[NDT][4];
 #pragma unroll
@@ -573,6 +577,8 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
                 const float lv = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
                 if constexpr (STAGE) __builtin_nontemporal_store(lv, pl + prow);
                 else pl[prow] = lv;
+                // the block's maximum score (log2 units), for the BLASST skip
+                if (pm) pm[prow] = m2[sb];
             }
         }
     }
@@ -590,7 +596,8 @@ template <typename T, int D, int BLK>
 __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void diag_combine_kernel(
     SegTable st, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
-    float sl2, T* __restrict__ o, float* __restrict__ lse)
+    const float* __restrict__ pm, float log2lam, float sl2, T* __restrict__ o,
+    float* __restrict__ lse)
 {
     // bf16 d = 128: V^T is loaded over K once the scores are done, so the
     // stage takes half the LDS and 3 workgroups fit a CU (2 otherwise)
@@ -598,6 +605,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
     using SM = std::conditional_t<ONE, SmemOne<T, D, BLK>, Smem<T, D, BLK>>;
     __shared__ __align__(16) SM sm;
     __shared__ float own_lse[BLK];
+    __shared__ float own_max[BLK];            // BLASST: own block's maximum (log2 units)
     constexpr int NDT = D / 16;
     constexpr int CH = 16 / sizeof(T);        // elements per 16-byte chunk
     constexpr int NCH = D / CH;               // chunks per row
@@ -653,14 +661,17 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int r = 32 * wave + 16 * sb + l16;
-            const float inv = 1.0f / wt.used_sum(sb, sum[sb]);
+            const float inv = __builtin_amdgcn_rcpf(wt.used_sum(sb, sum[sb]));
             float x[NDT][4];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) x[dt][r4] = wt.o[sb][dt][r4] * inv;
             store_lane_row<T, NDT>(own + r * D + g4 * (D / 4), x);
-            if (g4 == 0) own_lse[r] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+            if (g4 == 0) {
+                own_lse[r] = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
+                own_max[r] = m2[sb];
+            }
         }
     }
     __syncthreads();
@@ -682,16 +693,43 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
                 for (int e = 0; e < 4; ++e) acc[e] = __uint_as_float(w[e]);
             }
         }
-        float M = own_lse[r];
-        float wsum = 1.0f;
         // the query's K list positions (-1: nothing routed in that slot)
         const int32_t* rrow = rev + ((size_t)h * st.cu[st.nseq] + t0 + i * BLK + r) * K;
         const int64_t eb = st.ebase[s] + (int64_t)h * L * K;
         const int kmerge = K > 1 ? K : 0;      // K == 1: no routed partials exist
+        // BLASST ("BLASST", summary page, "Meccanismo di Pruning"): blocks in
+        // ascending order (the slot order), the own block last; a block whose
+        // maximum is more than -log2(lambda) below the running maximum of the
+        // kept blocks takes no part.  Without it every slot is kept.
+        uint32_t keepm = 0xffffffffu;
+        bool own_kept = true;
+        if (pm) {
+            float Mr = -INFINITY;
+            keepm = 0u;
+            for (int p = 0; p < kmerge; ++p) {
+                const int ps = rrow[p];
+                if (ps < 0) continue;
+                const float mt = pm[eb + ps];
+                if (!(Mr > -INFINITY && mt - Mr < log2lam)) {
+                    keepm |= 1u << p;
+                    Mr = fmaxf(Mr, mt);
+                }
+            }
+            own_kept = !(Mr > -INFINITY && own_max[r] - Mr < log2lam);
+        }
+        float M = own_lse[r];
+        float wsum = 1.0f;
+        if (!own_kept) {
+            M = -INFINITY;
+            wsum = 0.f;
+#pragma unroll
+            for (int e = 0; e < CH; ++e) acc[e] = 0.f;
+        }
         for (int p0 = 0; p0 < kmerge; p0 += PF) {
             int pos[PF];
 #pragma unroll
-            for (int u = 0; u < PF; ++u) pos[u] = (p0 + u < kmerge) ? rrow[p0 + u] : -1;
+            for (int u = 0; u < PF; ++u)
+                pos[u] = (p0 + u < kmerge && ((keepm >> (p0 + u)) & 1u)) ? rrow[p0 + u] : -1;
             float lp[PF];
             u32x4_t xv[PF];
 #pragma unroll
@@ -728,7 +766,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         }
         // stored position c*CH + e holds dim 16*dt + 4*gg + r4 with
         // gg = pos / (D/4), dt = (pos % (D/4)) / 4: runs of 4 consecutive dims
-        const float winv = 1.0f / wsum;
+        const float winv = __builtin_amdgcn_rcpf(wsum);
 #pragma unroll
         for (int e4 = 0; e4 < CH / 4; ++e4) {
             const int pos = c * CH + 4 * e4;
@@ -744,7 +782,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
 
 template <typename T, int D, int BLK>
 hipError_t routed_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, const void* k,
-                    const void* v, float sl2)
+                    const void* v, float sl2, bool block_max)
 {
     const int64_t nitems = L.st.total_items;
     if (nitems == 0) return hipSuccess;
@@ -753,20 +791,24 @@ hipError_t routed_t(const Launch& L, const WsLayout& ws, char* wsp, const void* 
     hipLaunchKernelGGL((routed_attn_kernel<T, D, BLK>), dim3((unsigned)grid), dim3(64 * kRoutedWaves), 0, L.stream,
                        L.st, (const Item*)(wsp + ws.items_off), (const uint32_t*)(wsp + ws.ent_off),
                        (const T*)q, (const T*)k, (const T*)v, sl2, (T*)(wsp + ws.po_off),
-                       (float*)(wsp + ws.pl_off), nitems, per_xcd);
+                       (float*)(wsp + ws.pl_off), block_max ? (float*)(wsp + ws.pm_off) : nullptr,
+                       nitems, per_xcd);
     return hipGetLastError();
 }
 
 template <typename T, int D, int BLK>
 hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, const void* k,
-                  const void* v, const int32_t* idx, float sl2, void* o, float* lse)
+                  const void* v, const int32_t* idx, float sl2, void* o, float* lse,
+                  float blasst_lambda)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
     (void)idx;   // the index pass turned idx into the reverse map
     hipLaunchKernelGGL((diag_combine_kernel<T, D, BLK>), dim3(L.st.total_blocks, L.st.H),
                        dim3(2 * BLK), 0, L.stream, L.st, (const T*)q, (const T*)k, (const T*)v,
                        (const int32_t*)(wsp + ws.rev_off), (const T*)(wsp + ws.po_off),
-                       (const float*)(wsp + ws.pl_off), sl2, (T*)o, lse);
+                       (const float*)(wsp + ws.pl_off),
+                       blasst_lambda > 0.f ? (const float*)(wsp + ws.pm_off) : nullptr,
+                       blasst_lambda > 0.f ? log2f(blasst_lambda) : 0.f, sl2, (T*)o, lse);
     return hipGetLastError();
 }
 
@@ -789,19 +831,19 @@ hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
     } while (0)
 
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
-                              const void* k, const void* v, float scale)
+                              const void* k, const void* v, float scale, bool block_max)
 {
     if (L.st.K <= 1) return hipSuccess;
     const float sl2 = scale * 1.4426950408889634f;
-    MOBA_DISPATCH(routed_t, L, ws, wsp, q, k, v, sl2);
+    MOBA_DISPATCH(routed_t, L, ws, wsp, q, k, v, sl2, block_max);
 }
 
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                                const void* k, const void* v, const int32_t* idx, float scale,
-                               void* o, float* lse)
+                               void* o, float* lse, float blasst_lambda)
 {
     const float sl2 = scale * 1.4426950408889634f;
-    MOBA_DISPATCH(diag_t, L, ws, wsp, q, k, v, idx, sl2, o, lse);
+    MOBA_DISPATCH(diag_t, L, ws, wsp, q, k, v, idx, sl2, o, lse, blasst_lambda);
 }
 
 }  // namespace moba

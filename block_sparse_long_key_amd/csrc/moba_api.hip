@@ -122,6 +122,7 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
             // partials are indexed like the entries (list order)
             w.po_bytes = (size_t)st.ebase[st.nseq] * L.D * esz;
             w.pl_bytes = (size_t)st.ebase[st.nseq] * 4;
+            w.pm_bytes = (size_t)st.ebase[st.nseq] * 4;
         }
     }
     if (bwd) {
@@ -137,6 +138,7 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
     w.rev_off = off;   off += align256(w.rev_bytes);
     w.po_off = off;    off += align256(w.po_bytes);
     w.pl_off = off;    off += align256(w.pl_bytes);
+    w.pm_off = off;    off += align256(w.pm_bytes);
     w.lst_off = off;   off += align256(w.lst_bytes);
     w.rs_off = off;    off += align256(w.rs_bytes);
     w.pq_off = off;    off += align256(w.pq_bytes);
@@ -464,6 +466,29 @@ moba_status attn_fwd_one(const moba_shape* shape, const void* q, const void* k, 
                              workspace_bytes, stream);
 }
 
+moba_status attn_fwd_blasst_one(const moba_shape* shape, const void* q, const void* k, const void* v,
+                                const int32_t* idx, float softmax_scale, float blasst_lambda, void* o,
+                                float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    Launch Ll, L;
+    moba_status st = attn_launch(shape, stream, &Ll, &L);
+    if (st != MOBA_OK) return st;
+    if (!(blasst_lambda >= 0.f && blasst_lambda <= 1.f)) return MOBA_ERR_INVALID_ARG;
+    if (expands(Ll)) return MOBA_ERR_UNSUPPORTED;
+    if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !idx_ok(idx) || !ptr_ok(o)) return MOBA_ERR_INVALID_ARG;
+    if (lse && ((uintptr_t)lse & 3u)) return MOBA_ERR_INVALID_ARG;
+    WsLayout ws;
+    st = check_ws(L, workspace, workspace_bytes, &ws, false, false);
+    if (st != MOBA_OK) return st;
+    if (L.tokens == 0) return MOBA_OK;
+    char* wsp = (char*)workspace;
+    const float scale = resolve_scale(softmax_scale, L.D);
+    hipError_t e = run_index(Ll, L, ws, wsp, idx);
+    if (e == hipSuccess) e = launch_routed_attn(L, ws, wsp, q, k, v, scale, blasst_lambda > 0.f);
+    if (e == hipSuccess) e = launch_diag_combine(L, ws, wsp, q, k, v, idx, scale, o, lse, blasst_lambda);
+    return hip_status(e);
+}
+
 moba_status attn_bwd_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                           const int32_t* idx, float softmax_scale, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace,
@@ -772,6 +797,30 @@ moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k,
     if (st != MOBA_OK) return st;
     return moba_attn_combine(shape, q, k, v, idx, softmax_scale, o, lse, workspace,
                              workspace_bytes, stream);
+}
+
+moba_status moba_attn_fwd_blasst(const moba_shape* shape, const void* q, const void* k, const void* v,
+                                 const int32_t* idx, float softmax_scale, float blasst_lambda, void* o,
+                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    MOBA_GROUPS(shape);
+    if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
+    MOBA_ATTN_GROUPS(false);
+    const size_t er = row * esize(shape);
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const size_t wsz = one::attn_fwd_workspace_bytes_one(&gr.sh);
+        moba_status st = one::attn_fwd_blasst_one(&gr.sh, at(q, gr.tok0, er), at(k, gr.tok0, er),
+                                                  at(v, gr.tok0, er), at(idx, gr.tok0, irow), softmax_scale,
+                                                  blasst_lambda, at(o, gr.tok0, er), at(lse, gr.tok0, lrow),
+                                                  at(workspace, (int64_t)wsoff, 1),
+                                                  G.n > 1 ? wsz : workspace_bytes, stream);
+        if (st != MOBA_OK) return st;
+        wsoff += wsz;
+    }
+    return MOBA_OK;
 }
 
 moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,

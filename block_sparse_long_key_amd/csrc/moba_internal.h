@@ -133,6 +133,7 @@ struct WsLayout {
     size_t rev_off, rev_bytes;       // int32 [H][tokens][K]: list position of (t, slot), -1 if none
     size_t po_off, po_bytes;         // partial o rows, list order (I/O dtype, D per row)
     size_t pl_off, pl_bytes;         // partial lse, list order, fp32 (log2 units)
+    size_t pm_off, pm_bytes;         // partial block maximum, list order, fp32 (log2 units; BLASST)
     size_t lst_off, lst_bytes;       // int2 [H][total blocks]: (first entry, count) of each list
     size_t rs_off, rs_bytes;         // backward: float2 [tokens][H] (lse in log2 units, dO . O)
     size_t pq_off, pq_bytes;         // backward: fp32 dq pieces, list order, then own-block rows
@@ -175,7 +176,8 @@ hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int3
                       bool det = false);
 hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
-                              const void* q, const void* k, const void* v, float scale);
+                              const void* q, const void* k, const void* v, float scale,
+                              bool block_max = false);
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                            const void* k, const void* v, const void* o, const float* lse,
                            const void* dout, float scale, void* dq, void* dk, void* dv);
@@ -184,8 +186,11 @@ hipError_t launch_attn_bwd_f32(const Launch& L, const WsLayout& ws, char* wsp, c
                                const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, float scale, void* dq, void* dk,
                                void* dv);
+// blasst_lambda > 0: the BLASST skip over the partials' block maxima
+// (which the routed pass must have stored, block_max = true)
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp,
                                const void* q, const void* k, const void* v,
-                               const int32_t* idx, float scale, void* o, float* lse);
+                               const int32_t* idx, float scale, void* o, float* lse,
+                               float blasst_lambda = 0.f);
 
 }  // namespace moba

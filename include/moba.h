@@ -231,6 +231,33 @@ moba_status moba_attn_fwd(const moba_shape *shape, const void *q,
                           void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
+/*
+ * moba_attn_fwd_blasst -- moba_attn_fwd with the BLASST block skip ("BLASST:
+ * Dynamic BLocked Attention Sparsity via Softmax Thresholding", section
+ * "Meccanismo di Pruning") applied to each query's selected blocks: the
+ * blocks are visited in ascending order, the own block last, keeping a
+ * running maximum M of the kept blocks' scores; a block whose maximum
+ * score m satisfies m - M < ln(blasst_lambda) is skipped (its keys take no
+ * part in the softmax).  The first block is always kept.
+ *   blasst_lambda in [0, 1] (else MOBA_ERR_INVALID_ARG); 0 keeps every
+ *   block (moba_attn_fwd's result).  o and lse are those of the softmax
+ *   over the kept blocks' keys.  Block sizes 64 and 128 (larger ones:
+ *   MOBA_ERR_UNSUPPORTED).  Block maxima are taken from the fp32 scores;
+ *   a decision within rounding of the threshold may go either way.
+ *   The key-block-major order computes every selected (query, block) pair
+ *   before any query's running maximum is known, so the skip is decided in
+ *   the merge of the per-block partials: it saves the merge's reads of the
+ *   skipped partials, not their computation.
+ *   Same workspace (moba_attn_fwd_workspace_bytes), other arguments and
+ *   errors as moba_attn_fwd.
+ */
+moba_status moba_attn_fwd_blasst(const moba_shape *shape, const void *q,
+                                 const void *k, const void *v,
+                                 const int32_t *idx, float softmax_scale,
+                                 float blasst_lambda, void *o, float *lse,
+                                 void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
 /* The three stages of moba_attn_fwd, in order, for stage timing: the
  * index inversion, the routed (past-block) attention, and the own-block
  * attention plus merge.  Running them in order on one stream with one
