@@ -529,7 +529,9 @@ extern "C" {
 
 int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
 
-const char* moba_status_string(moba_status s)
+// (an int: a C caller may pass any value, which a C++ enum parameter of
+// this range could not hold without undefined behaviour)
+const char* moba_status_string(int32_t s)
 {
     switch (s) {
         case MOBA_OK: return "ok";

@@ -318,7 +318,9 @@ size_t moba_attn_fwd_workspace_bytes(const moba_shape *shape);
 /* Total number of blocks (centroid rows) of `shape`; -1 on invalid shape. */
 int64_t moba_total_blocks(const moba_shape *shape);
 
-const char *moba_status_string(moba_status status);
+/* Text of a status value; any int is accepted ("unknown status" outside
+ * the enum).  The returned string is static. */
+const char *moba_status_string(int32_t status);
 int32_t moba_abi_version(void);
 
 #ifdef __cplusplus

@@ -579,6 +579,9 @@ static int seq_of_token(const int *cu, int nseq, int t)
     return s;
 }
 
+/* Steps 3-4 for the listed rows only (row = token * H + head).  idx,
+ * gap_a, gap_b and exempt are full-size ([tokens * H] rows) and only the
+ * listed rows are written. */
 int moba_oracle_route_rows(const float *q, const float *cent, int H, int d, int B,
                            int K, const int *cu, int nseq, const long long *rows,
                            int nrows, int *idx, double *gap_a, double *gap_b,
@@ -632,6 +635,8 @@ int moba_oracle_route_scores(const float *q, const float *cent, int H, int d, in
     return 0;
 }
 
+/* Step 5 for the listed rows only: idx, o and lse are full-size ([tokens *
+ * H] rows); only the listed rows of o and lse are written. */
 int moba_oracle_attend_rows(const float *q, const float *k, const float *v,
                             const int *idx, int H, int d, int B, int K,
                             const int *cu, int nseq, double scale,
