@@ -27,7 +27,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 4;          // channels per thread
-constexpr int kMaxW = 8;
 
 template <typename T> struct Row4;
 template <> struct Row4<float> {
@@ -62,9 +61,11 @@ __device__ __forceinline__ float silu_grad(float u)
     return sg * (1.0f + u * (1.0f - sg));
 }
 
-template <typename T, int MODE>
+// WK: the filter width, a compile-time constant (windows of WK registers,
+// exactly WK fmas per tap loop, no per-tap selects)
+template <typename T, int MODE, int WK>
 __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
-    SegTable st, int HD, const T* __restrict__ k, const float* __restrict__ w, int W,
+    SegTable st, int HD, const T* __restrict__ k, const float* __restrict__ w,
     const T* __restrict__ gk, T* __restrict__ dk, float* __restrict__ dwp)
 {
     const int gb = blockIdx.x;
@@ -77,19 +78,19 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
     const int ch = (blockIdx.y * kThreads + threadIdx.x) * kVec;
     if (ch >= HD) return;
 
-    float wr[kVec][kMaxW];
+    float wr[kVec][WK];
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int l = 0; l < kMaxW; ++l) wr[v][l] = l < W ? w[(size_t)(ch + v) * W + l] : 0.f;
+        for (int l = 0; l < WK; ++l) wr[v][l] = w[(size_t)(ch + v) * WK + l];
 
     // u_tau from direct loads (halo tokens only)
     auto conv_at = [&](int tau, float (&u)[kVec]) {
 #pragma unroll
         for (int v = 0; v < kVec; ++v) u[v] = 0.f;
 #pragma unroll
-        for (int m = kMaxW - 1; m >= 0; --m) {
-            if (m < W && tau - m >= 0) {
+        for (int m = WK - 1; m >= 0; --m) {
+            if (tau - m >= 0) {
                 float x[4];
                 Row4<T>::load(k + (t0 + tau - m) * HD + ch, x);
 #pragma unroll
@@ -101,15 +102,15 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
     // ewin[v][l] = e_{t+l} once e_t is shifted in, so before the first
     // (last-in-sequence-order) token ewin[v][m] holds e_{b+m}: the halo,
     // zero past the sequence end
-    float ewin[kVec][kMaxW];
+    float ewin[kVec][WK];
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int l = 0; l < kMaxW; ++l) ewin[v][l] = 0.f;
+        for (int l = 0; l < WK; ++l) ewin[v][l] = 0.f;
 #pragma unroll
-    for (int l = 1; l < kMaxW; ++l) {
+    for (int l = 1; l < WK; ++l) {
         const int tau = b - 1 + l;
-        if (l < W && tau < L) {
+        if (tau < L) {
             float gx[4];
             Row4<T>::load(gk + (t0 + tau) * HD + ch, gx);
             if constexpr (MODE == 1) {
@@ -123,15 +124,15 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
         }
     }
     // kwin[v][m] = k_{t-m} (zero before the sequence start)
-    float kwin[kVec][kMaxW];
+    float kwin[kVec][WK];
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int m = 0; m < kMaxW; ++m) kwin[v][m] = 0.f;
+        for (int m = 0; m < WK; ++m) kwin[v][m] = 0.f;
 #pragma unroll
-    for (int m = 0; m < kMaxW; ++m) {
+    for (int m = 0; m < WK; ++m) {
         const int tau = b - 1 - m;
-        if (m < W && tau >= 0) {
+        if (tau >= 0) {
             float x[4];
             Row4<T>::load(k + (t0 + tau) * HD + ch, x);
 #pragma unroll
@@ -139,11 +140,11 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
         }
     }
 
-    float dwa[kVec][kMaxW];
+    float dwa[kVec][WK];
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int l = 0; l < kMaxW; ++l) dwa[v][l] = 0.f;
+        for (int l = 0; l < WK; ++l) dwa[v][l] = 0.f;
 
 #pragma unroll 4
     for (int t = b - 1; t >= a; --t) {
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
         Row4<T>::load(gk + row, gx);
         // the k row that enters the window for the next (earlier) token
         float knext[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t - W >= 0) Row4<T>::load(k + (t0 + t - W) * HD + ch, knext);
+        if (t - WK >= 0) Row4<T>::load(k + (t0 + t - WK) * HD + ch, knext);
         float out[4];
 #pragma unroll
         for (int v = 0; v < kVec; ++v) {
@@ -160,37 +161,33 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
             if constexpr (MODE == 1) {
                 float u = 0.f;
 #pragma unroll
-                for (int m = kMaxW - 1; m >= 0; --m)
-                    if (m < W) u = __builtin_fmaf(wr[v][m], kwin[v][m], u);
+                for (int m = WK - 1; m >= 0; --m)
+                    u = __builtin_fmaf(wr[v][m], kwin[v][m], u);
                 e *= silu_grad(u);
             }
 #pragma unroll
-            for (int l = kMaxW - 1; l >= 1; --l) ewin[v][l] = ewin[v][l - 1];
+            for (int l = WK - 1; l >= 1; --l) ewin[v][l] = ewin[v][l - 1];
             ewin[v][0] = e;
             float acc = MODE == 1 ? gx[v] : 0.f;
 #pragma unroll
-            for (int l = 0; l < kMaxW; ++l)
-                if (l < W) acc = __builtin_fmaf(wr[v][l], ewin[v][l], acc);
+            for (int l = 0; l < WK; ++l)
+                acc = __builtin_fmaf(wr[v][l], ewin[v][l], acc);
             out[v] = acc;
 #pragma unroll
-            for (int l = 0; l < kMaxW; ++l)
-                if (l < W) dwa[v][l] = __builtin_fmaf(e, kwin[v][l], dwa[v][l]);
+            for (int l = 0; l < WK; ++l)
+                dwa[v][l] = __builtin_fmaf(e, kwin[v][l], dwa[v][l]);
 #pragma unroll
-            for (int m = 0; m < kMaxW - 1; ++m) kwin[v][m] = kwin[v][m + 1];
-            kwin[v][kMaxW - 1] = 0.f;
+            for (int m = 0; m < WK - 1; ++m) kwin[v][m] = kwin[v][m + 1];
             // the entering row is k_{t-W}, at index W-1 after the shift
-#pragma unroll
-            for (int m = 0; m < kMaxW; ++m)
-                if (m == W - 1) kwin[v][m] = knext[v];
+            kwin[v][WK - 1] = knext[v];
         }
         Row4<T>::store(dk + row, out);
     }
-    float* dst = dwp + ((size_t)gb * HD + ch) * W;
+    float* dst = dwp + ((size_t)gb * HD + ch) * WK;
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int l = 0; l < kMaxW; ++l)
-            if (l < W) dst[v * W + l] = dwa[v][l];
+        for (int l = 0; l < WK; ++l) dst[v * WK + l] = dwa[v][l];
 }
 
 // 16 waves x 64 columns per workgroup: wave r sums the blocks g = r mod 16
@@ -218,18 +215,35 @@ __global__ __launch_bounds__(64 * kRedWaves) void conv_dw_reduce_kernel(int nblk
     }
 }
 
-template <typename T, int MODE>
-hipError_t conv_bwd_t(const Launch& L, const void* k, const float* w, int W, const void* gk,
-                      void* dk, float* dwp)
+template <typename T, int MODE, int WK>
+hipError_t conv_bwd_w(const Launch& L, const void* k, const float* w, const void* gk, void* dk,
+                      float* dwp)
 {
     const int HD = L.st.H * L.D;
     const int nblk = L.st.total_blocks;
     if (nblk > 0) {
         dim3 grid(nblk, (HD + kThreads * kVec - 1) / (kThreads * kVec));
-        hipLaunchKernelGGL((conv_bwd_kernel<T, MODE>), grid, dim3(kThreads), 0, L.stream, L.st, HD,
-                           (const T*)k, w, W, (const T*)gk, (T*)dk, dwp);
+        hipLaunchKernelGGL((conv_bwd_kernel<T, MODE, WK>), grid, dim3(kThreads), 0, L.stream, L.st,
+                           HD, (const T*)k, w, (const T*)gk, (T*)dk, dwp);
     }
     return hipGetLastError();
+}
+
+template <typename T, int MODE>
+hipError_t conv_bwd_t(const Launch& L, const void* k, const float* w, int W, const void* gk,
+                      void* dk, float* dwp)
+{
+    switch (W) {
+        case 1: return conv_bwd_w<T, MODE, 1>(L, k, w, gk, dk, dwp);
+        case 2: return conv_bwd_w<T, MODE, 2>(L, k, w, gk, dk, dwp);
+        case 3: return conv_bwd_w<T, MODE, 3>(L, k, w, gk, dk, dwp);
+        case 4: return conv_bwd_w<T, MODE, 4>(L, k, w, gk, dk, dwp);
+        case 5: return conv_bwd_w<T, MODE, 5>(L, k, w, gk, dk, dwp);
+        case 6: return conv_bwd_w<T, MODE, 6>(L, k, w, gk, dk, dwp);
+        case 7: return conv_bwd_w<T, MODE, 7>(L, k, w, gk, dk, dwp);
+        case 8: return conv_bwd_w<T, MODE, 8>(L, k, w, gk, dk, dwp);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace

@@ -23,7 +23,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kVec = 4;          // channels per thread
-constexpr int kMaxW = 8;
 
 template <typename T> struct Vec4;
 template <> struct Vec4<float> {
@@ -88,10 +87,14 @@ __device__ __forceinline__ float silu_fast_bf16(float x, float acc, bool& safe)
 
 // CONV: apply the key convolution (MODE 0 plain, 1 SiLU + residual) and
 //       write k'.  POOL: write the block centroid of the (convolved) keys.
-template <typename T, bool CONV, bool POOL, int MODE>
+// WK: the filter width, a compile-time constant so that the sliding window
+//     is WK registers per channel and each output is exactly WK fmas
+//     (a run-time width would cost a select per possible tap: measured
+//     VALU-bound at 63 % busy with W = 3).  1 when CONV is false.
+template <typename T, bool CONV, bool POOL, int MODE, int WK>
 __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     SegTable st, int HD, const T* __restrict__ k, const float* __restrict__ w,
-    int W, T* __restrict__ kout, float* __restrict__ cent)
+    T* __restrict__ kout, float* __restrict__ cent)
 {
     const int g = blockIdx.x;
     const int s = seq_of_block(st, g);
@@ -103,12 +106,12 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     const int ch = (blockIdx.y * kThreads + threadIdx.x) * kVec;
     if (ch >= HD) return;
 
-    float wr[kVec][kMaxW];
-    float win[kVec][kMaxW];        // win[v][l] = x_{t-l} after the shift
+    float wr[kVec][WK];
+    float win[kVec][WK];           // win[v][l] = x_{t-l} after the shift
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
 #pragma unroll
-        for (int l = 0; l < kMaxW; ++l) {
+        for (int l = 0; l < WK; ++l) {
             wr[v][l] = 0.f;
             win[v][l] = 0.f;
         }
@@ -116,12 +119,11 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
 #pragma unroll
         for (int v = 0; v < kVec; ++v)
 #pragma unroll
-            for (int l = 0; l < kMaxW; ++l)
-                if (l < W) wr[v][l] = w[(size_t)(ch + v) * W + l];
+            for (int l = 0; l < WK; ++l) wr[v][l] = w[(size_t)(ch + v) * WK + l];
         // before the first shift, win[m] holds x_{a-1-m}
 #pragma unroll
-        for (int m = 0; m < kMaxW - 1; ++m) {
-            if (m < W - 1 && a - 1 - m >= 0) {
+        for (int m = 0; m < WK - 1; ++m) {
+            if (a - 1 - m >= 0) {
                 float x[4];
                 Vec4<T>::load(k + (size_t)(t0 + a - 1 - m) * HD + ch, x);
 #pragma unroll
@@ -143,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     double sum[kVec] = {0.0, 0.0, 0.0, 0.0};
     // (8 tokens in flight: plain conv / pooling 4-14 % faster than 4; the
     // SiLU mode is VALU-bound and keeps 4)
-#pragma unroll (MODE == 1 ? 4 : 8)
+    constexpr int kUnroll = MODE == 1 ? 4 : 8;
+#pragma unroll kUnroll
     for (int tl = a; tl < b; ++tl) {
         const size_t row = (size_t)(t0 + tl) * HD + ch;
         float x[4];
@@ -153,12 +156,12 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
 #pragma unroll
             for (int v = 0; v < kVec; ++v) {
 #pragma unroll
-                for (int l = kMaxW - 1; l >= 1; --l) win[v][l] = win[v][l - 1];
+                for (int l = WK - 1; l >= 1; --l) win[v][l] = win[v][l - 1];
                 win[v][0] = x[v];
+                // taps from the oldest token to the newest
                 float acc = 0.0f;
 #pragma unroll
-                for (int l = kMaxW - 1; l >= 0; --l)
-                    if (l < W) acc = __builtin_fmaf(wr[v][l], win[v][l], acc);
+                for (int l = WK - 1; l >= 0; --l) acc = __builtin_fmaf(wr[v][l], win[v][l], acc);
                 if constexpr (DEFER) {
                     bool safe;
                     y[v] = silu_fast_bf16(x[v], acc, safe);
@@ -215,15 +218,31 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     }
 }
 
-template <typename T, bool CONV, bool POOL, int MODE>
-hipError_t launch_t(const Launch& L, const void* k, const float* w, int W, void* kout, float* cent)
+template <typename T, bool CONV, bool POOL, int MODE, int WK>
+hipError_t launch_t(const Launch& L, const void* k, const float* w, void* kout, float* cent)
 {
     const int HD = L.st.H * L.D;
     dim3 grid(L.st.total_blocks, (HD + kThreads * kVec - 1) / (kThreads * kVec));
     if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL((conv_pool_kernel<T, CONV, POOL, MODE>), grid, dim3(kThreads), 0,
-                       L.stream, L.st, HD, (const T*)k, w, W, (T*)kout, cent);
+    hipLaunchKernelGGL((conv_pool_kernel<T, CONV, POOL, MODE, WK>), grid, dim3(kThreads), 0,
+                       L.stream, L.st, HD, (const T*)k, w, (T*)kout, cent);
     return hipGetLastError();
+}
+
+template <typename T, bool POOL, int MODE>
+hipError_t launch_w(const Launch& L, const void* k, const float* w, int W, void* kout, float* cent)
+{
+    switch (W) {
+        case 1: return launch_t<T, true, POOL, MODE, 1>(L, k, w, kout, cent);
+        case 2: return launch_t<T, true, POOL, MODE, 2>(L, k, w, kout, cent);
+        case 3: return launch_t<T, true, POOL, MODE, 3>(L, k, w, kout, cent);
+        case 4: return launch_t<T, true, POOL, MODE, 4>(L, k, w, kout, cent);
+        case 5: return launch_t<T, true, POOL, MODE, 5>(L, k, w, kout, cent);
+        case 6: return launch_t<T, true, POOL, MODE, 6>(L, k, w, kout, cent);
+        case 7: return launch_t<T, true, POOL, MODE, 7>(L, k, w, kout, cent);
+        case 8: return launch_t<T, true, POOL, MODE, 8>(L, k, w, kout, cent);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <typename T>
@@ -232,12 +251,12 @@ hipError_t dispatch_t(const Launch& L, const void* k, const float* w, int W, int
 {
     const bool conv = kout != nullptr;
     const bool pool = cent != nullptr;
-    if (!conv) return launch_t<T, false, true, 0>(L, k, w, W, kout, cent);
+    if (!conv) return launch_t<T, false, true, 0, 1>(L, k, w, kout, cent);
     if (mode == 0)
-        return pool ? launch_t<T, true, true, 0>(L, k, w, W, kout, cent)
-                    : launch_t<T, true, false, 0>(L, k, w, W, kout, cent);
-    return pool ? launch_t<T, true, true, 1>(L, k, w, W, kout, cent)
-                : launch_t<T, true, false, 1>(L, k, w, W, kout, cent);
+        return pool ? launch_w<T, true, 0>(L, k, w, W, kout, cent)
+                    : launch_w<T, false, 0>(L, k, w, W, kout, cent);
+    return pool ? launch_w<T, true, 1>(L, k, w, W, kout, cent)
+                : launch_w<T, false, 1>(L, k, w, W, kout, cent);
 }
 
 }  // namespace

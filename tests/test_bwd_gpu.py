@@ -170,6 +170,10 @@ CONV_CASES = {
     "silu-W3-ragged": (_spec("H", seqlens=(1, 127, 129, 700, 0, 300), heads=2), "silu_residual", 3),
     "W1": (_spec("H", seq=1000, heads=2), "plain", 1),
     "W8-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 8),
+    "W2-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 2),
+    "W5-ragged": (_spec("H", seqlens=(1, 127, 129, 700), heads=2), "plain", 5),
+    "W6-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 6),
+    "W7": (_spec("H", seq=1000, heads=2), "plain", 7),
     "f32-W4": (_spec("C1"), "plain", 4),
     "C3-full-W3": (dataclasses.replace(workloads.spec("C3"), plant=False), "plain", 3),
     # 150 ragged sequences: dw sums every group's block partials in one pass

@@ -376,6 +376,29 @@ def test_conv_silu_residual_bitexact(name, width):
     assert np.array_equal(_np(cent), oracle.centroids(ref, s.block_size, cu))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["plain", "silu_residual"])
+@pytest.mark.parametrize("width", range(1, 9))
+def test_key_conv_every_width_bitexact(width, mode, dtype):
+    """Every filter width the kernels are built for (1..8), both forms and
+    both I/O dtypes, on two ragged sequences with partial last blocks: k'
+    and its centroids bit-equal to the oracle."""
+    g = torch.Generator().manual_seed(100 + 10 * width + (mode == "plain"))
+    T, H, d, B = 700, 2, 64, 64
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = (torch.randn((T, H, d), generator=g) * 2.0).to(dt)
+    w = torch.randn((H, d, width), generator=g) * (1.0 / width) ** 0.5
+    cu = [0, 300, T]
+    print(f"[conv W={width} {mode} {dtype}]", flush=True)
+    ref = oracle.key_conv(k.float(), w, cu, mode=0 if mode == "plain" else 1,
+                          round_bf16=dtype == "bf16")
+    kk, cent = moba().moba_key_conv(k.to(DEV), w.to(DEV), B, mode, cu, with_centroids=True)
+    torch.cuda.synchronize()
+    got = _flat(kk, H)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+    assert np.array_equal(_np(cent), oracle.centroids(ref, B, cu))
+
+
 def test_conv_silu_residual_fp32_bitexact():
     """fp32 I/O: k' equals the oracle's fp64 formula rounded to fp32."""
     g = torch.Generator().manual_seed(31)
