@@ -26,29 +26,49 @@ namespace moba {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 4;          // channels per thread
-
-template <typename T> struct Row4;
-template <> struct Row4<float> {
-    static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
-        const float4 v = *reinterpret_cast<const float4*>(p);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+// N consecutive channels of one token row, unpacked to fp32 (N = 4 or 8)
+template <typename T, int N> struct RowN;
+template <int N> struct RowN<float, N> {
+    static __device__ __forceinline__ void load(const float* p, float (&x)[N]) {
+#pragma unroll
+        for (int c = 0; c < N / 4; ++c) {
+            const float4 v = *reinterpret_cast<const float4*>(p + 4 * c);
+            x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+        }
     }
-    static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
-        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    static __device__ __forceinline__ void store(float* p, const float (&x)[N]) {
+#pragma unroll
+        for (int c = 0; c < N / 4; ++c)
+            *reinterpret_cast<float4*>(p + 4 * c) = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
     }
 };
-template <> struct Row4<uint16_t> {
-    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[4]) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
-        x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+template <int N> struct RowN<uint16_t, N> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[N]) {
+        if constexpr (N == 8) {
+            const uint4 v = *reinterpret_cast<const uint4*>(p);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { x[2 * e] = bf16_lo(w[e]); x[2 * e + 1] = bf16_hi(w[e]); }
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+            x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+        }
     }
-    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[4]) {
-        uint2 v;
-        v.x = pack_bf16x2(x[0], x[1]);
-        v.y = pack_bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(p) = v;
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[N]) {
+        if constexpr (N == 8) {
+            uint4 v;
+            v.x = pack_bf16x2(x[0], x[1]);
+            v.y = pack_bf16x2(x[2], x[3]);
+            v.z = pack_bf16x2(x[4], x[5]);
+            v.w = pack_bf16x2(x[6], x[7]);
+            *reinterpret_cast<uint4*>(p) = v;
+        } else {
+            uint2 v;
+            v.x = pack_bf16x2(x[0], x[1]);
+            v.y = pack_bf16x2(x[2], x[3]);
+            *reinterpret_cast<uint2*>(p) = v;
+        }
     }
 };
 
@@ -62,8 +82,9 @@ __device__ __forceinline__ float silu_grad(float u)
 }
 
 // WK: the filter width, a compile-time constant (windows of WK registers,
-// exactly WK fmas per tap loop, no per-tap selects)
-template <typename T, int MODE, int WK>
+// exactly WK fmas per tap loop, no per-tap selects).  NV: channels per
+// thread, 8 where a workgroup then reads whole 2048-channel rows.
+template <typename T, int MODE, int WK, int NV>
 __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
     SegTable st, int HD, const T* __restrict__ k, const float* __restrict__ w,
     const T* __restrict__ gk, T* __restrict__ dk, float* __restrict__ dwp)
@@ -75,26 +96,26 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
     const int L = seq_len(st, s);
     const int a = jb * st.B;
     const int b = min(a + st.B, L);
-    const int ch = (blockIdx.y * kThreads + threadIdx.x) * kVec;
+    const int ch = (blockIdx.y * kThreads + threadIdx.x) * NV;
     if (ch >= HD) return;
 
-    float wr[kVec][WK];
+    float wr[NV][WK];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int l = 0; l < WK; ++l) wr[v][l] = w[(size_t)(ch + v) * WK + l];
 
     // u_tau from direct loads (halo tokens only)
-    auto conv_at = [&](int tau, float (&u)[kVec]) {
+    auto conv_at = [&](int tau, float (&u)[NV]) {
 #pragma unroll
-        for (int v = 0; v < kVec; ++v) u[v] = 0.f;
+        for (int v = 0; v < NV; ++v) u[v] = 0.f;
 #pragma unroll
         for (int m = WK - 1; m >= 0; --m) {
             if (tau - m >= 0) {
-                float x[4];
-                Row4<T>::load(k + (t0 + tau - m) * HD + ch, x);
+                float x[NV];
+                RowN<T, NV>::load(k + (t0 + tau - m) * HD + ch, x);
 #pragma unroll
-                for (int v = 0; v < kVec; ++v) u[v] = __builtin_fmaf(wr[v][m], x[v], u[v]);
+                for (int v = 0; v < NV; ++v) u[v] = __builtin_fmaf(wr[v][m], x[v], u[v]);
             }
         }
     };
@@ -102,61 +123,61 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
     // ewin[v][l] = e_{t+l} once e_t is shifted in, so before the first
     // (last-in-sequence-order) token ewin[v][m] holds e_{b+m}: the halo,
     // zero past the sequence end
-    float ewin[kVec][WK];
+    float ewin[NV][WK];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int l = 0; l < WK; ++l) ewin[v][l] = 0.f;
 #pragma unroll
     for (int l = 1; l < WK; ++l) {
         const int tau = b - 1 + l;
         if (tau < L) {
-            float gx[4];
-            Row4<T>::load(gk + (t0 + tau) * HD + ch, gx);
+            float gx[NV];
+            RowN<T, NV>::load(gk + (t0 + tau) * HD + ch, gx);
             if constexpr (MODE == 1) {
-                float u[kVec];
+                float u[NV];
                 conv_at(tau, u);
 #pragma unroll
-                for (int v = 0; v < kVec; ++v) gx[v] *= silu_grad(u[v]);
+                for (int v = 0; v < NV; ++v) gx[v] *= silu_grad(u[v]);
             }
 #pragma unroll
-            for (int v = 0; v < kVec; ++v) ewin[v][l - 1] = gx[v];
+            for (int v = 0; v < NV; ++v) ewin[v][l - 1] = gx[v];
         }
     }
     // kwin[v][m] = k_{t-m} (zero before the sequence start)
-    float kwin[kVec][WK];
+    float kwin[NV][WK];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int m = 0; m < WK; ++m) kwin[v][m] = 0.f;
 #pragma unroll
     for (int m = 0; m < WK; ++m) {
         const int tau = b - 1 - m;
         if (tau >= 0) {
-            float x[4];
-            Row4<T>::load(k + (t0 + tau) * HD + ch, x);
+            float x[NV];
+            RowN<T, NV>::load(k + (t0 + tau) * HD + ch, x);
 #pragma unroll
-            for (int v = 0; v < kVec; ++v) kwin[v][m] = x[v];
+            for (int v = 0; v < NV; ++v) kwin[v][m] = x[v];
         }
     }
 
-    float dwa[kVec][WK];
+    float dwa[NV][WK];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int l = 0; l < WK; ++l) dwa[v][l] = 0.f;
 
 #pragma unroll 4
     for (int t = b - 1; t >= a; --t) {
         const size_t row = (t0 + t) * HD + ch;
-        float gx[4];
-        Row4<T>::load(gk + row, gx);
+        float gx[NV];
+        RowN<T, NV>::load(gk + row, gx);
         // the k row that enters the window for the next (earlier) token
-        float knext[4] = {0.f, 0.f, 0.f, 0.f};
-        if (t - WK >= 0) Row4<T>::load(k + (t0 + t - WK) * HD + ch, knext);
-        float out[4];
+        float knext[NV] = {};
+        if (t - WK >= 0) RowN<T, NV>::load(k + (t0 + t - WK) * HD + ch, knext);
+        float out[NV];
 #pragma unroll
-        for (int v = 0; v < kVec; ++v) {
+        for (int v = 0; v < NV; ++v) {
             float e = gx[v];
             if constexpr (MODE == 1) {
                 float u = 0.f;
@@ -181,11 +202,11 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(
             // the entering row is k_{t-W}, at index W-1 after the shift
             kwin[v][WK - 1] = knext[v];
         }
-        Row4<T>::store(dk + row, out);
+        RowN<T, NV>::store(dk + row, out);
     }
     float* dst = dwp + ((size_t)gb * HD + ch) * WK;
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int l = 0; l < WK; ++l) dst[v * WK + l] = dwa[v][l];
 }
@@ -215,18 +236,29 @@ __global__ __launch_bounds__(64 * kRedWaves) void conv_dw_reduce_kernel(int nblk
     }
 }
 
-template <typename T, int MODE, int WK>
-hipError_t conv_bwd_w(const Launch& L, const void* k, const float* w, const void* gk, void* dk,
+template <typename T, int MODE, int WK, int NV>
+hipError_t conv_bwd_n(const Launch& L, const void* k, const float* w, const void* gk, void* dk,
                       float* dwp)
 {
     const int HD = L.st.H * L.D;
     const int nblk = L.st.total_blocks;
     if (nblk > 0) {
-        dim3 grid(nblk, (HD + kThreads * kVec - 1) / (kThreads * kVec));
-        hipLaunchKernelGGL((conv_bwd_kernel<T, MODE, WK>), grid, dim3(kThreads), 0, L.stream, L.st,
+        dim3 grid(nblk, (HD + kThreads * NV - 1) / (kThreads * NV));
+        hipLaunchKernelGGL((conv_bwd_kernel<T, MODE, WK, NV>), grid, dim3(kThreads), 0, L.stream, L.st,
                            HD, (const T*)k, w, (const T*)gk, (T*)dk, dwp);
     }
     return hipGetLastError();
+}
+
+// 8 channels per thread for plain convs of up to 4 taps on rows of 2048
+// channels or more (wider windows would not fit the registers)
+template <typename T, int MODE, int WK>
+hipError_t conv_bwd_w(const Launch& L, const void* k, const float* w, const void* gk, void* dk,
+                      float* dwp)
+{
+    if constexpr (MODE == 0 && WK <= 4)
+        if (L.st.H * L.D >= 2048) return conv_bwd_n<T, MODE, WK, 8>(L, k, w, gk, dk, dwp);
+    return conv_bwd_n<T, MODE, WK, 4>(L, k, w, gk, dk, dwp);
 }
 
 template <typename T, int MODE>

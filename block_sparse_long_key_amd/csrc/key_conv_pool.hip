@@ -22,19 +22,25 @@ namespace moba {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kVec = 4;          // channels per thread
 
-template <typename T> struct Vec4;
-template <> struct Vec4<float> {
-    static __device__ __forceinline__ void load(const float* p, float (&x)[4]) {
-        float4 v = *reinterpret_cast<const float4*>(p);
-        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+// N consecutive channels of one token row (N = 4: 8 / 16 bytes, N = 8: 16 /
+// 32 bytes), unpacked to fp32
+template <typename T, int N> struct VecIO;
+template <int N> struct VecIO<float, N> {
+    static __device__ __forceinline__ void load(const float* p, float (&x)[N]) {
+#pragma unroll
+        for (int c = 0; c < N / 4; ++c) {
+            const float4 v = *reinterpret_cast<const float4*>(p + 4 * c);
+            x[4 * c] = v.x; x[4 * c + 1] = v.y; x[4 * c + 2] = v.z; x[4 * c + 3] = v.w;
+        }
     }
-    static __device__ __forceinline__ void store(float* p, const float (&x)[4]) {
-        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    static __device__ __forceinline__ void store(float* p, const float (&x)[N]) {
+#pragma unroll
+        for (int c = 0; c < N / 4; ++c)
+            *reinterpret_cast<float4*>(p + 4 * c) = make_float4(x[4 * c], x[4 * c + 1], x[4 * c + 2], x[4 * c + 3]);
     }
 };
-template <> struct Vec4<uint16_t> {
+template <> struct VecIO<uint16_t, 4> {
     static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[4]) {
         uint2 v = *reinterpret_cast<const uint2*>(p);
         x[0] = __uint_as_float(v.x << 16);
@@ -47,6 +53,25 @@ template <> struct Vec4<uint16_t> {
         v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
         v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
         *reinterpret_cast<uint2*>(p) = v;
+    }
+};
+template <> struct VecIO<uint16_t, 8> {
+    static __device__ __forceinline__ void load(const uint16_t* p, float (&x)[8]) {
+        const uint4 v = *reinterpret_cast<const uint4*>(p);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = __uint_as_float(w[e] << 16);
+            x[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+        }
+    }
+    static __device__ __forceinline__ void store(uint16_t* p, const float (&x)[8]) {
+        uint4 v;
+        v.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+        v.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+        v.z = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+        v.w = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+        *reinterpret_cast<uint4*>(p) = v;
     }
 };
 
@@ -91,7 +116,11 @@ __device__ __forceinline__ float silu_fast_bf16(float x, float acc, bool& safe)
 //     is WK registers per channel and each output is exactly WK fmas
 //     (a run-time width would cost a select per possible tap: measured
 //     VALU-bound at 63 % busy with W = 3).  1 when CONV is false.
-template <typename T, bool CONV, bool POOL, int MODE, int WK>
+// NV: channels per thread (4 or 8): a workgroup covers 256 * NV channels of
+//     a token row, so rows of 2048 channels are read whole with 16-byte bf16
+//     loads (plain conv C5-shaped 0.321 -> 0.234 ms; with 1024-channel rows
+//     half the threads would idle, so 4 there).
+template <typename T, bool CONV, bool POOL, int MODE, int WK, int NV>
 __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     SegTable st, int HD, const T* __restrict__ k, const float* __restrict__ w,
     T* __restrict__ kout, float* __restrict__ cent)
@@ -103,13 +132,13 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     const int L = seq_len(st, s);
     const int a = jb * st.B;
     const int b = min(a + st.B, L);
-    const int ch = (blockIdx.y * kThreads + threadIdx.x) * kVec;
+    const int ch = (blockIdx.y * kThreads + threadIdx.x) * NV;
     if (ch >= HD) return;
 
-    float wr[kVec][WK];
-    float win[kVec][WK];           // win[v][l] = x_{t-l} after the shift
+    float wr[NV][WK];
+    float win[NV][WK];           // win[v][l] = x_{t-l} after the shift
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
+    for (int v = 0; v < NV; ++v)
 #pragma unroll
         for (int l = 0; l < WK; ++l) {
             wr[v][l] = 0.f;
@@ -117,17 +146,17 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
         }
     if constexpr (CONV) {
 #pragma unroll
-        for (int v = 0; v < kVec; ++v)
+        for (int v = 0; v < NV; ++v)
 #pragma unroll
             for (int l = 0; l < WK; ++l) wr[v][l] = w[(size_t)(ch + v) * WK + l];
         // before the first shift, win[m] holds x_{a-1-m}
 #pragma unroll
         for (int m = 0; m < WK - 1; ++m) {
             if (a - 1 - m >= 0) {
-                float x[4];
-                Vec4<T>::load(k + (size_t)(t0 + a - 1 - m) * HD + ch, x);
+                float x[NV];
+                VecIO<T, NV>::load(k + (size_t)(t0 + a - 1 - m) * HD + ch, x);
 #pragma unroll
-                for (int v = 0; v < kVec; ++v) win[v][m] = x[v];
+                for (int v = 0; v < NV; ++v) win[v][m] = x[v];
             }
         }
     }
@@ -142,19 +171,19 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     __shared__ float4 fq[DEFER ? kQ : 1][kThreads];
     int nq = 0;
 
-    double sum[kVec] = {0.0, 0.0, 0.0, 0.0};
+    double sum[NV] = {};
     // (8 tokens in flight: plain conv / pooling 4-14 % faster than 4; the
     // SiLU mode is VALU-bound and keeps 4)
     constexpr int kUnroll = MODE == 1 ? 4 : 8;
 #pragma unroll kUnroll
     for (int tl = a; tl < b; ++tl) {
         const size_t row = (size_t)(t0 + tl) * HD + ch;
-        float x[4];
-        Vec4<T>::load(k + row, x);
-        float y[4];
+        float x[NV];
+        VecIO<T, NV>::load(k + row, x);
+        float y[NV];
         if constexpr (CONV) {
 #pragma unroll
-            for (int v = 0; v < kVec; ++v) {
+            for (int v = 0; v < NV; ++v) {
 #pragma unroll
                 for (int l = WK - 1; l >= 1; --l) win[v][l] = win[v][l - 1];
                 win[v][0] = x[v];
@@ -168,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
                     if (!safe) {
                         if (nq < kQ) {
                             fq[nq][threadIdx.x] = make_float4(x[v], acc, y[v],
-                                                              __int_as_float(((tl - a) << 2) | v));
+                                                              __int_as_float(((tl - a) << 3) | v));
                             ++nq;
                         } else {
                             y[v] = silu_exact<T>(x[v], acc);
@@ -180,14 +209,14 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
                     y[v] = IO<T>::round(acc);
                 }
             }
-            Vec4<T>::store(kout + row, y);
+            VecIO<T, NV>::store(kout + row, y);
         } else {
 #pragma unroll
-            for (int v = 0; v < kVec; ++v) y[v] = x[v];
+            for (int v = 0; v < NV; ++v) y[v] = x[v];
         }
         if constexpr (POOL) {
 #pragma unroll
-            for (int v = 0; v < kVec; ++v) sum[v] += (double)y[v];
+            for (int v = 0; v < NV; ++v) sum[v] += (double)y[v];
         }
     }
     if constexpr (DEFER) {
@@ -197,13 +226,13 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
         for (int e = 0; e < nq; ++e) {
             const float4 f = fq[e][threadIdx.x];
             const int pos = __float_as_int(f.w);
-            const int tl = a + (pos >> 2), v = pos & 3;
+            const int tl = a + (pos >> 3), v = pos & 7;
             const float yx = silu_exact<T>(f.x, f.y);
             if (yx != f.z) {
                 kout[(size_t)(t0 + tl) * HD + ch + v] = f32_to_bf16(yx);
                 const double dlt = (double)yx - (double)f.z;
 #pragma unroll
-                for (int u = 0; u < kVec; ++u)
+                for (int u = 0; u < NV; ++u)
                     if (u == v) sum[u] += dlt;
             }
         }
@@ -211,36 +240,47 @@ __global__ __launch_bounds__(kThreads) void conv_pool_kernel(
     if constexpr (POOL) {
         const double cnt = (double)(b - a);
         float* dst = cent + (size_t)g * HD + ch;
-        float r[4];
+        float r[NV];
 #pragma unroll
-        for (int v = 0; v < kVec; ++v) r[v] = (float)(sum[v] / cnt);
-        *reinterpret_cast<float4*>(dst) = make_float4(r[0], r[1], r[2], r[3]);
+        for (int v = 0; v < NV; ++v) r[v] = (float)(sum[v] / cnt);
+        VecIO<float, NV>::store(dst, r);
     }
 }
 
-template <typename T, bool CONV, bool POOL, int MODE, int WK>
+template <typename T, bool CONV, bool POOL, int MODE, int WK, int NV>
 hipError_t launch_t(const Launch& L, const void* k, const float* w, void* kout, float* cent)
 {
     const int HD = L.st.H * L.D;
-    dim3 grid(L.st.total_blocks, (HD + kThreads * kVec - 1) / (kThreads * kVec));
+    dim3 grid(L.st.total_blocks, (HD + kThreads * NV - 1) / (kThreads * NV));
     if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL((conv_pool_kernel<T, CONV, POOL, MODE, WK>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((conv_pool_kernel<T, CONV, POOL, MODE, WK, NV>), grid, dim3(kThreads), 0,
                        L.stream, L.st, HD, (const T*)k, w, (T*)kout, cent);
     return hipGetLastError();
+}
+
+// 8 channels per thread where a token row has 2048 channels or more (plain
+// conv of up to 4 taps and pooling; the SiLU mode and wider filters, whose
+// windows would take most of the registers, keep 4)
+template <typename T, bool CONV, bool POOL, int MODE, int WK>
+hipError_t launch_nv(const Launch& L, const void* k, const float* w, void* kout, float* cent)
+{
+    if constexpr (MODE == 0 && WK <= 4)
+        if (L.st.H * L.D >= 2048) return launch_t<T, CONV, POOL, MODE, WK, 8>(L, k, w, kout, cent);
+    return launch_t<T, CONV, POOL, MODE, WK, 4>(L, k, w, kout, cent);
 }
 
 template <typename T, bool POOL, int MODE>
 hipError_t launch_w(const Launch& L, const void* k, const float* w, int W, void* kout, float* cent)
 {
     switch (W) {
-        case 1: return launch_t<T, true, POOL, MODE, 1>(L, k, w, kout, cent);
-        case 2: return launch_t<T, true, POOL, MODE, 2>(L, k, w, kout, cent);
-        case 3: return launch_t<T, true, POOL, MODE, 3>(L, k, w, kout, cent);
-        case 4: return launch_t<T, true, POOL, MODE, 4>(L, k, w, kout, cent);
-        case 5: return launch_t<T, true, POOL, MODE, 5>(L, k, w, kout, cent);
-        case 6: return launch_t<T, true, POOL, MODE, 6>(L, k, w, kout, cent);
-        case 7: return launch_t<T, true, POOL, MODE, 7>(L, k, w, kout, cent);
-        case 8: return launch_t<T, true, POOL, MODE, 8>(L, k, w, kout, cent);
+        case 1: return launch_nv<T, true, POOL, MODE, 1>(L, k, w, kout, cent);
+        case 2: return launch_nv<T, true, POOL, MODE, 2>(L, k, w, kout, cent);
+        case 3: return launch_nv<T, true, POOL, MODE, 3>(L, k, w, kout, cent);
+        case 4: return launch_nv<T, true, POOL, MODE, 4>(L, k, w, kout, cent);
+        case 5: return launch_nv<T, true, POOL, MODE, 5>(L, k, w, kout, cent);
+        case 6: return launch_nv<T, true, POOL, MODE, 6>(L, k, w, kout, cent);
+        case 7: return launch_nv<T, true, POOL, MODE, 7>(L, k, w, kout, cent);
+        case 8: return launch_nv<T, true, POOL, MODE, 8>(L, k, w, kout, cent);
     }
     return hipErrorInvalidValue;
 }
@@ -251,7 +291,7 @@ hipError_t dispatch_t(const Launch& L, const void* k, const float* w, int W, int
 {
     const bool conv = kout != nullptr;
     const bool pool = cent != nullptr;
-    if (!conv) return launch_t<T, false, true, 0, 1>(L, k, w, kout, cent);
+    if (!conv) return launch_nv<T, false, true, 0, 1>(L, k, w, kout, cent);
     if (mode == 0)
         return pool ? launch_w<T, true, 0>(L, k, w, W, kout, cent)
                     : launch_w<T, false, 0>(L, k, w, W, kout, cent);

@@ -174,6 +174,11 @@ CONV_CASES = {
     "W5-ragged": (_spec("H", seqlens=(1, 127, 129, 700), heads=2), "plain", 5),
     "W6-silu": (_spec("H", seq=1000, heads=2), "silu_residual", 6),
     "W7": (_spec("H", seq=1000, heads=2), "plain", 7),
+    # rows of 2048 channels: plain convs of up to 4 taps run 8 channels per thread
+    "wide-W2-d128": (_spec("C5", seqlens=(300, 129, 211), heads=16), "plain", 2),
+    "wide-W4-d128": (_spec("C5", seqlens=(700,), heads=16), "plain", 4),
+    "wide-W5-d128": (_spec("C5", seqlens=(500,), heads=16), "plain", 5),
+    "wide-f32-W3": (dataclasses.replace(_spec("C5", seqlens=(400,), heads=16), dtype="f32", block_size=64), "plain", 3),
     "f32-W4": (_spec("C1"), "plain", 4),
     "C3-full-W3": (dataclasses.replace(workloads.spec("C3"), plant=False), "plain", 3),
     # 150 ragged sequences: dw sums every group's block partials in one pass

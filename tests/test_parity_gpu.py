@@ -399,6 +399,31 @@ def test_key_conv_every_width_bitexact(width, mode, dtype):
     assert np.array_equal(_np(cent), oracle.centroids(ref, B, cu))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("width", [1, 2, 3, 4, 5])
+def test_key_conv_wide_rows_bitexact(width, dtype):
+    """Token rows of 2048 channels (16 heads x d = 128), where plain convs of
+    up to 4 taps and the pooling run 8 channels per thread: k' and the
+    centroids bit-equal to the oracle (width 5 takes the 4-channel path on
+    the same rows); pooling alone too."""
+    g = torch.Generator().manual_seed(200 + width)
+    T, H, d = 600, 16, 128
+    B = 128 if dtype == "bf16" else 64          # (fp32 at d = 128 takes B = 64)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    k = (torch.randn((T, H, d), generator=g) * 2.0).to(dt)
+    w = torch.randn((H, d, width), generator=g) * (1.0 / width) ** 0.5
+    cu = [0, 250, T]
+    print(f"[wide conv W={width} {dtype}]", flush=True)
+    ref = oracle.key_conv(k.float(), w, cu, mode=0, round_bf16=dtype == "bf16")
+    kk, cent = moba().moba_key_conv(k.to(DEV), w.to(DEV), B, "plain", cu, with_centroids=True)
+    c0 = moba().moba_centroids(k.to(DEV), B, cu)
+    torch.cuda.synchronize()
+    got = _flat(kk, H)
+    assert np.array_equal(got, ref), f"{int((got != ref).sum())} elements differ"
+    assert np.array_equal(_np(cent), oracle.centroids(ref, B, cu))
+    assert np.array_equal(_np(c0), oracle.centroids(k.float(), B, cu))
+
+
 def test_conv_silu_residual_fp32_bitexact():
     """fp32 I/O: k' equals the oracle's fp64 formula rounded to fp32."""
     g = torch.Generator().manual_seed(31)
