@@ -329,13 +329,14 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
     }
 }
 
-// Block sizes above 128: a selected block of B = r * 128 keys is the union
-// of its r sub-blocks of 128 keys, and the query's own block splits into the
+// Blocks larger than the attention kernels' (128 keys; 64 for fp32 at
+// d = 128): a selected block of B = r * ab keys is the union of its r
+// sub-blocks of ab keys, and the query's own block splits into the
 // sub-blocks before its own sub-block (every key of which precedes the
 // query) and its own sub-block (token-causal).  Attention over the selection
-// is therefore attention over 128-key blocks with this expanded list, which
-// the 128-key kernels run unchanged.  One thread per (token, head) row.
-__global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int r, int Kp,
+// is therefore attention over ab-key blocks with this expanded list, which
+// the ab-key kernels run unchanged.  One thread per (token, head) row.
+__global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int r, int lab, int Kp,
                                                              const int32_t* __restrict__ idx,
                                                              int32_t* __restrict__ pidx, int64_t rows)
 {
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int 
     }
     const int tl = t - stl.cu[s];
     const int il = tl / stl.B;                   // logical own block
-    const int pt = tl >> 7;                      // physical own block
+    const int pt = tl >> lab;                    // physical own block
     const int32_t* in = idx + row * K;
     int32_t* out = pidx + row * Kp;
     int n = 0;
@@ -369,13 +370,14 @@ __global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int 
 
 }  // namespace
 
-hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx)
+hipError_t launch_expand_idx(const Launch& Ll, int ab, int Kp, const int32_t* idx, int32_t* pidx)
 {
     const int64_t rows = (int64_t)Ll.tokens * Ll.st.H;
     if (rows == 0) return hipSuccess;
-    const int r = Ll.st.B / 128;
+    const int r = Ll.st.B / ab;
+    const int lab = 31 - __builtin_clz((unsigned)ab);
     hipLaunchKernelGGL(expand_idx_kernel, dim3((unsigned)((rows + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                       Ll.stream, Ll.st, r, Kp, idx, pidx, rows);
+                       Ll.stream, Ll.st, r, lab, Kp, idx, pidx, rows);
     return hipGetLastError();
 }
 

@@ -29,14 +29,14 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
         return MOBA_ERR_UNSUPPORTED;
     if (sh->top_k < 1) return MOBA_ERR_INVALID_ARG;
     if (sh->top_k > 32) return MOBA_ERR_UNSUPPORTED;
-    // blocks of 256 / 512 keys are attended as 2 / 4 blocks of 128: the
-    // expanded selection must fit 32 slots
+    // the MFMA router takes top_k <= 8 with blocks of 256 / 512 keys
     if (sh->block_size > 128 && sh->top_k > 8) return MOBA_ERR_UNSUPPORTED;
+    // blocks larger than the attention kernels' are attended as their
+    // sub-blocks: the expanded selection must fit 32 slots
+    const int ab = att_block(sh->dtype, sh->head_dim, sh->block_size);
+    if (sh->top_k * (sh->block_size / ab) > 32) return MOBA_ERR_UNSUPPORTED;
     // the fp32 router runs one thread per query of a block (<= 256)
     if (sh->dtype == MOBA_F32 && sh->block_size > 256) return MOBA_ERR_UNSUPPORTED;
-    // fp32 keeps a whole (128-key) block of K and V in LDS: B * d <= 8192
-    const int att_b = sh->block_size < 128 ? sh->block_size : 128;
-    if (sh->dtype == MOBA_F32 && sh->head_dim * att_b > 8192) return MOBA_ERR_UNSUPPORTED;
 
     memset(L, 0, sizeof(*L));
     SegTable& st = L->st;
@@ -103,8 +103,9 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
 }
 
 // bwd: the backward's workspace (index + its own buffers, no forward partials)
-// expand: the selection is re-expressed in 128-key blocks first (block
-// sizes 256 / 512); L is then the 128-key launch
+// expand: the selection is re-expressed in the attention kernels' blocks
+// first (block sizes 256 / 512; 128 in fp32 at d = 128); L is then the
+// attention launch
 WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
 {
     WsLayout w;
@@ -155,24 +156,26 @@ bool ptr_ok(const void* p) { return p != nullptr && aligned16(p); }
 bool idx_ok(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 
 
-// The attention entry points work on 128-key blocks when the shape's blocks
-// are larger: Ll is the shape's own launch (routing granularity), La the
-// one the attention kernels run with (block 128, top_k * B / 128 slots).
+// The attention entry points work on att_block()-key blocks when the
+// shape's blocks are larger: Ll is the shape's own launch (routing
+// granularity), La the one the attention kernels run with (block ab,
+// top_k * B / ab slots).
 moba_status attn_launch(const moba_shape* sh, hipStream_t stream, Launch* Ll, Launch* La)
 {
     moba_status st = make_launch(sh, Ll, stream);
     if (st != MOBA_OK) return st;
-    if (sh->block_size <= 128) {
+    const int ab = att_block(sh->dtype, sh->head_dim, sh->block_size);
+    if (sh->block_size <= ab) {
         *La = *Ll;
         return MOBA_OK;
     }
     moba_shape p = *sh;
-    p.block_size = 128;
-    p.top_k = sh->top_k * (sh->block_size / 128);
+    p.block_size = ab;
+    p.top_k = sh->top_k * (sh->block_size / ab);
     return make_launch(&p, La, stream);
 }
 
-bool expands(const Launch& Ll) { return Ll.st.B > 128; }
+bool expands(const Launch& Ll) { return Ll.st.B > att_block(Ll.dtype, Ll.D, Ll.st.B); }
 
 moba_status check_ws(const Launch& L, const void* ws, size_t bytes, WsLayout* out, bool bwd = false,
                      bool expand = false)
@@ -399,7 +402,7 @@ hipError_t run_index(const Launch& Ll, const Launch& La, const WsLayout& ws, cha
 {
     if (expands(Ll)) {
         int32_t* px = (int32_t*)(wsp + ws.px_off);
-        hipError_t e = launch_expand_idx(Ll, La.st.K, idx, px);
+        hipError_t e = launch_expand_idx(Ll, La.st.B, La.st.K, idx, px);
         if (e != hipSuccess) return e;
         idx = px;
     }

@@ -23,6 +23,16 @@ constexpr int kInvChunkBlocks = 32;
 // largest number of blocks of one sequence (LDS histogram of the inversion)
 constexpr int kMaxBlocksPerSeq = 16384;
 
+// Keys per block of the attention kernels: the shape's block size up to
+// 128; fp32 at d = 128 attends 64-key blocks (a block of K and V^T in fp32
+// must fit LDS: B * d <= 8192).  Larger blocks are attended as the union of
+// their sub-blocks of this size.
+inline int att_block(int dtype, int head_dim, int block_size)
+{
+    const int cap = (dtype == MOBA_F32 && head_dim == 128) ? 64 : 128;
+    return block_size < cap ? block_size : cap;
+}
+
 struct SegTable {
     int32_t nseq;       // number of independent sequences
     int32_t H;          // heads
@@ -174,7 +184,8 @@ hipError_t launch_route(const Launch& L, const void* q, const float* cent, void*
 // det: place each list's entries in an order that depends only on idx
 hipError_t launch_inv(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
                       bool det = false);
-hipError_t launch_expand_idx(const Launch& Ll, int Kp, const int32_t* idx, int32_t* pidx);
+// ab: the attention launch's block size (a divisor of Ll's)
+hipError_t launch_expand_idx(const Launch& Ll, int ab, int Kp, const int32_t* idx, int32_t* pidx);
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
                               const void* q, const void* k, const void* v, float scale,
                               bool block_max = false);

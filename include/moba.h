@@ -49,14 +49,17 @@
  * Support matrix: head_dim 64 or 128; block_size 64, 128, 256 or 512
  * (256 / 512: top_k <= 8, the summary page's MoBA-256 / MoBA-512 variants,
  * "Configurazione MoBA"); top_k 1..32; conv width 1..8; dtype bf16 (fast
- * path) or fp32 (correctness path; block_size * head_dim <= 8192 counting
- * blocks above 128 as 128, block_size <= 256); any number of sequences;
- * at most 16384 blocks per sequence; tokens * heads < 2^27 per call.
- * Blocks of 256 / 512 keys: routing (centroids, scores, top-k) works on the
- * blocks as given; the attention calls attend a selected block as its 2 / 4
- * sub-blocks of 128 keys (the same key set, so the same result), with the
- * query's own block split into the sub-blocks before its own sub-block and
- * its own sub-block (token-causal).
+ * path) or fp32 (correctness path; block_size <= 256); any number of
+ * sequences; at most 16384 blocks per sequence; tokens * heads < 2^27 per
+ * call.  The attention kernels work on blocks of up to 128 keys, 64 for
+ * fp32 at head_dim 128; top_k times the number of such sub-blocks per
+ * block must not exceed 32 (fp32, head_dim 128, block_size 128: top_k <=
+ * 16).
+ * Larger blocks: routing (centroids, scores, top-k) works on the blocks as
+ * given; the attention calls attend a selected block as its sub-blocks
+ * (the same key set, so the same result), with the query's own block split
+ * into the sub-blocks before its own sub-block and its own sub-block
+ * (token-causal).
  */
 #ifndef MOBA_H_
 #define MOBA_H_
@@ -241,8 +244,9 @@ moba_status moba_attn_fwd(const moba_shape *shape, const void *q,
  * part in the softmax).  The first block is always kept.
  *   blasst_lambda in [0, 1] (else MOBA_ERR_INVALID_ARG); 0 keeps every
  *   block (moba_attn_fwd's result).  o and lse are those of the softmax
- *   over the kept blocks' keys.  Block sizes 64 and 128 (larger ones:
- *   MOBA_ERR_UNSUPPORTED).  Block maxima are taken from the fp32 scores;
+ *   over the kept blocks' keys.  Shapes whose blocks the attention
+ *   kernels take whole only (block size 64 or 128, not fp32 at head_dim
+ *   128 with 128-key blocks; others: MOBA_ERR_UNSUPPORTED).  Block maxima are taken from the fp32 scores;
  *   a decision within rounding of the threshold may go either way.
  *   The key-block-major order computes every selected (query, block) pair
  *   before any query's running maximum is known, so the skip is decided in

@@ -55,6 +55,8 @@ CASES = {
     "C4-4k": _spec("C4", seq=4096, heads=2),
     "C5-4k": _spec("C5", seq=4096, heads=2),
     "d128-B64-ragged": _spec("C5", seqlens=(1000, 777), heads=2, block_size=64, top_k=4),
+    # fp32 at d = 128: 128-key blocks attended as 64-key sub-blocks
+    "f32-d128-B128": _spec("C5", seqlens=(700, 330), heads=2, block_size=128, top_k=6, dtype="f32"),
     "ragged": _spec("H", seqlens=(1, 127, 129, 700, 0, 300), heads=2),
     "top1": _spec("H", seq=1000, heads=2, top_k=1),
     "top32-B64": _spec("C4", seq=4096, heads=1, top_k=32),

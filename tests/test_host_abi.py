@@ -85,7 +85,7 @@ def test_large_blocks_attend_as_128_key_blocks(lib):
     (dict(B=256, K=9), UNSUPPORTED), (dict(dtype=0, B=512), UNSUPPORTED),
     (dict(K=0), INVALID), (dict(K=33), UNSUPPORTED), (dict(dtype=7), INVALID),
     (dict(heads=0), INVALID),
-    (dict(dtype=0, d=128, B=128), UNSUPPORTED),
+    (dict(dtype=0, d=128, B=128, K=17), UNSUPPORTED),   # 17 x 2 sub-blocks > 32 slots
     (dict(cu=[0, 10, 5]), INVALID), (dict(cu=[1, 10]), INVALID),
     (dict(cu=list(range(0, 2000, 10)) + [1990 + 16385 * 64], B=64), UNSUPPORTED),  # 16385 blocks in the last group
     (dict(cu=list(range(0, 2000, 10)) + [1995, 1990]), INVALID),  # decreasing past group 0
@@ -99,6 +99,25 @@ def test_bad_shapes_rejected_on_host(lib, kw, code):
     assert rc == code
     assert lib.moba_total_blocks(ctypes.byref(sh)) == -1
     assert lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh)) == 0
+
+
+def test_fp32_d128_attends_64_key_sub_blocks(lib):
+    """fp32 at d = 128 attends 64-key blocks: B = 128 / 256 selections are
+    expanded to 2 / 4 sub-blocks, so the workspace is that of B = 64 with
+    top_k * B / 64 slots plus the expanded selection."""
+    for B, K in ((128, 16), (128, 1), (256, 8)):
+        sh = _shape(batch=2, seq=4096, d=128, B=B, K=K, dtype=0)
+        assert lib.moba_total_blocks(ctypes.byref(sh)) == 2 * 4096 // B
+        ws = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(sh))
+        ref = lib.moba_attn_fwd_workspace_bytes(ctypes.byref(_shape(batch=2, seq=4096, d=128, B=64,
+                                                                   K=K * B // 64, dtype=0)))
+        assert ws >= ref + 2 * 4096 * sh.heads * (K * B // 64) * 4
+        assert lib.moba_attn_bwd_workspace_bytes(ctypes.byref(sh)) > 0
+    p = ctypes.c_void_p(16 * 1024)
+    sh = _shape(batch=2, seq=4096, d=128, B=128, K=8, dtype=0)
+    # BLASST takes whole blocks only
+    assert lib.moba_attn_fwd_blasst(ctypes.byref(sh), p, p, p, p, ctypes.c_float(0.0),
+                                    ctypes.c_float(0.5), p, None, p, 1 << 40, None) == UNSUPPORTED
 
 
 def test_largest_accepted_shapes(lib):

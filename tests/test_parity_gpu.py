@@ -337,6 +337,11 @@ def test_route_all_scores_tied_in_the_first_blocks(K):
     ([(53 * i) % 257 for i in range(64)], 2, 64, 64, 4, "bf16"),  # 64 sequences (one launch table), one empty
     ([(53 * i) % 257 for i in range(200)], 2, 64, 64, 4, "bf16"),  # 200 sequences: 4 groups of <= 64
     ([(29 * i) % 150 for i in range(70)], 1, 128, 64, 3, "f32"),    # 70 sequences, fp32, d = 128
+    # fp32 at d = 128 attends 64-key sub-blocks of larger blocks
+    ([700, 330], 2, 128, 128, 6, "f32"),      # B = 128, ragged, two sequences
+    ([1100], 1, 128, 128, 16, "f32"),         # B = 128, k = 16: 32 expanded slots
+    ([1000], 1, 128, 128, 1, "f32"),          # B = 128, k = 1: own block split in two
+    ([1500], 1, 128, 256, 8, "f32"),          # B = 256: 4 sub-blocks per block
 ])
 def test_edge_cases(seqlens, H, d, B, K, dtype):
     print(f"[edge {seqlens} H{H} d{d} B{B} K{K} {dtype}]", flush=True)
