@@ -404,7 +404,7 @@ __device__ __forceinline__ void store4(T* p, const float (&x)[4])
 }
 
 // ------------------------------------------------------------------------
-// routed attention: one item = (key block j, <= kItemRows gathered queries),
+// routed attention: one item = (key block j, <= item_rows gathered queries),
 // processed in tiles of 128 queries (4 waves x 2 sub-tiles x 16) while K_j
 // and V_j stay in LDS
 template <typename T, int D, int BLK>

@@ -10,7 +10,7 @@
 //              matrix cm[chunk][j] for the lists j this chunk can reach;
 //   scan    -- one workgroup per (sequence, head): list totals, list offsets,
 //              per-chunk positions (in place), the work items (runs of
-//              <= kItemRows entries of one list) for the routed attention,
+//              <= item_rows entries of one list) for the routed attention,
 //              and the (first entry, count) of every whole list;
 //   scatter -- same grid as count: entries (token << 5 | slot) written at the
 //              chunk's positions with LDS cursors, and the reverse map
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
     const int per = (n + kScanThreads - 1) / kScanThreads;
     const int j0 = threadIdx.x * per, j1 = min(n, j0 + per);
     int se = 0, si = 0;
-    for (int j = j0; j < j1; ++j) { se += tot[j]; si += (tot[j] + kItemRows - 1) / kItemRows; }
+    const int IR = st.item_rows;
+    for (int j = j0; j < j1; ++j) { se += tot[j]; si += (tot[j] + IR - 1) / IR; }
     part_e[threadIdx.x] = se;
     part_i[threadIdx.x] = si;
     __syncthreads();
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
         tot[j] = be;
         ioff[j] = bi;
         be += t;
-        bi += (t + kItemRows - 1) / kItemRows;
+        bi += (t + IR - 1) / IR;
         // keep the list total in the scan result: ioff/tot of j+1 give it
     }
     __syncthreads();
@@ -175,11 +176,11 @@ __global__ __launch_bounds__(kScanThreads) void inv_scan_kernel(SegTable st, int
         }
         const int total = run - beg;
         lst[(int64_t)h * st.total_blocks + g0 + j] = make_int2(beg, total);
-        const int nit = (total + kItemRows - 1) / kItemRows;
+        const int nit = (total + IR - 1) / IR;
         for (int r = 0; r < nit; ++r) {
             Item it;
-            it.begin = beg + r * kItemRows;
-            it.count = min(kItemRows, total - r * kItemRows);
+            it.begin = beg + r * IR;
+            it.count = min(IR, total - r * IR);
             it.g = g0 + j;
             it.h = h;
             items[ib + ioff[j] + r] = it;

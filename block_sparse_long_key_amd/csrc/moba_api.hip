@@ -73,6 +73,7 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
     st.chunk = kInvChunkBlocks;
     if (maxn > 1024)
         while (st.chunk * 16 < maxn) st.chunk *= 2;
+    st.item_rows = item_rows_for(sh->dtype, sh->head_dim);
     st.boff[0] = 0;
     st.cbase[0] = 0;
     st.cmbase[0] = 0;
@@ -89,7 +90,7 @@ moba_status make_launch(const moba_shape* sh, Launch* L, hipStream_t stream)
         // lists are sized for K entries per row so that any idx row (even one
         // that omits its own block) stays in bounds
         st.ebase[s + 1] = st.ebase[s] + (int64_t)st.H * Ls * st.K;
-        const int64_t cap = (int64_t)Ls * st.K / kItemRows + n;
+        const int64_t cap = (int64_t)Ls * st.K / st.item_rows + n;
         st.ibase[s + 1] = st.ibase[s] + (int64_t)st.H * cap;
     }
     st.total_blocks = st.boff[st.nseq];

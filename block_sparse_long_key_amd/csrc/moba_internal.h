@@ -13,8 +13,18 @@
 namespace moba {
 
 constexpr int kMaxSeqs = MOBA_MAX_SEQS;
-// most queries per routed-attention work item (looped in tiles of 128)
+// most queries per routed-attention work item (looped in tiles of 128);
+// SegTable::item_rows holds the launch's value: this one, or twice it for
+// bf16 at d = 128 (routed attention at 64K x 16 heads: d = 128 items of
+// 4096 rows 1.823 -> 1.767 ms, against d = 64 items of 2048 rows 0.839 vs
+// 0.851 ms with 4096 and 0.865 with 1024).  Kernels that copy an item's
+// entries to LDS (fp32, and d = 64 with 64-key blocks) size the copy by
+// this constant and always get it.
 constexpr int kItemRows = 2048;
+inline int item_rows_for(int dtype, int head_dim)
+{
+    return (dtype == MOBA_BF16 && head_dim == 128) ? 2 * kItemRows : kItemRows;
+}
 // query blocks per inversion chunk (one workgroup of the count/scatter
 // passes): this many, or for sequences of more than 1024 blocks the power of
 // two reaching 1/16 of the longest one's blocks, so a chunk's entries still
@@ -42,6 +52,7 @@ struct SegTable {
     int32_t total_chunks;   // inversion chunks over all sequences (per head)
     int32_t chunk;          // query blocks per inversion chunk
     int64_t total_items;    // routed-attention item capacity over all (seq, head)
+    int32_t item_rows;      // most entries per item
     int32_t cu[kMaxSeqs + 1];     // token start of sequence s
     int32_t boff[kMaxSeqs + 1];   // first global block of sequence s
     int32_t cbase[kMaxSeqs + 1];  // first inversion chunk of sequence s
@@ -55,7 +66,7 @@ __host__ __device__ inline int seq_nblk(const SegTable& st, int s) { return st.b
 __host__ __device__ inline int seq_nchunk(const SegTable& st, int s) { return st.cbase[s + 1] - st.cbase[s]; }
 __host__ __device__ inline int64_t seq_item_cap(const SegTable& st, int s) {
     // a row lists at most K blocks (K-1 when it holds its own block, as it should)
-    return (int64_t)seq_len(st, s) * st.K / kItemRows + seq_nblk(st, s);
+    return (int64_t)seq_len(st, s) * st.K / st.item_rows + seq_nblk(st, s);
 }
 
 // sequence holding global block g (boff is non-decreasing; empty sequences
@@ -127,7 +138,7 @@ typedef uint16_t u16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-// routed-attention work item: a run of <= kItemRows entries of one list
+// routed-attention work item: a run of <= item_rows entries of one list
 struct Item {
     int32_t begin;   // first entry, relative to the (seq, head) entries base
     int32_t count;   // 0 = empty slot
