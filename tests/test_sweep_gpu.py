@@ -1,0 +1,93 @@
+"""Seeded random sweep of the support matrix on the GPU: every case draws a
+dtype, head dim, block size, top-k, head count, a ragged varlen batch
+(empty and one-token sequences included), an optional key convolution
+(width 1..8, plain or k + SiLU) and a softmax scale, runs the whole forward
+through the C ABI and checks it against the oracle to the same bar as the
+fixed cases: k' bit-exact, the selection on every row (P3: exact, or a valid
+tolerant top-(k-1) at an oracle near-tie), O and LSE on every row against
+the oracle's attention on the GPU's selection.  Every third case also runs
+the attention backward (dq, dk', dv against the oracle's fp64 gradients for
+the same selection).  Cases follow the pages' task definition ("Optimizing
+Mixture of Block Attention", summary page, "Definizione del Compito") and
+key convolution ("Progettazione della Convoluzione delle Chiavi
+(Appendice B)")."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+import oracle  # noqa: E402
+import test_bwd_gpu as tb  # noqa: E402
+import test_parity_gpu as tp  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+NCASES = 64
+
+
+def _draw(i):
+    """Case i of the sweep: a shape inside the support matrix."""
+    g = np.random.default_rng(7100 + i)
+    dtype = "bf16" if g.random() < 0.7 else "f32"
+    d = int(g.choice([64, 128]))
+    Bs = [64, 128, 256] + ([512] if dtype == "bf16" else [])
+    B = int(g.choice(Bs))
+    ab = min(B, 64 if (dtype == "f32" and d == 128) else 128)
+    kmax = min(8 if B > 128 else 32, 32 // (B // ab))
+    K = int(g.integers(1, kmax + 1))
+    H = int(g.integers(1, 4))
+    nseq = int(g.integers(1, 5))
+    lens = [int(x) for x in g.integers(0, 1600, size=nseq)]
+    if g.random() < 0.3:
+        lens[int(g.integers(0, nseq))] = int(g.choice([0, 1, B - 1, B + 1]))
+    if sum(lens) == 0:
+        lens[0] = B + 3
+    W = int(g.integers(1, 9)) if g.random() < 0.4 else 0
+    mode = "silu_residual" if (W and g.random() < 0.4) else "plain"
+    scale = float(g.uniform(0.05, 0.3)) if g.random() < 0.3 else None
+    return dict(dtype=dtype, d=d, B=B, K=K, H=H, lens=lens, W=W, mode=mode, scale=scale)
+
+
+@pytest.mark.parametrize("i", range(NCASES))
+def test_random_shape_matches_oracle(i):
+    c = _draw(i)
+    print(f"[sweep {i}] {c}", flush=True)
+    dtype, d, B, K, H, lens = c["dtype"], c["d"], c["B"], c["K"], c["H"], c["lens"]
+    T = sum(lens)
+    g = torch.Generator().manual_seed(9300 + i)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    q = torch.randn((T, H, d), generator=g).to(dt)
+    k = torch.randn((T, H, d), generator=g).to(dt)
+    v = torch.randn((T, H, d), generator=g).to(dt)
+    w = torch.randn((H, d, c["W"]), generator=g) / max(c["W"], 1) ** 0.5 if c["W"] else None
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    mode = 0 if c["mode"] == "plain" else 1
+    ref = oracle.forward(q, k, v, B, K, cu, conv_w=w, conv_mode=mode,
+                         round_bf16=(dtype == "bf16"), scale=c["scale"] or 0.0)
+    m = tp.moba()
+    gq, gk, gv = (t.to(DEV) for t in (q, k, v))
+    o, lse, idx, kk = m.moba_fwd(gq, gk, gv, B, K, conv_w=None if w is None else w.to(DEV),
+                                 conv_mode=c["mode"], cu_seqlens=cu, scale=c["scale"])
+    torch.cuda.synchronize()
+    if w is not None:
+        got = tp._np(kk).reshape(ref["k_conv"].shape)
+        assert np.array_equal(got, ref["k_conv"]), f"k' differs in {int((got != ref['k_conv']).sum())} elements"
+    tp._verify_forward(o, lse, idx, ref, q, ref["k_conv"], v, B, K, cu, dtype, f"sweep {i}",
+                       scale=c["scale"] or 0.0)
+    if i % 3:
+        return
+    # backward for the GPU's selection (equal to the oracle's: exactness was
+    # asserted above), on the convolved keys the forward attended
+    do = torch.randn((T, H, d), generator=g).to(dt)
+    kc = torch.from_numpy(ref["k_conv"]).to(dt)
+    dq, dk, dv = m.moba_attn_bwd(gq, kc.to(DEV), gv, idx, o, lse, do.to(DEV), B, K,
+                                 cu_seqlens=cu, scale=c["scale"])
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attend_bwd(q, kc, v, ref["idx"], do, B, K, cu, scale=c["scale"] or 0.0)
+    for got, r, what in ((dq, rq, "dq"), (dk, rk, "dk'"), (dv, rv, "dv")):
+        tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype)
