@@ -77,20 +77,28 @@ __device__ __forceinline__ float pick(const float (&a)[KMAX], int p)
     return r;
 }
 
-// ascending sort of the first n entries (others must be INT_MAX)
+// ascending sort of the first n entries (others must be INT_MAX): a bitonic
+// sorting network over KMAX (a power of two) entries, every index fixed at
+// compile time (KMAX/2 * log2(KMAX) * (log2(KMAX) + 1) / 2 compare-exchanges)
 template <int KMAX>
 __device__ __forceinline__ void sort_asc(int (&x)[KMAX])
 {
+    static_assert((KMAX & (KMAX - 1)) == 0, "KMAX must be a power of two");
 #pragma unroll
-    for (int pass = 0; pass < KMAX; ++pass) {
+    for (int k = 2; k <= KMAX; k <<= 1)
 #pragma unroll
-        for (int p = (pass & 1); p + 1 < KMAX; p += 2) {
-            int lo = min(x[p], x[p + 1]);
-            int hi = max(x[p], x[p + 1]);
-            x[p] = lo;
-            x[p + 1] = hi;
-        }
-    }
+        for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+            for (int p = 0; p < KMAX; ++p) {
+                const int l = p ^ j;
+                if (l > p) {
+                    const int lo = min(x[p], x[l]);
+                    const int hi = max(x[p], x[l]);
+                    const bool up = (p & k) == 0;
+                    x[p] = up ? lo : hi;
+                    x[l] = up ? hi : lo;
+                }
+            }
 }
 
 template <typename T, int D, int KMAX>
@@ -279,6 +287,25 @@ __device__ __forceinline__ int key_block(float k, uint32_t lmask)
     return (int)(__float_as_uint(k) & lmask);
 }
 
+// Top N of two descending lists x and y, sorted, into x: c[p] = max(x[p],
+// y[N-1-p]) is bitonic and holds the top N of both; a bitonic clean sorts it.
+template <int N>
+__device__ __forceinline__ void top_of_two(float (&x)[N], const float (&y)[N], float inf)
+{
+#pragma unroll
+    for (int p = 0; p < N; ++p) x[p] = fmax2(x[p], y[N - 1 - p], inf);
+#pragma unroll
+    for (int st2 = N / 2; st2 >= 1; st2 >>= 1)
+#pragma unroll
+        for (int p = 0; p < N; ++p)
+            if ((p & st2) == 0) {
+                const float hi = fmax2(x[p], x[p + st2], inf);
+                const float lo = fmin2(x[p], x[p + st2], inf);
+                x[p] = hi;
+                x[p + st2] = lo;
+            }
+}
+
 // Sorted (descending) top-N merge of the lists of lanes l, l^16, l^32, l^48.
 // The first NIN entries of x are the lane's own sorted list (the rest -INF).
 template <int N, int NIN>
@@ -290,18 +317,7 @@ __device__ __forceinline__ void merge_lanes(float (&x)[N])
         float y[N];
 #pragma unroll
         for (int p = 0; p < N; ++p) y[p] = (m == 16 && p >= NIN) ? -INFINITY : __shfl_xor(x[p], m);
-#pragma unroll
-        for (int p = 0; p < N; ++p) x[p] = fmax2(x[p], y[N - 1 - p], inf);
-#pragma unroll
-        for (int st2 = N / 2; st2 >= 1; st2 >>= 1)
-#pragma unroll
-            for (int p = 0; p < N; ++p)
-                if ((p & st2) == 0) {
-                    const float hi = fmax2(x[p], x[p + st2], inf);
-                    const float lo = fmin2(x[p], x[p + st2], inf);
-                    x[p] = hi;
-                    x[p + st2] = lo;
-                }
+        top_of_two<N>(x, y, inf);
     }
 }
 
@@ -405,7 +421,8 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         return;
     }
 
-    // query fragments (B operand) and |q|^2
+    // query fragments (B operand) and |q|^2 (bf16 pair dot products; |q|
+    // only scales the error bound E, which carries a 2 % margin)
     u16x8_t qb[2][NKS];
     float qn2[2];
 #pragma unroll
@@ -416,10 +433,11 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         for (int ks = 0; ks < NKS; ++ks) {
             u16x8_t z = {0, 0, 0, 0, 0, 0, 0, 0};
             qb[sb][ks] = valid[sb] ? *(const u16x8_t*)(qp + 32 * ks + 8 * g4) : z;
+            const u32x4_t qw = __builtin_bit_cast(u32x4_t, qb[sb][ks]);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = bf16_to_f32(qb[sb][ks][e]);
-                acc = __builtin_fmaf(x, x, acc);
+            for (int e = 0; e < 4; ++e) {
+                const bf16x2_t x2 = __builtin_bit_cast(bf16x2_t, qw[e]);
+                acc = __builtin_amdgcn_fdot2_f32_bf16(x2, x2, acc, false);
             }
         }
         acc += __shfl_xor(acc, 16);
@@ -482,63 +500,68 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                     acc[r] = (jb + 4 * g4 + r < i) ? acc[r] : -__FLT_MAX__;
             }
             // keys: the scores with their low LB mantissa bits replaced by j.
-            // A key at or below the lane's last kept key changes nothing;
-            // each insertion is masked to the lanes whose key passes the
-            // threshold of the group's start (straight-line code: at these
-            // list lengths nearly every wave has such a lane for every key)
-            const float thr = key[sb][LL - 1];
+            // Every key runs through the med3 chain in every lane: one at or
+            // below the lane's last kept key leaves the list as it was, so
+            // no per-key mask is needed (at these list lengths nearly every
+            // wave has a passing lane for every key, and a mask only adds
+            // the compare and the exec updates)
             float x[4];
-            bool pass[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const uint32_t j = (uint32_t)(jb + 4 * g4 + r);
                 x[r] = __uint_as_float((__float_as_uint(acc[r]) & ~lmask) | j);
-                pass[r] = x[r] > thr;
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                if (pass[r]) {
 #pragma unroll
-                    for (int p = LL - 1; p >= 1; --p)
-                        key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x[r]);
-                    key[sb][0] = fmax2(key[sb][0], x[r], pinf);
-                }
+                for (int p = LL - 1; p >= 1; --p)
+                    key[sb][p] = __builtin_amdgcn_fmed3f(key[sb][p - 1], key[sb][p], x[r]);
+                key[sb][0] = fmax2(key[sb][0], x[r], pinf);
             }
         }
     };
 
-    for (int j0 = 0; j0 < i; j0 += TB) {
-        __syncthreads();
-        // stage the tile: hi / lo bf16 rows (split once by route_prep_kernel)
-        // and the row norms; the global loads of the whole tile are issued
-        // before any of them is used
-        constexpr int NCH = TB * (D / 8);           // 16-byte chunks of a tile
-        constexpr int NIT = (NCH + NT - 1) / NT;
-        u32x4_t xh[NIT], xl[NIT];
+    // tile staging: a thread's 16-byte chunks of a 64-block tile; rows past
+    // the scan are clamped to block i - 1 (always inside the sequence), so
+    // every load is in bounds and the partial group's extra rows hold real
+    // centroids, whose scores are replaced before selection.  The next
+    // tile's loads are in flight while the current tile is scored when that
+    // takes few registers (d = 64 with 128-query blocks or larger).
+    constexpr int NCH = TB * (D / 8);               // 16-byte chunks of a tile
+    constexpr int NIT = (NCH + NT - 1) / NT;
+    constexpr bool kPrefetch = NIT <= 2;
+    u32x4_t xh[NIT], xl[NIT];
+    float cn = 0.f;
+    auto fetch = [&](int j0) {
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = threadIdx.x + it * NT;
-            const int r = e / (D / 8), c8 = e % (D / 8);
-            xh[it] = u32x4_t{0u, 0u, 0u, 0u};
-            xl[it] = xh[it];
-            if (e < NCH && j0 + r < i) {
-                const size_t off = (size_t)(j0 + r) * H * D + 8 * c8;
+            if (NCH % NT == 0 || e < NCH) {
+                const int r = e / (D / 8), c8 = e % (D / 8);
+                const size_t off = (size_t)min(j0 + r, i - 1) * H * D + 8 * c8;
                 xh[it] = *(const u32x4_t*)(hbase + off);
                 xl[it] = *(const u32x4_t*)(lbase + off);
             }
         }
-        if (threadIdx.x < TB && j0 + (int)threadIdx.x < i)
-            cmax2 = fmaxf(cmax2, nbase[(size_t)(j0 + threadIdx.x) * H]);
+        if (threadIdx.x < TB) cn = nbase[(size_t)min(j0 + (int)threadIdx.x, i - 1) * H];
+    };
+    if constexpr (kPrefetch) fetch(0);
+    for (int j0 = 0; j0 < i; j0 += TB) {
+        __syncthreads();                            // the previous tile is consumed
+        if constexpr (!kPrefetch) fetch(j0);
 #pragma unroll
         for (int it = 0; it < NIT; ++it) {
             const int e = threadIdx.x + it * NT;
-            const int r = e / (D / 8), c8 = e % (D / 8);
-            if (e < NCH) {
+            if (NCH % NT == 0 || e < NCH) {
+                const int r = e / (D / 8), c8 = e % (D / 8);
                 *(u32x4_t*)(chi + r * CS + 8 * c8) = xh[it];
                 *(u32x4_t*)(clo + r * CS + 8 * c8) = xl[it];
             }
         }
+        cmax2 = fmaxf(cmax2, cn);
         __syncthreads();
+        if constexpr (kPrefetch)
+            if (j0 + TB < i) fetch(j0 + TB);
         for (int bt = 0; bt < TB / 16; ++bt) {
             const int jb = j0 + 16 * bt;
             if (jb + 16 > i) break;                 // full groups here
@@ -561,45 +584,67 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
     const float cmax = sqrtf(cm2);
     const float E0 = (1.52587890625e-05f + (float)(2 * D + 16) * 1.1920929e-07f) * 1.02f;
 
+    // Both sub-tiles are merged in one pass.  In the first exchange (lanes
+    // l, l^16) a lane keeps the list of the sub-tile ps = g4 & 1 it finishes
+    // and sends its partner the other one, so even lane groups merge
+    // sub-tile 0 and odd ones sub-tile 1; the second exchange (l, l^32)
+    // pairs lanes of the same parity.  Afterwards every lane holds the sorted
+    // top KMAX keys of query l16 of sub-tile ps.
+    const int ps = g4 & 1;
+    float mk[KMAX];
+    {
+        float y[KMAX];
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) {
+            mk[p] = ps ? key[1][p] : key[0][p];
+            y[p] = __shfl_xor(ps ? key[0][p] : key[1][p], 16);
+        }
+        top_of_two<KMAX>(mk, y, pinf);
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) y[p] = __shfl_xor(mk[p], 32);
+        top_of_two<KMAX>(mk, y, pinf);
+    }
+    float a = mk[0], b = mk[0];
+#pragma unroll
+    for (int p = 1; p < KMAX; ++p) {
+        a = (p == K - 2) ? mk[p] : a;
+        b = (p == K - 1) ? mk[p] : b;
+    }
+    // a lane whose last kept key is above b may have dropped one of the top
+    // K: then nothing here is trusted (overflow -> fp64 path)
+    float lastmax = fmaxf(ps ? key[1][LL - 1] : key[0][LL - 1],
+                          __shfl_xor(ps ? key[0][LL - 1] : key[1][LL - 1], 16));
+    lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
+    const bool overflow = lastmax > b;
+    // keys are within 2^(LB-23)|s| of the MFMA scores
+    const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
+    const float Er = E0 * sqrtf(ps ? qn2[1] : qn2[0]) * cmax + 1e-30f;   // MFMA score vs fp64 score
+    const float E = Er + dk;
+    const bool vp = ps ? valid[1] : valid[0];
+    const bool flag = overflow || !(a - b > 2.0f * E);
+    if (g4 < 2 && vp && !flag) {
+        int sel[KMAX];
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p) sel[p] = p < K - 1 ? key_block(mk[p], lmask) : 0x7fffffff;
+        sort_asc<KMAX>(sel);
+        int32_t* out = idx + ((size_t)(st.cu[s] + (ps ? tl[1] : tl[0])) * H + h) * K;
+#pragma unroll
+        for (int p = 0; p < KMAX; ++p)
+            if (p < K - 1) out[p] = sel[p];
+        out[K - 1] = i;
+    }
+    const uint64_t flagged = __ballot(vp && flag);
+    if (!flagged) return;
+
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        // merge the 4 lanes of a query (lanes l16 + 16*g4): two rounds of
-        // "top N of two sorted lists" -- c[p] = max(x[p], y[N-1-p]) is
-        // bitonic and holds the top N of both, a bitonic clean sorts it;
-        // afterwards all 4 lanes hold the query's sorted top N keys
-        float mk[KMAX];
-#pragma unroll
-        for (int p = 0; p < KMAX; ++p) mk[p] = key[sb][p];
-        merge_lanes<KMAX, KMAX>(mk);
-        float a = mk[0], b = mk[0];
-#pragma unroll
-        for (int p = 1; p < KMAX; ++p) {
-            a = (p == K - 2) ? mk[p] : a;
-            b = (p == K - 1) ? mk[p] : b;
-        }
-        // a lane whose last kept key is above b may have dropped one of the
-        // top K: then nothing here is trusted (overflow -> fp64 path)
-        const float mylast = key[sb][LL - 1];
-        float lastmax = fmaxf(mylast, __shfl_xor(mylast, 16));
-        lastmax = fmaxf(lastmax, __shfl_xor(lastmax, 32));
-        const bool overflow = lastmax > b;
-        // keys are within 2^(LB-23)|s| of the MFMA scores
-        const float dk = ldexpf(fmaxf(fabsf(a), fabsf(b)), LB - 23) * 1.02f;
-        const float Er = E0 * sqrtf(qn2[sb]) * cmax + 1e-30f;     // MFMA score vs fp64 score
-        const float E = Er + dk;
-        const bool flag = overflow || !(a - b > 2.0f * E);
-        if (g4 == 0 && valid[sb] && !flag) {
-            int sel[KMAX];
-#pragma unroll
-            for (int p = 0; p < KMAX; ++p) sel[p] = p < K - 1 ? key_block(mk[p], lmask) : 0x7fffffff;
-            sort_asc<KMAX>(sel);
-            int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
-#pragma unroll
-            for (int p = 0; p < KMAX; ++p)
-                if (p < K - 1) out[p] = sel[p];
-            out[K - 1] = i;
-        }
-        if (!__ballot(valid[sb] && flag)) continue;
+        // sub-tile sb's rows were finished by the lane groups of parity sb
+        if (!(flagged & (0x0000FFFF0000FFFFull << (16 * sb)))) continue;
+        const int src = l16 + 16 * sb;
+        const float as = __shfl(a, src), Es = __shfl(E, src), Ers = __shfl(Er, src);
+        const float lms = __shfl(lastmax, src);
+        const bool fls = __shfl((int)flag, src) != 0;
+        const bool ovs = __shfl((int)overflow, src) != 0;
 
         constexpr int MW = 2 * KMAX;
         float wk[MW];
@@ -620,12 +665,12 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
         // the F in fp64; if the (K-1)-th of them is above ub they hold the
         // selection.  Failing that (or with no room for a hint) the row is
         // marked for a full fp64 re-selection.
-        const float tlow = a - 2.0f * E;
+        const float tlow = as - 2.0f * Es;
         float next = wk[0];
 #pragma unroll
         for (int p = 1; p < MW; ++p) next = (p == K) ? wk[p] : next;
-        const bool cands = !overflow && next < tlow && lastmax < tlow;
-        if (g4 == 0 && valid[sb] && flag) {
+        const bool cands = !ovs && next < tlow && lms < tlow;
+        if (g4 == 0 && valid[sb] && fls) {
             int32_t* out = idx + ((size_t)(st.cu[s] + tl[sb]) * H + h) * K;
             if (cands) {
 #pragma unroll
@@ -636,9 +681,9 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
                 float kf = wk[0];
 #pragma unroll
                 for (int p = 1; p < MW; ++p) kf = (p == F) ? wk[p] : kf;
-                const float kn = fmaxf(kf, lastmax);
+                const float kn = fmaxf(kf, lms);
                 const float ub = kn == -INFINITY ? -INFINITY
-                                                 : (kn + ldexpf(fabsf(kn), LB - 22)) + Er;
+                                                 : (kn + ldexpf(fabsf(kn), LB - 22)) + Ers;
                 out[0] = kHint;
                 out[1] = __float_as_int(ub);
 #pragma unroll
