@@ -64,50 +64,69 @@ def _cpu_model() -> str:
     return ""
 
 
-def cpu_baseline(spec, x, nthreads=None):
+def cpu_baseline(spec, x, nthreads=None, budget_s=10.0):
     """The CPU oracle (as it stands) on a bounded sample of the workload: the
     whole forward (key conv when the workload has one, centroids, routing,
-    attention) of every head, on up to 16 threads (one (sequence, head) at a
-    time per thread).  The sample is the whole workload, except for the
-    512K-token sequence, whose first 131072 tokens are taken (its full
-    routing alone would take minutes).  C1 (one head, 1024 tokens) is also
-    timed on one thread."""
+    attention) of whole sequences with every head, on up to 16 threads (one
+    (sequence, head) at a time per thread).  Sequences are timed one after
+    another in their order until budget_s seconds have been spent or all of
+    them are done, so a slow host times fewer of them; the value is the
+    sampled sequences' effective FLOPs over their time.  A sequence longer
+    than 131072 tokens is cut to its first 131072 (the full routing of the
+    512K-token sequence alone would take minutes).  C1 (one head, 1024
+    tokens) is also timed on one thread."""
+    import dataclasses
+
     import oracle
 
     avail = len(os.sched_getaffinity(0))
-    threads = nthreads or min(16, avail)
+    threads = min(nthreads or min(16, avail), spec.heads)
     H = spec.heads
-    sample = spec
-    if spec.seqlens is None and spec.seq > 131072:
-        sample = spec.scaled(131072, "-prefix")
-        x = {n: (x[n][:, :131072] if n in ("q", "k", "v") else x[n]) for n in x}
-    q, k, v = (x[n].float().contiguous() for n in ("q", "k", "v"))
     w = x["conv_w"]
-    cu = x["cu_seqlens"] or workloads.segments(sample)
     mode = 0 if spec.conv_mode == "plain" else 1
     rb = spec.dtype == "bf16"
+    cap = 131072
+    # the workload's sequences as (q, k, v) token slices [L, H, d]
+    if spec.seqlens is not None:
+        cu = x["cu_seqlens"]
+        seqs = [tuple(x[n][cu[i]:cu[i + 1]] for n in ("q", "k", "v")) for i in range(len(cu) - 1)]
+    else:
+        seqs = [tuple(x[n][b] for n in ("q", "k", "v")) for b in range(spec.batch)]
+    cut = any(t[0].shape[0] > cap for t in seqs)
+    seqs = [tuple(a[:cap] for a in t) for t in seqs]
 
-    def run(th):
+    def run(t, th):
+        q, k, v = (a.float().contiguous() for a in t)
+        L = q.shape[0]
         t0 = time.perf_counter()
-        oracle.forward(q, k, v, spec.block_size, spec.top_k, cu, conv_w=w, conv_mode=mode,
+        oracle.forward(q, k, v, spec.block_size, spec.top_k, [0, L], conv_w=w, conv_mode=mode,
                        round_bf16=rb, nthreads=th)
         return time.perf_counter() - t0
 
-    # the oracle runs one (sequence, head) per thread at a time
-    threads = min(threads, (len(cu) - 1) * H)
-    dt = run(threads)
-    f_sample = workloads.eff_flops(sample)["total"]
+    def flops(L):
+        one = dataclasses.replace(spec, batch=1, seq=L, seqlens=None)
+        return workloads.eff_flops(one)["total"]
+
+    dt, f_sample, ntok, done = 0.0, 0, 0, 0
+    for t in seqs:
+        dt += run(t, threads)
+        f_sample += flops(t[0].shape[0])
+        ntok += t[0].shape[0]
+        done += 1
+        if dt >= budget_s:
+            break
     steps = ("key conv, " if w is not None else "") + "centroids, routing, attention"
-    what = ("the whole workload" if sample is spec else
-            f"the first {sample.seq} tokens of each of the {sample.batch} sequence(s)")
+    what = (f"{done} of the {len(seqs)} sequence(s)" + (f" (each cut to its first {cap} tokens)" if cut else "")
+            + f", {ntok} tokens")
     out = {
         "value": f_sample / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
         "sample": f"{what}, all {H} heads: full forward ({steps}) in fp64 C on {threads} "
-                  f"threads; {dt:.1f} s; cpu: {_cpu_model()}",
+                  f"threads; {dt:.1f} s (sequences are added until {budget_s:.0f} s are spent); "
+                  f"cpu: {_cpu_model()}",
         "seconds": dt,
     }
     if spec.name == "C1":
-        dt1 = run(1)
+        dt1 = sum(run(t, 1) for t in seqs[:done])
         out["single_thread"] = {"value": f_sample / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1,
                                 "seconds": dt1}
     return out
