@@ -738,7 +738,10 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
             int j = 0x7fffffff;
             int32_t* row = nullptr;
             if (src >= 0) row = idx + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * K;
-            if (src >= 0 && p < K) {
+            // (a candidate is a past block whenever the scores are finite;
+            // the check keeps the centroid read inside the sequence's rows
+            // when a query or centroid holds a NaN)
+            if (src >= 0 && p < K && -row[p] - 2 >= 0 && -row[p] - 2 < i) {
                 j = -row[p] - 2;
                 const uint16_t* qp = q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D;
                 const float4* cp = (const float4*)(cbase + (size_t)j * H * D);

@@ -38,6 +38,12 @@
  *     support matrix below), MOBA_ERR_WORKSPACE_TOO_SMALL.  A failed launch
  *     returns MOBA_ERR_HIP.  Device faults surface at the caller's next sync.
  *     Nothing is printed, nothing throws.
+ *   - Non-finite inputs: a NaN or infinity in a query row leaves that row's
+ *     selection and output unspecified and every other row as it would be
+ *     without it; one in k, v or a centroid leaves the rows that read it
+ *     unspecified.  In every case the calls touch only the buffers they are
+ *     given (block ids outside [0, own block) in idx are ignored by the
+ *     attention calls).
  *   - Calls are stateless and may be issued from several host threads.
  *   - A call over more sequences than one launch table holds
  *     (MOBA_MAX_SEQS, a varlen batch or a uniform batch of more rows) runs
