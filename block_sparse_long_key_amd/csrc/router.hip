@@ -717,6 +717,29 @@ __global__ __launch_bounds__(2 * BLK, ((D == 64 && KMAX <= 8) ? 4 : 1)) void rou
 // candidate): the lane re-scores its candidate, ranks it against the row's
 // others by shuffles, and the K-1 best are written in ascending block order,
 // the own block last.
+// fp64 score of a bf16 query row against an fp32 centroid row, summed
+// sequentially over the channels (every product is exact in fp64)
+template <int D>
+__device__ __forceinline__ double score64(const uint16_t* qp, const float* crow)
+{
+    const float4* cp = (const float4*)crow;
+    double acc = 0.0;
+#pragma unroll
+    for (int c8 = 0; c8 < D / 8; ++c8) {
+        const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
+        const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
+        acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
+        acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
+        acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
+        acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
+        acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
+        acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
+        acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
+        acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
+    }
+    return acc;
+}
+
 template <int D, int BLK, int KMAX>
 __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uint16_t* __restrict__ q,
                                                    const float* cbase, int32_t* __restrict__ idx,
@@ -743,23 +766,8 @@ __device__ __forceinline__ void fix_candidate_rows(const SegTable& st, const uin
             // when a query or centroid holds a NaN)
             if (src >= 0 && p < K && -row[p] - 2 >= 0 && -row[p] - 2 < i) {
                 j = -row[p] - 2;
-                const uint16_t* qp = q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D;
-                const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
-                double acc = 0.0;
-#pragma unroll
-                for (int c8 = 0; c8 < D / 8; ++c8) {
-                    const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
-                    const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
-                    acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
-                    acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
-                    acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
-                    acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
-                    acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
-                    acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
-                    acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
-                    acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
-                }
-                sc = acc;
+                sc = score64<D>(q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D,
+                                cbase + (size_t)j * H * D);
             }
             // rank against the row's candidates; the last-ranked is dropped
             int rank = 0, pos = 0;
@@ -820,23 +828,8 @@ __device__ __forceinline__ uint64_t fix_hint_rows(const SegTable& st, const uint
                 const int id = (int)((p & 1) ? (w >> 16) : (w & 0xffffu));
                 if (id != kHintNone) {
                     j = id;
-                    const uint16_t* qp = q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D;
-                    const float4* cp = (const float4*)(cbase + (size_t)j * H * D);
-                    double acc = 0.0;
-#pragma unroll
-                    for (int c8 = 0; c8 < D / 8; ++c8) {
-                        const u32x4_t qw = *(const u32x4_t*)(qp + 8 * c8);
-                        const float4 c0 = cp[2 * c8], c1 = cp[2 * c8 + 1];
-                        acc = __builtin_fma((double)bf16_lo(qw[0]), (double)c0.x, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[0]), (double)c0.y, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[1]), (double)c0.z, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[1]), (double)c0.w, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[2]), (double)c1.x, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[2]), (double)c1.y, acc);
-                        acc = __builtin_fma((double)bf16_lo(qw[3]), (double)c1.z, acc);
-                        acc = __builtin_fma((double)bf16_hi(qw[3]), (double)c1.w, acc);
-                    }
-                    sc = acc;
+                    sc = score64<D>(q + ((size_t)(st.cu[s] + i * BLK + r0 + src) * H + h) * D,
+                                    cbase + (size_t)j * H * D);
                 }
             }
         }
