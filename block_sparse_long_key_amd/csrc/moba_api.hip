@@ -381,6 +381,17 @@ moba_status route_topk_one(const moba_shape* shape, const void* q, const float* 
     return hip_status(launch_route(L, q, cent, workspace, idx));
 }
 
+// whether one group's routing workspace fits the fixed scratch buffer
+moba_status route_noalloc_fits(const moba_shape* shape)
+{
+    Launch L;
+    const moba_status st = make_launch(shape, &L, nullptr);
+    if (st != MOBA_OK) return st;
+    if (L.dtype == MOBA_BF16 && route_ws_bytes(L) > (size_t)MOBA_ROUTE_SCRATCH_BYTES)
+        return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    return MOBA_OK;
+}
+
 moba_status route_topk_noalloc_one(const moba_shape* shape, const void* q, const float* cent,
                                     int32_t* idx, hipStream_t stream)
 {
@@ -388,8 +399,8 @@ moba_status route_topk_noalloc_one(const moba_shape* shape, const void* q, const
     moba_status st = make_launch(shape, &L, stream);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(q) || !ptr_ok(cent) || !idx_ok(idx)) return MOBA_ERR_INVALID_ARG;
-    if (L.dtype == MOBA_BF16 && route_ws_bytes(L) > (size_t)MOBA_ROUTE_SCRATCH_BYTES)
-        return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    st = route_noalloc_fits(shape);
+    if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
     void* ws = nullptr;
     hipError_t e = route_scratch(&ws);
@@ -707,6 +718,13 @@ moba_status moba_route_topk_noalloc(const moba_shape* shape, const void* q, cons
 {
     MOBA_GROUPS(shape);
     if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
+    // every group must fit the scratch buffer before the first launch
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const moba_status st = one::route_noalloc_fits(&gr.sh);
+        if (st != MOBA_OK) return st;
+    }
     const size_t row = (size_t)shape->heads * shape->head_dim;
     const size_t irow = (size_t)shape->heads * (shape->top_k > 0 ? shape->top_k : 0) * 4;
     for (int g = 0; g < G.n; ++g) {

@@ -276,6 +276,12 @@ def test_route_noalloc_refuses_shapes_beyond_its_scratch(lib):
     need = lib.moba_route_topk_workspace_bytes(ctypes.byref(big))
     assert need > 32 << 20
     assert lib.moba_route_topk_noalloc(ctypes.byref(big), fake, fake, fake, None) == WS_SMALL
+    # more sequences than one launch group: the second group alone (one
+    # 262144-token sequence of 64 heads) is too big, and the call is refused
+    # before the first group is launched (no HIP call is made at all here)
+    cu = [128 * n for n in range(65)] + [128 * 64 + 262144]
+    multi = _shape(cu=cu, heads=64, d=64, B=64, K=8)
+    assert lib.moba_route_topk_noalloc(ctypes.byref(multi), fake, fake, fake, None) == WS_SMALL
     # invalid arguments are still refused as such
     assert lib.moba_route_topk_noalloc(ctypes.byref(_shape()), None, fake, fake, None) == INVALID
     assert lib.moba_route_topk_noalloc(ctypes.byref(_shape(d=96)), fake, fake, fake, None) == UNSUPPORTED
