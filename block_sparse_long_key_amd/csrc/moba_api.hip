@@ -368,15 +368,27 @@ size_t route_topk_workspace_bytes_one(const moba_shape* shape)
     return std::max(route_ws_bytes(L), (size_t)256);
 }
 
-moba_status route_topk_one(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+// every check of moba_route_topk on one group, without launching
+moba_status route_topk_ok(const moba_shape* shape, const void* q, const float* cent,
+                          const int32_t* idx, const void* workspace, size_t workspace_bytes)
 {
     Launch L;
-    moba_status st = make_launch(shape, &L, stream);
+    moba_status st = make_launch(shape, &L, nullptr);
     if (st != MOBA_OK) return st;
     if (!ptr_ok(q) || !ptr_ok(cent) || !idx_ok(idx)) return MOBA_ERR_INVALID_ARG;
     if (!workspace || ((uintptr_t)workspace & 255u) != 0) return MOBA_ERR_INVALID_ARG;
     if (workspace_bytes < std::max(route_ws_bytes(L), (size_t)256)) return MOBA_ERR_WORKSPACE_TOO_SMALL;
+    return MOBA_OK;
+}
+
+moba_status route_topk_one(const moba_shape* shape, const void* q, const float* cent, int32_t* idx,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    moba_status st = route_topk_ok(shape, q, cent, idx, workspace, workspace_bytes);
+    if (st != MOBA_OK) return st;
+    Launch L;
+    st = make_launch(shape, &L, stream);
+    if (st != MOBA_OK) return st;
     if (L.tokens == 0) return MOBA_OK;
     return hip_status(launch_route(L, q, cent, workspace, idx));
 }
@@ -702,6 +714,15 @@ moba_status moba_route_topk(const moba_shape* shape, const void* q, const float*
     if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
     const size_t row = (size_t)shape->heads * shape->head_dim;
     const size_t irow = (size_t)shape->heads * (shape->top_k > 0 ? shape->top_k : 0) * 4;
+    // every group is checked (arguments, workspace size) before the first launch
+    for (int g = 0; g < G.n; ++g) {
+        Group gr;
+        group(G, g, &gr);
+        const moba_status st = one::route_topk_ok(&gr.sh, at(q, gr.tok0, row * esize(shape)),
+                                                  at(cent, gr.blk0, row * 4), at(idx, gr.tok0, irow),
+                                                  workspace, workspace_bytes);
+        if (st != MOBA_OK) return st;
+    }
     for (int g = 0; g < G.n; ++g) {
         Group gr;
         group(G, g, &gr);
@@ -745,6 +766,8 @@ moba_status moba_route_topk_noalloc(const moba_shape* shape, const void* q, cons
     (void)row; (void)irow; (void)lrow;                                                  \
     const size_t need_ = (bwd_) ? moba_attn_bwd_workspace_bytes(shape)                   \
                                 : moba_attn_fwd_workspace_bytes(shape);                  \
+    if (G.n > 1 && need_ > 0 && (!workspace || ((uintptr_t)workspace & 255u) != 0))    \
+        return MOBA_ERR_INVALID_ARG;                                                    \
     if (G.n > 1 && workspace_bytes < need_) return MOBA_ERR_WORKSPACE_TOO_SMALL;        \
     size_t wsoff = 0;
 

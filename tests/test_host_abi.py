@@ -282,6 +282,15 @@ def test_route_noalloc_refuses_shapes_beyond_its_scratch(lib):
     cu = [128 * n for n in range(65)] + [128 * 64 + 262144]
     multi = _shape(cu=cu, heads=64, d=64, B=64, K=8)
     assert lib.moba_route_topk_noalloc(ctypes.byref(multi), fake, fake, fake, None) == WS_SMALL
+    # the same for moba_route_topk with a caller's workspace that holds the
+    # first group's routing data but not the second's
+    small = lib.moba_route_topk_workspace_bytes(ctypes.byref(_shape(cu=cu[:65], heads=64, d=64, B=64, K=8)))
+    assert 0 < small < lib.moba_route_topk_workspace_bytes(ctypes.byref(multi))
+    wsp = ctypes.c_void_p(1 << 24)             # 256-byte aligned, never dereferenced
+    assert lib.moba_route_topk(ctypes.byref(multi), fake, fake, fake, wsp, small, None) == WS_SMALL
+    # and a multi-group attention call without a workspace
+    assert lib.moba_attn_fwd(ctypes.byref(multi), fake, fake, fake, fake, ctypes.c_float(0.0), fake,
+                             None, None, 0, None) == INVALID
     # invalid arguments are still refused as such
     assert lib.moba_route_topk_noalloc(ctypes.byref(_shape()), None, fake, fake, None) == INVALID
     assert lib.moba_route_topk_noalloc(ctypes.byref(_shape(d=96)), fake, fake, fake, None) == UNSUPPORTED
