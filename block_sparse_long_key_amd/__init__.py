@@ -156,6 +156,11 @@ def _dev(*ts: torch.Tensor):
             continue
         if not t.is_cuda:
             raise MobaError("tensors must be on the GPU")
+        # the kernels run on the current device: a tensor elsewhere would be
+        # read through a foreign pointer
+        if t.device.index != torch.cuda.current_device():
+            raise MobaError(f"tensors must be on the current device (cuda:{torch.cuda.current_device()}), "
+                            f"got {t.device}")
         if not t.is_contiguous():
             raise MobaError("tensors must be contiguous")
 
