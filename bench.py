@@ -132,6 +132,15 @@ def cpu_baseline(spec, x, nthreads=None, budget_s=10.0):
     return out
 
 
+def _memory(dev, workspace_bytes):
+    """Device memory of the step: the workspace, and torch's peak allocated
+    bytes over the warm-up and timed steps (inputs, outputs, centroids, idx
+    and workspaces: the library itself allocates nothing)."""
+    return {"workspace_bytes": int(workspace_bytes),
+            "peak_allocated_bytes": int(torch.cuda.max_memory_allocated(dev)),
+            "peak_allocated_GiB": round(torch.cuda.max_memory_allocated(dev) / 2**30, 3)}
+
+
 def _calib_copy(args, dev):
     """One plain device copy of --calib-copy-mib MiB (a kernel of known size
     for scaling the HBM byte counters)."""
@@ -221,6 +230,7 @@ def main():
         mark(5)
 
     _calib_copy(args, dev)
+    torch.cuda.reset_peak_memory_stats(dev)
 
     for _ in range(args.warmup):
         step()
@@ -302,6 +312,7 @@ def main():
                              if traffic else None),
         },
     }
+    out["memory"] = _memory(dev, ws.numel())
     out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(spec, x)
     print(json.dumps(out), flush=True)
 
@@ -339,6 +350,7 @@ def bench_bwd(args, moba):
             # dL/dk' -> dL/dk and dL/dw through the key convolution
             moba.moba_key_conv_bwd(k, w, dk, B, spec.conv_mode, cu_seqlens=cu, workspace=wsc)
 
+    torch.cuda.reset_peak_memory_stats(dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -367,7 +379,7 @@ def bench_bwd(args, moba):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. N(0,1) q/k/v/dO, CPU torch.Generator)",
         "config": {"workload": f"moba_attn_bwd {spec.name}: {spec.desc}",
                    "batch": spec.batch, "seq_len": spec.seq, "heads": spec.heads,
@@ -376,6 +388,7 @@ def bench_bwd(args, moba):
         "pct_of_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "event_ms_median": round(sorted(ms_ev)[len(ms_ev) // 2], 4),
         "event_ms_min": round(min(ms_ev), 4),
+        "memory": _memory(dev, ws.numel() + (wsc.numel() if wsc is not None else 0)),
     }
     print(json.dumps(out), flush=True)
 
