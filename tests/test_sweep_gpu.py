@@ -25,7 +25,7 @@ import test_parity_gpu as tp  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-NCASES = 64
+NCASES = int(os.environ.get("MOBA_SWEEP_CASES", "192"))   # more cases on request
 
 
 def _draw(i):
@@ -89,5 +89,12 @@ def test_random_shape_matches_oracle(i):
                                  cu_seqlens=cu, scale=c["scale"])
     torch.cuda.synchronize()
     rq, rk, rv = oracle.attend_bwd(q, kc, v, ref["idx"], do, B, K, cu, scale=c["scale"] or 0.0)
+    # bound for an exactly-zero reference (every query attends one key): dS
+    # is the difference of two fp32 dot products over d channels, each
+    # within about d 2^-24 sum |dO_c v_c|; dq / dk' scale it by the softmax
+    # scale and |k| / |q| (8x margin)
+    sc = c["scale"] or d ** -0.5
+    mag = d * float(do.float().abs().max()) * float(v.float().abs().max())
+    ztol = 8 * d * 2.0 ** -24 * mag * sc * max(float(kc.float().abs().max()), float(q.float().abs().max()))
     for got, r, what in ((dq, rq, "dq"), (dk, rk, "dk'"), (dv, rv, "dv")):
-        tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype)
+        tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype, zero_tol=ztol)
