@@ -48,11 +48,20 @@ def _flat(x, H):
     return a.reshape(-1, H, a.shape[-1])
 
 
-def _check_o(o_gpu, lse_gpu, o_ref, lse_ref, dtype, rows=None, what=""):
+def _check_o(o_gpu, lse_gpu, o_ref, lse_ref, dtype, rows=None, what="", out_round=False):
+    """O and LSE against the oracle.  out_round: the max bar counts only the
+    error beyond the rounding of each output to bf16 itself (half an ulp of
+    |O_ref|), which no bf16 result can avoid and which the absolute bar
+    leaves out once |O| grows past 1 (sharp softmax scales)."""
     mx, mean, ltol = _tol(dtype)
     o = _np(o_gpu).reshape(o_ref.shape[0], -1, o_ref.shape[-1]) if rows is None else o_gpu
     err = np.abs(o.astype(np.float64) - o_ref)
-    assert err.max() <= mx, f"{what} max |O err| {err.max():.3e} > {mx}"
+    if out_round:
+        half_ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(o_ref), 1e-30))) - 8)
+        over = (err - half_ulp).max()
+        assert over <= mx, f"{what} max |O err| beyond the output rounding {over:.3e} > {mx}"
+    else:
+        assert err.max() <= mx, f"{what} max |O err| {err.max():.3e} > {mx}"
     assert err.mean() <= mean, f"{what} mean |O err| {err.mean():.3e} > {mean}"
     if lse_gpu is not None:
         l = _np(lse_gpu).reshape(lse_ref.shape) if rows is None else lse_gpu
@@ -71,7 +80,7 @@ def _assert_exact(drows, what):
                              f"(valid, but the router claims an exact selection)")
 
 
-def _verify_forward(o, lse, idx, ref, q, kc, v, B, K, cu, dtype, what, scale=0.0):
+def _verify_forward(o, lse, idx, ref, q, kc, v, B, K, cu, dtype, what, scale=0.0, out_round=False):
     """Whole-array check of one forward: selection (P3) on every row, O and
     LSE (P4) on every row against the oracle's attention on the same
     selection (the GPU's own row where the selections differ), then
@@ -88,7 +97,7 @@ def _verify_forward(o, lse, idx, ref, q, kc, v, B, K, cu, dtype, what, scale=0.0
                                                  scale=scale)
         o_ref[drows], lse_ref[drows] = ro, rl
     _check_o(_np(o).reshape(-1, d), None if lse is None else _np(lse).reshape(-1), o_ref, lse_ref,
-             dtype, rows=True, what=what)
+             dtype, rows=True, what=what, out_round=out_round)
     _assert_exact(drows, what)
 
 

@@ -77,8 +77,14 @@ def test_random_shape_matches_oracle(i):
     if w is not None:
         got = tp._np(kk).reshape(ref["k_conv"].shape)
         assert np.array_equal(got, ref["k_conv"]), f"k' differs in {int((got != ref['k_conv']).sum())} elements"
+    # the drawn softmax scales reach 3.4x 1/sqrt(d): outputs near single v
+    # rows, |O| up to ~4, so the O bar counts the error beyond O's own bf16
+    # rounding, and the backward's max bar is 1.5e-2 (~8u) where the scale is
+    # sharper than 1/sqrt(d) (fewer keys average out the bf16 roundings of
+    # P and dS); the mean bars are unchanged
+    sharp = c["scale"] is not None and c["scale"] > d ** -0.5
     tp._verify_forward(o, lse, idx, ref, q, ref["k_conv"], v, B, K, cu, dtype, f"sweep {i}",
-                       scale=c["scale"] or 0.0)
+                       scale=c["scale"] or 0.0, out_round=(dtype == "bf16"))
     if i % 3:
         return
     # backward for the GPU's selection (equal to the oracle's: exactness was
@@ -97,4 +103,5 @@ def test_random_shape_matches_oracle(i):
     mag = d * float(do.float().abs().max()) * float(v.float().abs().max())
     ztol = 8 * d * 2.0 ** -24 * mag * sc * max(float(kc.float().abs().max()), float(q.float().abs().max()))
     for got, r, what in ((dq, rq, "dq"), (dk, rk, "dk'"), (dv, rv, "dv")):
-        tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype, zero_tol=ztol)
+        tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype, zero_tol=ztol,
+                  max_bar=1.5e-2 if (sharp and dtype == "bf16") else None)
