@@ -26,6 +26,7 @@ import test_parity_gpu as tp  # noqa: E402
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 NCASES = int(os.environ.get("MOBA_SWEEP_CASES", "192"))   # more cases on request
+FIRST = int(os.environ.get("MOBA_SWEEP_FIRST", "0"))      # index of the first case
 
 
 def _draw(i):
@@ -51,7 +52,7 @@ def _draw(i):
     return dict(dtype=dtype, d=d, B=B, K=K, H=H, lens=lens, W=W, mode=mode, scale=scale)
 
 
-@pytest.mark.parametrize("i", range(NCASES))
+@pytest.mark.parametrize("i", range(FIRST, FIRST + NCASES))
 def test_random_shape_matches_oracle(i):
     c = _draw(i)
     print(f"[sweep {i}] {c}", flush=True)
