@@ -20,6 +20,7 @@ import torch
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 import oracle  # noqa: E402
+import test_blasst_gpu as tbl  # noqa: E402
 import test_bwd_gpu as tb  # noqa: E402
 import test_parity_gpu as tp  # noqa: E402
 
@@ -27,6 +28,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 NCASES = int(os.environ.get("MOBA_SWEEP_CASES", "192"))   # more cases on request
 FIRST = int(os.environ.get("MOBA_SWEEP_FIRST", "0"))      # index of the first case
+NBLASST = int(os.environ.get("MOBA_SWEEP_BLASST_CASES", "48"))
 
 
 def _draw(i):
@@ -106,3 +108,25 @@ def test_random_shape_matches_oracle(i):
     for got, r, what in ((dq, rq, "dq"), (dk, rk, "dk'"), (dv, rv, "dv")):
         tb._check(f"sweep {i}", tp._np(got).reshape(-1, H, d), r, what, dtype, zero_tol=ztol,
                   max_bar=1.5e-2 if (sharp and dtype == "bf16") else None)
+
+
+@pytest.mark.parametrize("i", range(FIRST, FIRST + NBLASST))
+def test_random_blasst_matches_oracle(i):
+    """The BLASST skip ("BLASST", summary page, "Meccanismo di Pruning") on a
+    drawn shape: blocks the attention kernels take whole (B <= 128; 64 for
+    fp32 at d = 128), a drawn lambda, the default scale; the bar and the
+    treatment of near-threshold decisions are those of test_blasst_gpu."""
+    c = _draw(i)
+    dtype, d, K, H, lens = c["dtype"], c["d"], c["K"], c["H"], c["lens"]
+    B = min(c["B"], 64 if (dtype == "f32" and d == 128) else 128)
+    lam = float(np.random.default_rng(9900 + i).uniform(0.05, 0.95))
+    print(f"[sweep-blasst {i}] {dict(c, B=B)} lambda={lam:.3f}", flush=True)
+    T = sum(lens)
+    g = torch.Generator().manual_seed(9300 + i)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    x = {n: torch.randn((T, H, d), generator=g).to(dt) for n in ("q", "k", "v")}
+    cu = [0]
+    for L in lens:
+        cu.append(cu[-1] + L)
+    x["cu_seqlens"] = cu
+    tbl.check_blasst(x, cu, B, K, lam, dtype, f"sweep-blasst {i}")
