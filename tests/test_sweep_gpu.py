@@ -88,6 +88,18 @@ def test_random_shape_matches_oracle(i):
     sharp = c["scale"] is not None and c["scale"] > d ** -0.5
     tp._verify_forward(o, lse, idx, ref, q, ref["k_conv"], v, B, K, cu, dtype, f"sweep {i}",
                        scale=c["scale"] or 0.0, out_round=(dtype == "bf16"))
+    if w is not None:
+        # key conv backward for a drawn dL/dk' (the fixed conv cases' bar:
+        # dk one rounding to the I/O dtype, dw within 1e-5 of max |dw|)
+        gkc = torch.randn((T, H, d), generator=g).to(dt)
+        dkx, dwx = m.moba_key_conv_bwd(gk, w.to(DEV), gkc.to(DEV), B, c["mode"], cu_seqlens=cu)
+        torch.cuda.synchronize()
+        rkx, rwx = oracle.key_conv_bwd(k, w.numpy(), gkc, cu, mode)
+        ekx = np.abs(tp._np(dkx).reshape(-1, H, d).astype(np.float64) - rkx)
+        rel = 2.0 ** -8 if dtype == "bf16" else 1e-6
+        assert np.all(ekx <= rel * np.abs(rkx) + 1e-6 * np.abs(rkx).max()), f"sweep {i} conv dk max err {ekx.max():.3e}"
+        ewx = np.abs(dwx.cpu().numpy().astype(np.float64) - rwx)
+        assert ewx.max() <= 1e-5 * max(np.abs(rwx).max(), 1e-30), f"sweep {i} conv dw max err {ewx.max():.3e}"
     if i % 3:
         return
     # backward for the GPU's selection (equal to the oracle's: exactness was
