@@ -59,10 +59,10 @@ def _load():
         lib.moba_oracle_attend_rows.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _P, _I, _P, _P]
         lib.moba_oracle_route_scores.argtypes = [_P, _P, _I, _I, _I, _P, _I, _P, _I, _I, _P]
         lib.moba_oracle_attend_blasst.argtypes = [_P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D, _D,
-                                                  _P, _P, _D, _P, _P, _P, _I]
+                                                  _P, _P, _D, _P, _P, _P, _P, _I]
         lib.moba_oracle_attend_blasst.restype = _I
         lib.moba_oracle_route_scores.restype = _I
-        lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
+        lib.moba_oracle_attend_bwd.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _I, _D,
                                                _P, _P, _P, _P, _P, _I]
         lib.moba_oracle_attend_bwd.restype = _I
         lib.moba_oracle_key_conv_bwd.argtypes = [_P, _P, _P, _I, _I, _I, _I, _P, _I, _P, _P, _I]
@@ -194,7 +194,8 @@ def forward(q, k, v, B: int, K: int, cu, conv_w=None, conv_mode: int = 0,
 
 
 def attend_blasst(q, k, v, idx, B: int, K: int, cu, lam: float, scale: float = 0.0,
-                  keep=None, flip=None, tau: float = 1e-4, nthreads: Optional[int] = None):
+                  keep=None, flip=None, tau: float = 1e-4, nthreads: Optional[int] = None,
+                  return_keep: bool = False):
     """Step 5 with the BLASST block skip (blocks visited in ascending order,
     own block last; a block whose maximum score is below the running maximum
     of the attended scores + ln(lam) is skipped).  lam = 0 keeps every block.
@@ -203,7 +204,9 @@ def attend_blasst(q, k, v, idx, B: int, K: int, cu, lam: float, scale: float = 0
     per idx slot.  flip (uint64 [T, H], optional) takes the near decisions
     whose bit is set the other way.  Returns (o f64 [T,H,d], lse f64 [T,H],
     near uint64 [T,H]): bit b of near marks a decision on the b-th visited
-    block within tau * max(1, |M|) of the threshold.
+    block within tau * max(1, |M|) of the threshold.  With return_keep, a
+    fourth result holds the decisions taken (bool [T, H, K]: True where the
+    slot's block was attended, own block included).
     """
     import math
     q, k, v = _f32(q), _f32(k), _f32(v)
@@ -220,13 +223,17 @@ def attend_blasst(q, k, v, idx, B: int, K: int, cu, lam: float, scale: float = 0
     if flip is not None:
         fl = np.ascontiguousarray(np.asarray(flip, dtype=np.uint64).reshape(T, H))
     ll = math.log(lam) if lam > 0 else -math.inf
+    ko = np.zeros((T, H, K), dtype=np.uint8) if return_keep else None
     rc = _load().moba_oracle_attend_blasst(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), H, d, B, K,
                                            _ptr(c), len(c) - 1, float(scale), float(ll),
                                            None if kp is None else _ptr(kp),
                                            None if fl is None else _ptr(fl), float(tau),
                                            _ptr(o), _ptr(lse), _ptr(near),
+                                           None if ko is None else _ptr(ko),
                                            nthreads or default_threads())
     assert rc == 0
+    if return_keep:
+        return o, lse, near, ko.astype(bool)
     return o, lse, near
 
 
@@ -290,17 +297,22 @@ def attend_rows(q, k, v, idx, B: int, K: int, cu, rows, scale: float = 0.0):
 
 
 def attend_bwd(q, k, v, idx, dout, B: int, K: int, cu, scale: float = 0.0,
-               qsel=None, kbsel=None, nthreads: Optional[int] = None):
+               qsel=None, kbsel=None, nthreads: Optional[int] = None, keep=None):
     """Gradients of the attention output for the fixed selection idx.
 
     dout is dL/dO ([T, H, d]).  Returns (dq, dk, dv), f64 [T, H, d].
     qsel (bool [T, H]) limits the rows whose dq is computed, kbsel (bool
     [total_blocks, H]) the key blocks whose dk / dv are computed; entries
-    outside them are NaN.
+    outside them are NaN.  keep (bool [T, H, K], optional): the BLASST
+    decisions per idx slot (as attend_blasst's keep); only the kept blocks'
+    keys, the own block's included, are in a row's key set.
     """
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     T, H, d = q.shape
     idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(T, H, K)
+    kp = None
+    if keep is not None:
+        kp = np.ascontiguousarray(np.asarray(keep, dtype=np.uint8).reshape(T, H, K))
     c = _cu(cu)
     dq = np.full((T, H, d), np.nan)
     dk = np.full((T, H, d), np.nan)
@@ -309,7 +321,8 @@ def attend_bwd(q, k, v, idx, dout, B: int, K: int, cu, scale: float = 0.0,
     ks = None if kbsel is None else np.ascontiguousarray(np.asarray(kbsel, dtype=np.uint8))
     if ks is not None:
         assert ks.shape == (total_blocks(cu, B), H)
-    rc = _load().moba_oracle_attend_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(dout),
+    rc = _load().moba_oracle_attend_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(idx),
+                                        None if kp is None else _ptr(kp), _ptr(dout),
                                         H, d, B, K, _ptr(c), len(c) - 1, float(scale),
                                         None if qs is None else _ptr(qs),
                                         None if ks is None else _ptr(ks),

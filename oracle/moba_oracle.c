@@ -445,6 +445,9 @@ int moba_oracle_attend(const float *q, const float *k, const float *v,
  *   decision that a different rounding of the scores may take the other
  *   way); flip (optional, uint64 per row): such near decisions whose bit is
  *   set are taken the other way (the later ones still follow the rule).
+ *   keep_out (optional, uint8 [rows][K]): the decisions taken, per slot:
+ *   1 where the slot's block was attended (the own block's slot included),
+ *   0 for skipped blocks and for slots that name no block of the row.
  * ===================================================================== */
 typedef struct {
     attn_ctx a;
@@ -452,6 +455,7 @@ typedef struct {
     const unsigned char *keep;
     const unsigned long long *flip;
     unsigned long long *near;
+    unsigned char *keep_out;
 } blasst_ctx;
 
 static void blasst_one(blasst_ctx *c, int s, int h, int tl, double *z, int *keys,
@@ -510,6 +514,12 @@ static void blasst_one(blasst_ctx *c, int s, int h, int tl, double *z, int *keys
         kept[b] = kb;
     }
     if (c->near) c->near[r] = near;
+    if (c->keep_out) {
+        unsigned char *ko = c->keep_out + r * a->K;
+        for (int p = 0; p < a->K; ++p) ko[p] = 0;
+        for (int b = 0; b < nb; ++b)
+            if (bslot[b] >= 0) ko[bslot[b]] = (unsigned char)(kept[b] != 0);
+    }
     /* softmax over the kept blocks' keys */
     double Mk = -INFINITY;
     for (int b = 0; b < nb; ++b) {
@@ -556,12 +566,12 @@ int moba_oracle_attend_blasst(const float *q, const float *k, const float *v,
                               const int *cu, int nseq, double scale, double log_lambda,
                               const unsigned char *keep, const unsigned long long *flip,
                               double tau, double *o, double *lse, unsigned long long *near,
-                              int nthreads)
+                              unsigned char *keep_out, int nthreads)
 {
     if (B < 1 || K < 1 || K > 63) return 1;
     if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
     blasst_ctx c = {{q, k, v, idx, o, lse, cu, H, d, B, K, scale}, log_lambda, tau, keep, flip,
-                    near};
+                    near, keep_out};
     run_jobs(blasst_job, &c, nseq * H, nthreads);
     return 0;
 }
@@ -680,10 +690,18 @@ int moba_oracle_attend_rows(const float *q, const float *k, const float *v,
  * written; kbsel (uint8 per (global block, head), NULL = all) picks the key
  * blocks whose dk / dv are written.  Unpicked outputs are left untouched;
  * picked dk / dv are overwritten with the sum over every row.
+ * keep (optional, uint8 [rows][K]): the backward of the BLASST variant of
+ * step 5 for fixed decisions (BLASST page, "Meccanismo di Pruning", and its
+ * sparsity-aware training): slot p's block is in the key set iff
+ * keep[row][p] != 0, the own block included (its slot is the one with
+ * idx == i; a row that lists no own block keeps it), as in the BLASST
+ * forward with an explicit keep.  The skip decisions are piecewise constant
+ * in q and k, so, as for the router, nothing flows through them.
  * ===================================================================== */
 typedef struct {
     const float *q, *k, *v, *dout;
     const int *idx;
+    const unsigned char *keep;
     const unsigned char *qsel, *kbsel;
     double *dq, *dk, *dv;
     const int *cu, *boff;
@@ -713,19 +731,27 @@ static void bwd_job(void *vctx, int job)
         size_t t = (size_t)(t0 + tl);
         int i = tl / c->B;
         const int *row = c->idx + (t * H + h) * c->K;
-        int nk = 0;
+        const unsigned char *kp = c->keep ? c->keep + (t * H + h) * c->K : NULL;
+        int nk = 0, own = 1;
         for (int p = 0; p < c->K; ++p) {
             int j = row[p];
-            if (j < 0 || j >= i) continue;
+            if (kp && j == i) own = kp[p] != 0;
+            if (j < 0 || j >= i || (kp && !kp[p])) continue;
             for (int u = j * c->B; u < (j + 1) * c->B && u < L; ++u) keys[nk++] = u;
         }
-        for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
+        if (own)
+            for (int u = i * c->B; u <= tl; ++u) keys[nk++] = u;
         /* is this row needed at all? */
         int want_q = !c->qsel || c->qsel[t * H + h];
         int want_k = 0;
         for (int e = 0; e < nk && !want_k; ++e)
             want_k = !c->kbsel || c->kbsel[(size_t)(c->boff[s] + keys[e] / c->B) * H + h];
         if (!want_q && !want_k) continue;
+        if (nk == 0) {                           /* every block dropped: no keys, no gradient */
+            double *dqr = c->dq + (t * H + h) * d;
+            for (int ch = 0; ch < d; ++ch) dqr[ch] = 0.0;
+            continue;
+        }
         const float *qv = c->q + (t * H + h) * d;
         const float *dov = c->dout + (t * H + h) * d;
         double M = -INFINITY;
@@ -775,15 +801,15 @@ static void bwd_job(void *vctx, int job)
 }
 
 int moba_oracle_attend_bwd(const float *q, const float *k, const float *v,
-                           const int *idx, const float *dout, int H, int d, int B,
-                           int K, const int *cu, int nseq, double scale,
+                           const int *idx, const unsigned char *keep, const float *dout,
+                           int H, int d, int B, int K, const int *cu, int nseq, double scale,
                            const unsigned char *qsel, const unsigned char *kbsel,
                            double *dq, double *dk, double *dv, int nthreads)
 {
     if (B < 1 || K < 1) return 1;
     if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
     int *boff = block_offsets(cu, nseq, B);
-    bwd_ctx c = {q, k, v, dout, idx, qsel, kbsel, dq, dk, dv, cu, boff, H, d, B, K, scale};
+    bwd_ctx c = {q, k, v, dout, idx, keep, qsel, kbsel, dq, dk, dv, cu, boff, H, d, B, K, scale};
     run_jobs(bwd_job, &c, nseq * H, nthreads);
     free(boff);
     return 0;

@@ -26,7 +26,8 @@ int moba_oracle_attend_blasst(const float *q, const float *k, const float *v, co
                               int H, int d, int B, int K, const int *cu, int nseq, double scale,
                               double log_lambda, const unsigned char *keep,
                               const unsigned long long *flip, double tau, double *o,
-                              double *lse, unsigned long long *near, int nthreads);
+                              double *lse, unsigned long long *near, unsigned char *keep_out,
+                              int nthreads);
 int moba_oracle_route_rows(const float *q, const float *cent, int H, int d, int B, int K,
                            const int *cu, int nseq, const long long *rows, int nrows, int *idx,
                            double *gap_a, double *gap_b, unsigned char *exempt);
@@ -37,7 +38,7 @@ int moba_oracle_attend_rows(const float *q, const float *k, const float *v, cons
                             int H, int d, int B, int K, const int *cu, int nseq, double scale,
                             const long long *rows, int nrows, double *o, double *lse);
 int moba_oracle_attend_bwd(const float *q, const float *k, const float *v, const int *idx,
-                           const float *dout, int H, int d, int B, int K, const int *cu,
+                           const unsigned char *keep, const float *dout, int H, int d, int B, int K, const int *cu,
                            int nseq, double scale, const unsigned char *qsel,
                            const unsigned char *kbsel, double *dq, double *dk, double *dv,
                            int nthreads);
@@ -106,10 +107,11 @@ static void run_case(const int *cu, int nseq, int H, int d, int B, int K, int W,
     unsigned long long *near = (unsigned long long *)malloc(sizeof(unsigned long long) * (rows + 1));
     for (size_t i = 0; i < rows * K; ++i) keep[i] = (unsigned char)(i % 3 != 1);
     for (size_t i = 0; i < rows; ++i) flip[i] = (i % 5 == 0) ? ~0ull : 0ull;
+    unsigned char *kept = (unsigned char *)malloc(rows * K + 1);
     CHECK(moba_oracle_attend_blasst(q, kc, v, idx, H, d, B, K, cu, nseq, 0.0, log(0.01), NULL,
-                                    NULL, 1e-4, o, lse, near, nthreads));
+                                    NULL, 1e-4, o, lse, near, kept, nthreads));
     CHECK(moba_oracle_attend_blasst(q, kc, v, idx, H, d, B, K, cu, nseq, 0.0, log(0.5), keep,
-                                    flip, 1e-2, o, lse, near, nthreads));
+                                    flip, 1e-2, o, lse, near, NULL, nthreads));
 
     /* row-sampled variants: every third (token, head) row */
     long long *rs = (long long *)malloc(sizeof(long long) * (rows + 1));
@@ -132,19 +134,29 @@ static void run_case(const int *cu, int nseq, int H, int d, int B, int K, int W,
     double *dq = (double *)malloc(sizeof(double) * (rows * d + 1));
     double *dk2 = (double *)malloc(sizeof(double) * (rows * d + 1));
     double *dv = (double *)malloc(sizeof(double) * (rows * d + 1));
-    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, g, H, d, B, K, cu, nseq, 0.0, NULL, NULL, dq,
-                                 dk2, dv, nthreads));
+    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, NULL, g, H, d, B, K, cu, nseq, 0.0, NULL, NULL,
+                                 dq, dk2, dv, nthreads));
     finite_or_fail(dq, rows * d, "dq");
     unsigned char *qsel = (unsigned char *)malloc(rows + 1);
     unsigned char *kbsel = (unsigned char *)malloc((size_t)nb * H + 1);
     for (size_t i = 0; i < rows; ++i) qsel[i] = (unsigned char)(i % 2);
     for (size_t i = 0; i < (size_t)nb * H; ++i) kbsel[i] = (unsigned char)(i % 3 == 0);
-    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, g, H, d, B, K, cu, nseq, 0.5, qsel, kbsel, dq,
-                                 dk2, dv, nthreads));
+    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, NULL, g, H, d, B, K, cu, nseq, 0.5, qsel, kbsel,
+                                 dq, dk2, dv, nthreads));
+    /* the BLASST backward on the decisions of the lambda = 0.01 forward, and
+       on a mask that drops every block of some rows */
+    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, kept, g, H, d, B, K, cu, nseq, 0.0, NULL, NULL,
+                                 dq, dk2, dv, nthreads));
+    finite_or_fail(dq, rows * d, "dq (blasst)");
+    for (size_t i = 0; i < rows * K; ++i) keep[i] = (unsigned char)(i % 7 != 0 && i % 5 != 2);
+    for (size_t i = 0; i < rows * K && i < 4 * (size_t)K; ++i) keep[i] = 0;
+    CHECK(moba_oracle_attend_bwd(q, kc, v, idx, keep, g, H, d, B, K, cu, nseq, 0.0, NULL, NULL,
+                                 dq, dk2, dv, nthreads));
+    finite_or_fail(dq, rows * d, "dq (dropped rows)");
 
     free(q); free(k); free(v); free(g); free(w); free(kc); free(dk); free(dw); free(cent);
     free(idx); free(ga); free(gb); free(ex); free(o); free(lse); free(keep); free(flip);
-    free(near); free(rs); free(idx2); free(sc); free(dq); free(dk2); free(dv); free(qsel);
+    free(near); free(kept); free(rs); free(idx2); free(sc); free(dq); free(dk2); free(dv); free(qsel);
     free(kbsel);
 }
 

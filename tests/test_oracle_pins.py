@@ -754,3 +754,121 @@ def test_blasst_first_block_kept_and_v_ones():
     o0, l0 = oracle.attend(q, k, v, idx, B, K, cu)
     assert not np.allclose(o1, o0)             # something was skipped
     assert np.all(l1 <= l0 + 1e-12)            # dropping keys only lowers the LSE
+
+
+# ------------------------------------------------------- BLASST backward ----
+# The BLASST page's sparsity-aware training needs the gradient of the
+# skipped softmax: for fixed decisions it is the gradient of attention over
+# the kept blocks' keys (the decisions are piecewise constant, as the router
+# is).  Pinned against autograd of the library's masked SDPA, central
+# differences of the keep-mask forward (pinned above against SDPA), the
+# all-kept case and the decisions of the crafted case.
+def _blasst_mask(idx, keep, s0, s1, h, B, K):
+    L = s1 - s0
+    m = np.zeros((L, L), bool)
+    for tl in range(L):
+        i = tl // B
+        row, kp = idx[s0 + tl, h], keep[s0 + tl, h]
+        own_kept = True
+        for p in range(K):
+            j = row[p]
+            if j == i:
+                own_kept = bool(kp[p])
+            elif 0 <= j < i and kp[p]:
+                m[tl, j * B:min((j + 1) * B, L)] = True
+        if own_kept:
+            m[tl, i * B:tl + 1] = True
+    return m
+
+
+def test_blasst_bwd_all_kept_is_plain_backward():
+    q, k, v, idx, cu, B, K = _blasst_case(64)
+    do = _bf16(_rand(q.shape, 65))
+    plain = oracle.attend_bwd(q, k, v, idx, do, B, K, cu)
+    kept = oracle.attend_bwd(q, k, v, idx, do, B, K, cu, keep=np.ones(idx.shape, bool))
+    assert all(np.array_equal(a, b) for a, b in zip(plain, kept))
+
+
+@pytest.mark.parametrize("seed", [66, 67])
+def test_blasst_bwd_matches_autograd_of_masked_sdpa(seed):
+    """Random keep choices (own blocks dropped in some rows); rows whose
+    every block is dropped have no keys and a zero dq."""
+    q, k, v, idx, cu, B, K = _blasst_case(seed)
+    T, H, d = q.shape
+    do = _bf16(_rand(q.shape, seed + 10))
+    keep = np.random.default_rng(seed).random(idx.shape) < 0.6
+    own_dropped = 0
+    scale = 0.37
+    dq, dk, dv = oracle.attend_bwd(q, k, v, idx, do, B, K, cu, scale=scale, keep=keep)
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        for h in range(H):
+            m = _blasst_mask(idx, keep, s0, s1, h, B, K)
+            own_dropped += int(sum(not m[t, t] for t in range(s1 - s0)))
+            rows = m.any(1)
+            tq, tk, tv = (torch.from_numpy(x[s0:s1, h]).double().requires_grad_() for x in (q, k, v))
+            mm = torch.from_numpy(m)
+            o = F.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=mm[None],
+                                               scale=scale)[0]
+            # keyless rows come out NaN from SDPA; they carry no gradient
+            o = torch.where(torch.from_numpy(rows)[:, None], o, torch.zeros_like(o))
+            o.backward(torch.from_numpy(do[s0:s1, h]).double())
+            for ours, ref in ((dq, tq), (dk, tk), (dv, tv)):
+                g = ref.grad.numpy()
+                assert np.allclose(ours[s0:s1, h], np.nan_to_num(g, nan=0.0), rtol=1e-10, atol=1e-12)
+            assert np.all(dq[s0:s1, h][~rows] == 0.0)
+    assert own_dropped > 0
+
+
+def test_blasst_bwd_matches_central_differences():
+    B, K = 4, 3
+    q, k, v, do, cu = _bwd_case(80, T=24, H=1, d=4, cu=(0, 24))
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    keep = np.random.default_rng(8).random(idx.shape) < 0.7
+    keep[:, :, 0] = True                       # no row without keys
+    grads = dict(zip("qkv", oracle.attend_bwd(q, k, v, idx, do, B, K, cu, keep=keep)))
+    base = {"q": q, "k": k, "v": v}
+
+    def loss(x):
+        o, _, _ = oracle.attend_blasst(x["q"], x["k"], x["v"], idx, B, K, cu, 0.0, keep=keep)
+        return float(np.sum(o * do.astype(np.float64)))
+
+    g = np.random.default_rng(6)
+    for name in "qkv":
+        for _ in range(12):
+            t, c = int(g.integers(0, 24)), int(g.integers(0, 4))
+            xp = {n: a.copy() for n, a in base.items()}
+            xm = {n: a.copy() for n, a in base.items()}
+            xp[name][t, 0, c] += np.float32(1e-3)
+            xm[name][t, 0, c] -= np.float32(1e-3)
+            step = float(xp[name][t, 0, c]) - float(xm[name][t, 0, c])
+            fd = (loss(xp) - loss(xm)) / step
+            assert abs(fd - grads[name][t, 0, c]) <= 1e-5 * max(1.0, abs(fd)), (name, t, c)
+
+
+def test_blasst_decisions_output():
+    """The decisions attend_blasst reports, on the crafted case of
+    test_blasst_crafted_skips (block 3 skipped for t = 8 and 9), and on a
+    random case where feeding them back as keep reproduces O and LSE."""
+    B, K = 2, 5
+    firsts = [[1.0, 0.0], [3.0, -1.0], [2.5, 2.0], [0.5, 0.0], [2.2, 9.0]]
+    T = 10
+    q = np.zeros((T, 1, 2), np.float32)
+    q[:, 0, 0] = 1.0
+    k = np.zeros((T, 1, 2), np.float32)
+    for j, (a, b) in enumerate(firsts):
+        k[2 * j, 0, 0], k[2 * j + 1, 0, 0] = a, b
+    v = _rand((T, 1, 2), 62)
+    idx = np.full((T, 1, K), -1, np.int32)
+    idx[8] = [[0, 1, 2, 3, 4]]
+    idx[:8] = [[0, -1, -1, -1, -1]]
+    idx[9] = idx[8]
+    *_, kp = oracle.attend_blasst(q, k, v, idx, B, K, [0, T], math.exp(-1.0), scale=1.0,
+                                  return_keep=True)
+    assert kp[8, 0].tolist() == [True, True, True, False, True] == kp[9, 0].tolist()
+    assert kp[0, 0].tolist() == [True, False, False, False, False]
+    # random: the decisions fed back reproduce the rule's result exactly
+    q, k, v, idx, cu, B, K = _blasst_case(68)
+    o, lse, _, kp = oracle.attend_blasst(q, k, v, idx, B, K, cu, 0.2, return_keep=True)
+    assert not kp[idx >= 0].all() and not kp[idx < 0].any()
+    o2, l2, _ = oracle.attend_blasst(q, k, v, idx, B, K, cu, 0.0, keep=kp)
+    assert np.array_equal(o, o2) and np.array_equal(lse, l2)
