@@ -317,11 +317,28 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _attended_keys(kept, cu, B):
+    """(query, key) pairs a kept selection attends: B keys per listed past
+    block (a past block is always whole) plus the causal own-block keys of
+    the rows that list their own block.  Runs on the device, untimed."""
+    T, H, K = kept.shape
+    tl = torch.empty(T, dtype=torch.int64, device=kept.device)
+    for a, b in zip(cu[:-1], cu[1:]):
+        tl[a:b] = torch.arange(b - a, device=kept.device)
+    own = (tl // B)[:, None, None]
+    past = ((kept >= 0) & (kept < own)).sum()
+    own_rows = (kept == own).any(-1)
+    causal = (tl % B + 1)[:, None].expand(T, H)
+    return int(past) * B + int(causal[own_rows].sum())
+
+
 def bench_bwd(args, moba):
     """One step = one moba_attn_bwd call (index inversion, D = dO.O, the
     per-key-block list kernel and the dq merge) on the forward's selection,
     o and lse, which are computed once before the timed region; with a key
-    convolution, also moba_key_conv_bwd (dk' -> dk, dw)."""
+    convolution, also moba_key_conv_bwd (dk' -> dk, dw).  With
+    --blasst-lambda the forward is the BLASST one and the step is
+    moba_attn_bwd_blasst on its kept selection; FLOPs count the kept pairs."""
     spec = workloads.spec(args.config)
     x = workloads.make(spec)
     dev = torch.device("cuda:0")
@@ -331,7 +348,10 @@ def bench_bwd(args, moba):
     do = workloads.grad_output(spec).to(dev)
     cu = x["cu_seqlens"]
     B, K = spec.block_size, spec.top_k
-    o, lse, idx, kk = moba.moba_fwd(q, k, v, B, K, conv_w=w, conv_mode=spec.conv_mode, cu_seqlens=cu)
+    blasst = args.blasst_lambda is not None
+    o, lse, idx, kk = moba.moba_fwd(q, k, v, B, K, conv_w=w, conv_mode=spec.conv_mode, cu_seqlens=cu,
+                                    blasst_lambda=args.blasst_lambda)
+    bwd = moba.moba_attn_bwd_blasst if blasst else moba.moba_attn_bwd
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(max(256, moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
                      dtype=torch.uint8, device=dev)
@@ -344,8 +364,7 @@ def bench_bwd(args, moba):
                           dtype=torch.uint8, device=dev)
 
     def step():
-        moba.moba_attn_bwd(q, kk, v, idx, o, lse, do, B, K, cu_seqlens=cu, workspace=ws,
-                           out=(dq, dk, dv))
+        bwd(q, kk, v, idx, o, lse, do, B, K, cu_seqlens=cu, workspace=ws, out=(dq, dk, dv))
         if w is not None:
             # dL/dk' -> dL/dk and dL/dw through the key convolution
             moba.moba_key_conv_bwd(k, w, dk, B, spec.conv_mode, cu_seqlens=cu, workspace=wsc)
@@ -367,9 +386,13 @@ def bench_bwd(args, moba):
     ms_step = wall * 1e3 / args.steps
     ms_ev = [a.elapsed_time(b) for a, b in evs]
     fl = workloads.eff_flops_bwd(spec)
+    if blasst:
+        cu_tok = workloads.segments(spec)
+        fl = {"total": 10 * spec.head_dim * _attended_keys(idx.reshape(-1, spec.heads, K), cu_tok, B)}
     value = fl["total"] / (ms_step * 1e-3) / 1e12
     out = {
-        "metric": "MoBA attention bwd effective TFLOP/s (10 d FLOPs per attended key)",
+        "metric": "MoBA attention bwd effective TFLOP/s (10 d FLOPs per attended key)"
+                  + (f", BLASST lambda={args.blasst_lambda} (kept pairs only)" if blasst else ""),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -381,7 +404,8 @@ def bench_bwd(args, moba):
         "vs_baseline": None,
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic (seeded i.i.d. N(0,1) q/k/v/dO, CPU torch.Generator)",
-        "config": {"workload": f"moba_attn_bwd {spec.name}: {spec.desc}",
+        "config": {"workload": f"{'moba_attn_bwd_blasst' if blasst else 'moba_attn_bwd'} "
+                               f"{spec.name}: {spec.desc}",
                    "batch": spec.batch, "seq_len": spec.seq, "heads": spec.heads,
                    "head_dim": spec.head_dim, "block_size": B, "top_k": K,
                    "F_eff_bwd": fl["total"]},

@@ -35,12 +35,12 @@ __all__ = [
     "moba_attn_index", "moba_attn_routed", "moba_attn_combine", "moba_fwd", "fwd",
     "moba_attn_fwd_workspace_bytes", "moba_route_topk_workspace_bytes", "moba_total_blocks",
     "library_path",
-    "moba_attn_bwd", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
+    "moba_attn_bwd", "moba_attn_bwd_blasst", "moba_attn_bwd_workspace_bytes", "moba_key_conv_bwd",
     "moba_key_conv_bwd_workspace_bytes", "moba_attention",
     "MobaError",
 ]
 
-_ABI_VERSION = 2                 # MOBA_ABI_VERSION of include/moba.h
+_ABI_VERSION = 3                 # MOBA_ABI_VERSION of include/moba.h
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmoba_amd.so")
 _lib = None
@@ -84,11 +84,12 @@ def _load():
         "moba_route_topk": [SH, P, P, P, P, SZ, P],
         "moba_route_topk_noalloc": [SH, P, P, P, P],
         "moba_attn_fwd": [SH, P, P, P, P, F32, P, P, P, SZ, P],
-        "moba_attn_fwd_blasst": [SH, P, P, P, P, F32, F32, P, P, P, SZ, P],
+        "moba_attn_fwd_blasst": [SH, P, P, P, P, F32, F32, P, P, P, P, SZ, P],
         "moba_attn_index": [SH, P, P, SZ, P],
         "moba_attn_routed": [SH, P, P, P, F32, P, SZ, P],
         "moba_attn_combine": [SH, P, P, P, P, F32, P, P, P, SZ, P],
         "moba_attn_bwd": [SH, P, P, P, P, F32, P, P, P, P, P, P, P, SZ, P],
+        "moba_attn_bwd_blasst": [SH, P, P, P, P, F32, P, P, P, P, P, P, P, SZ, P],
         "moba_key_conv_bwd": [SH, P, P, I32, I32, P, P, P, P, SZ, P],
     }
     for name, args in sig.items():
@@ -424,13 +425,17 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                   block_size: int, top_k: int, scale: Optional[float] = None,
                   cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
                   return_lse: bool = True, out: Optional[torch.Tensor] = None,
-                  blasst_lambda: Optional[float] = None, stream=None):
+                  blasst_lambda: Optional[float] = None, return_kept: bool = False,
+                  kept_out: Optional[torch.Tensor] = None, stream=None):
     """Attention over the listed blocks + the causal own block.
 
     blasst_lambda (0..1): skip, per query, the selected blocks whose
     maximum score is below the running maximum + ln(lambda) (BLASST, blocks
     in ascending order, the own block last; moba_attn_fwd_blasst).
-    Returns (o, lse) with lse fp32 [..., heads] (None if not requested).
+    Returns (o, lse) with lse fp32 [..., heads] (None if not requested);
+    with blasst_lambda and return_kept, (o, lse, kept_idx): the attended
+    selection (int32 like idx, written into kept_out when given), which
+    moba_attn_bwd_blasst takes.
     """
     _qkv(q, k, v)
     _idx(idx, q, top_k)
@@ -440,13 +445,19 @@ def moba_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     _like(out, q, "out")
     lse = torch.empty(_rows(q), dtype=torch.float32, device=q.device) if return_lse else None
     workspace = _workspace(q, block_size, top_k, cu_seqlens, workspace)
+    if return_kept and blasst_lambda is None:
+        raise MobaError("return_kept needs blasst_lambda")
     if blasst_lambda is not None:
+        kept = None
+        if return_kept:
+            kept = torch.empty_like(idx) if kept_out is None else kept_out
+            _like(kept, idx, "kept_out")
         rc = _load().moba_attn_fwd_blasst(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
                                           float(scale or 0.0), float(blasst_lambda), _p(out),
-                                          _p(lse), _p(workspace), workspace.numel(),
+                                          _p(lse), _p(kept), _p(workspace), workspace.numel(),
                                           _stream(stream))
         _check(rc, "moba_attn_fwd_blasst")
-        return out, lse
+        return (out, lse, kept) if return_kept else (out, lse)
     rc = _load().moba_attn_fwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
                                float(scale or 0.0), _p(out), _p(lse), _p(workspace),
                                workspace.numel(), _stream(stream))
@@ -469,8 +480,9 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
     """The whole MoBA forward: [key conv] -> centroids -> route -> attention
     (with the BLASST block skip when blasst_lambda is given).
 
-    Returns (o, lse, idx, k_used) where k_used is k' when a conv ran.  With
-    ``stream`` every step runs (and every buffer is allocated) on it.
+    Returns (o, lse, idx, k_used) where k_used is k' when a conv ran; with
+    blasst_lambda, idx is the attended (kept) selection.  With ``stream``
+    every step runs (and every buffer is allocated) on it.
     """
     if conv_w is not None:
         kk, cent = moba_key_conv(k, conv_w, block_size, conv_mode, cu_seqlens,
@@ -483,8 +495,11 @@ def moba_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
                    moba_route_topk_workspace_bytes(q, block_size, top_k, cu_seqlens), 256)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     idx = moba_route_topk(q, cent, block_size, top_k, cu_seqlens, workspace=workspace)
-    o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace,
-                           blasst_lambda=blasst_lambda)
+    if blasst_lambda is not None:
+        o, lse, kept = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace,
+                                     blasst_lambda=blasst_lambda, return_kept=True)
+        return o, lse, kept, kk
+    o, lse = moba_attn_fwd(q, kk, v, idx, block_size, top_k, scale, cu_seqlens, workspace)
     return o, lse, idx, kk
 
 
@@ -503,7 +518,7 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
                   block_size: int, top_k: int, scale: Optional[float] = None,
                   cu_seqlens=None, workspace: Optional[torch.Tensor] = None,
                   out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
-                  stream=None):
+                  stream=None, _entry: str = "moba_attn_bwd"):
     """Gradients (dq, dk, dv) of moba_attn_fwd's output for the selection idx.
 
     o and lse are that forward's outputs; dout is dL/dO.  bf16 (fast path) or
@@ -528,12 +543,23 @@ def moba_attn_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _ws(workspace, need)
-    rc = _load().moba_attn_bwd(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
-                               float(scale or 0.0), _p(o), _p(lse), _p(dout), _p(dq),
-                               _p(dk), _p(dv), _p(workspace), workspace.numel(),
-                               _stream(stream))
-    _check(rc, "moba_attn_bwd")
+    rc = getattr(_load(), _entry)(ctypes.byref(sh), _p(q), _p(k), _p(v), _p(idx),
+                                  float(scale or 0.0), _p(o), _p(lse), _p(dout), _p(dq),
+                                  _p(dk), _p(dv), _p(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check(rc, _entry)
     return dq, dk, dv
+
+
+def moba_attn_bwd_blasst(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                         kept_idx: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+                         dout: torch.Tensor, block_size: int, top_k: int, **kw):
+    """Gradients of moba_attn_fwd_blasst's output for the decisions it took:
+    kept_idx is that call's attended selection (return_kept=True); a row's
+    own block takes part only where kept_idx lists it.  Other arguments as
+    moba_attn_bwd."""
+    return moba_attn_bwd(q, k, v, kept_idx, o, lse, dout, block_size, top_k,
+                         _entry="moba_attn_bwd_blasst", **kw)
 
 
 class _MobaAttention(torch.autograd.Function):
@@ -543,33 +569,39 @@ class _MobaAttention(torch.autograd.Function):
     router."""
 
     @staticmethod
-    def forward(ctx, q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale):
+    def forward(ctx, q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale,
+                blasst_lambda):
         o, lse, idx, kk = moba_fwd(q, k, v, block_size, top_k, conv_w, conv_mode,
-                                   cu_seqlens, scale)
+                                   cu_seqlens, scale, blasst_lambda=blasst_lambda)
         ctx.save_for_backward(q, k, v, conv_w, o, lse, idx, kk)
-        ctx.cfg = (block_size, top_k, conv_mode, cu_seqlens, scale)
+        ctx.cfg = (block_size, top_k, conv_mode, cu_seqlens, scale, blasst_lambda)
         ctx.mark_non_differentiable(lse)
         return o, lse
 
     @staticmethod
     def backward(ctx, do, _dlse):
         q, k, v, conv_w, o, lse, idx, kk = ctx.saved_tensors
-        block_size, top_k, conv_mode, cu_seqlens, scale = ctx.cfg
-        dq, dkk, dv = moba_attn_bwd(q, kk, v, idx, o, lse, do.contiguous(), block_size, top_k,
-                                    scale, cu_seqlens)
+        block_size, top_k, conv_mode, cu_seqlens, scale, blasst_lambda = ctx.cfg
+        bwd = moba_attn_bwd if blasst_lambda is None else moba_attn_bwd_blasst
+        dq, dkk, dv = bwd(q, kk, v, idx, o, lse, do.contiguous(), block_size, top_k,
+                          scale=scale, cu_seqlens=cu_seqlens)
         dk, dw = dkk, None
         if conv_w is not None:
             dk, dw = moba_key_conv_bwd(k, conv_w, dkk, block_size, conv_mode, cu_seqlens)
-        return dq, dk, dv, dw, None, None, None, None, None
+        return dq, dk, dv, dw, None, None, None, None, None, None
 
 
 def moba_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_size: int,
                    top_k: int, conv_w: Optional[torch.Tensor] = None,
                    conv_mode: str = "plain", cu_seqlens=None,
-                   scale: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                   scale: Optional[float] = None,
+                   blasst_lambda: Optional[float] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """MoBA attention as a differentiable op: returns (o, lse).
 
-    Gradients flow to q, k, v and the conv filter (bf16 backward; the
-    selection itself carries none).
+    Gradients flow to q, k, v and the conv filter (the selection itself
+    carries none).  With blasst_lambda the forward applies the BLASST block
+    skip and the backward differentiates the kept blocks' softmax (BLASST's
+    sparsity-aware training); the skip decisions carry no gradient either.
     """
-    return _MobaAttention.apply(q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale)
+    return _MobaAttention.apply(q, k, v, conv_w, block_size, top_k, conv_mode, cu_seqlens, scale,
+                                blasst_lambda)

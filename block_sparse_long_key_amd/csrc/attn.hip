@@ -597,7 +597,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
     SegTable st, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
     const float* __restrict__ pm, float log2lam, float sl2, T* __restrict__ o,
-    float* __restrict__ lse)
+    float* __restrict__ lse, const int32_t* __restrict__ idx, int32_t* __restrict__ kept)
 {
     // bf16 d = 128: V^T is loaded over K once the scores are done, so the
     // stage takes half the LDS and 3 workgroups fit a CU (2 otherwise)
@@ -717,6 +717,19 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
             }
             own_kept = !(Mr > -INFINITY && own_max[r] - Mr < log2lam);
         }
+        // the attended selection: idx's routed blocks that were kept, then
+        // the own block if kept, ascending, -1 padded
+        if (kept && c == 0) {
+            const int32_t* irow = idx + qrow * K;
+            int32_t* krow = kept + qrow * K;
+            int n = 0;
+            for (int p = 0; p < kmerge; ++p) {
+                const int j = irow[p];
+                if (j >= 0 && j < i && rrow[p] >= 0 && ((keepm >> p) & 1u)) krow[n++] = j;
+            }
+            if (own_kept && n < K) krow[n++] = i;
+            for (; n < K; ++n) krow[n] = -1;
+        }
         float M = own_lse[r];
         float wsum = 1.0f;
         if (!own_kept) {
@@ -799,16 +812,18 @@ hipError_t routed_t(const Launch& L, const WsLayout& ws, char* wsp, const void* 
 template <typename T, int D, int BLK>
 hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, const void* k,
                   const void* v, const int32_t* idx, float sl2, void* o, float* lse,
-                  float blasst_lambda)
+                  float blasst_lambda, int32_t* kept)
 {
     if (L.st.total_blocks == 0) return hipSuccess;
-    (void)idx;   // the index pass turned idx into the reverse map
+    // the index pass turned idx into the reverse map; idx itself is read
+    // only to write the kept selection
     hipLaunchKernelGGL((diag_combine_kernel<T, D, BLK>), dim3(L.st.total_blocks, L.st.H),
                        dim3(2 * BLK), 0, L.stream, L.st, (const T*)q, (const T*)k, (const T*)v,
                        (const int32_t*)(wsp + ws.rev_off), (const T*)(wsp + ws.po_off),
                        (const float*)(wsp + ws.pl_off),
                        blasst_lambda > 0.f ? (const float*)(wsp + ws.pm_off) : nullptr,
-                       blasst_lambda > 0.f ? log2f(blasst_lambda) : 0.f, sl2, (T*)o, lse);
+                       blasst_lambda > 0.f ? log2f(blasst_lambda) : 0.f, sl2, (T*)o, lse,
+                       idx, kept);
     return hipGetLastError();
 }
 
@@ -840,10 +855,10 @@ hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp, co
 
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                                const void* k, const void* v, const int32_t* idx, float scale,
-                               void* o, float* lse, float blasst_lambda)
+                               void* o, float* lse, float blasst_lambda, int32_t* kept)
 {
     const float sl2 = scale * 1.4426950408889634f;
-    MOBA_DISPATCH(diag_t, L, ws, wsp, q, k, v, idx, sl2, o, lse, blasst_lambda);
+    MOBA_DISPATCH(diag_t, L, ws, wsp, q, k, v, idx, sl2, o, lse, blasst_lambda, kept);
 }
 
 }  // namespace moba

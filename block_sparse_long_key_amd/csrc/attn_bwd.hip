@@ -124,7 +124,7 @@ __global__ __launch_bounds__((64 * bwd_waves<D, BLK>()), 2) void bwd_list_kernel
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float2* __restrict__ rowstat, float sl2, float scale,
     float* __restrict__ pq, int64_t diag_base, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv,
-    int64_t nlists, int64_t per_xcd, int routed)
+    int64_t nlists, int64_t per_xcd, int routed, const uint8_t* __restrict__ own)
 {
     using S = BwdSmem<D, BLK>;
     __shared__ __align__(16) S sm;
@@ -217,7 +217,11 @@ __global__ __launch_bounds__((64 * bwd_waves<D, BLK>()), 2) void bwd_list_kernel
             u32x4_t z = {0u, 0u, 0u, 0u};
             pre_q[p] = ok ? *(const u32x4_t*)(q + row * D + 8 * sc) : z;
             pre_do[p] = ok ? *(const u32x4_t*)(dout + row * D + 8 * sc) : z;
-            pre_stat[p] = (ok && sc == 0) ? rowstat[row] : make_float2(__builtin_inff(), 0.f);
+            // a row that leaves its own block out (own[row] == 0) takes
+            // part in the own-block tile with P = 0: no dK / dV share and a
+            // zero dq piece
+            const bool live = ok && !(own && tile < ndiag && !own[row]);
+            pre_stat[p] = (live && sc == 0) ? rowstat[row] : make_float2(__builtin_inff(), 0.f);
             pre_dest[p] = ok ? dest : -1;
         }
     };
@@ -447,10 +451,26 @@ __global__ __launch_bounds__(kBwdThreads) void dq_combine_kernel(SegTable st, in
         u32x2_t{pack_bf16x2(acc.x * scale, acc.y * scale), pack_bf16x2(acc.z * scale, acc.w * scale)};
 }
 
+// own[row] = 1 iff idx's row lists the row's own block (t - cu[s]) / B
+__global__ __launch_bounds__(kBwdThreads) void own_flags_kernel(SegTable st, int64_t rows,
+                                                                const int32_t* __restrict__ idx,
+                                                                uint8_t* __restrict__ own)
+{
+    const int64_t row = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+    if (row >= rows) return;
+    const int t = (int)(row / st.H);
+    const int s = seq_of_token(st, t);
+    const int i = (t - st.cu[s]) / st.B;
+    const int32_t* r = idx + row * st.K;
+    bool f = false;
+    for (int p = 0; p < st.K; ++p) f |= r[p] == i;
+    own[row] = f ? 1 : 0;
+}
+
 template <int D, int BLK>
 hipError_t bwd_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, const void* k,
                  const void* v, const void* o, const float* lse, const void* dout, float scale,
-                 void* dq, void* dk, void* dv)
+                 void* dq, void* dk, void* dv, const uint8_t* own)
 {
     const SegTable& st = L.st;
     const int64_t rows = (int64_t)L.tokens * st.H;
@@ -473,7 +493,7 @@ hipError_t bwd_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, 
                            (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v,
                            (const uint16_t*)dout, (const float2*)rowstat, scale * 1.4426950408889634f,
                            scale, pq, diag_base, (uint16_t*)dk, (uint16_t*)dv, nlists, per_xcd,
-                           st.K > 1 ? 1 : 0);
+                           st.K > 1 ? 1 : 0, own);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -490,15 +510,26 @@ hipError_t bwd_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, 
 
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                            const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float scale, void* dq, void* dk, void* dv)
+                           const void* dout, float scale, void* dq, void* dk, void* dv,
+                           const uint8_t* own)
 {
     if (L.dtype != MOBA_BF16) return hipErrorInvalidValue;
     const int B = L.st.B;
-    if (L.D == 64 && B == 64) return bwd_t<64, 64>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv);
-    if (L.D == 64 && B == 128) return bwd_t<64, 128>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv);
-    if (L.D == 128 && B == 64) return bwd_t<128, 64>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv);
-    if (L.D == 128 && B == 128) return bwd_t<128, 128>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv);
+    if (L.D == 64 && B == 64) return bwd_t<64, 64>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv, own);
+    if (L.D == 64 && B == 128) return bwd_t<64, 128>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv, own);
+    if (L.D == 128 && B == 64) return bwd_t<128, 64>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv, own);
+    if (L.D == 128 && B == 128)
+        return bwd_t<128, 128>(L, ws, wsp, q, k, v, o, lse, dout, scale, dq, dk, dv, own);
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_own_flags(const Launch& L, const int32_t* idx, uint8_t* own)
+{
+    const int64_t rows = (int64_t)L.tokens * L.st.H;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(own_flags_kernel, dim3((unsigned)((rows + kBwdThreads - 1) / kBwdThreads)),
+                       dim3(kBwdThreads), 0, L.stream, L.st, rows, idx, own);
+    return hipGetLastError();
 }
 
 }  // namespace moba

@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(SegTable st, const int32
                                                        const float* __restrict__ v,
                                                        const float* __restrict__ dout,
                                                        const float2* __restrict__ rowstat, float sl2,
-                                                       float scale, float* __restrict__ dq)
+                                                       float scale, float* __restrict__ dq,
+                                                       const uint8_t* __restrict__ own)
 {
     constexpr int CPL = D / 64;                  // channels per lane: c = 64 e + lane
     const int t = blockIdx.x, h = blockIdx.y;
@@ -84,8 +85,9 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(SegTable st, const int32
     const float2 rs = rowstat[row];
     const int32_t* sel = idx + row * K;
     // the listed past blocks in idx order (entries >= i or < 0 skipped, as the
-    // forward does), then the own block up to t
-    for (int p = 0; p <= K; ++p) {
+    // forward does), then the own block up to t (unless own[row] == 0)
+    const int pend = (own && !own[row]) ? K - 1 : K;
+    for (int p = 0; p <= pend; ++p) {
         int j = i;
         if (p < K) {
             j = sel[p];
@@ -119,7 +121,8 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(SegTable st, const int2*
                                                        const float* __restrict__ v,
                                                        const float* __restrict__ dout,
                                                        const float2* __restrict__ rowstat, float sl2,
-                                                       float scale, float* __restrict__ dk, float* __restrict__ dv)
+                                                       float scale, float* __restrict__ dk, float* __restrict__ dv,
+                                                       const uint8_t* __restrict__ own)
 {
     constexpr int CPL = D / 64;
     const int u = blockIdx.x, h = blockIdx.y;    // key token u (global), head h
@@ -166,9 +169,10 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(SegTable st, const int2*
         const uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K + le.x;
         for (int e = 0; e < le.y; ++e) add_row((int)(ent[e] >> 5));
     }
-    // the own-block queries t >= u
+    // the own-block queries t >= u (those that attend their own block)
     const int tend = min((j + 1) * B, L);
-    for (int tl = ul; tl < tend; ++tl) add_row(st.cu[s] + tl);
+    for (int tl = ul; tl < tend; ++tl)
+        if (!own || own[(size_t)(st.cu[s] + tl) * H + h]) add_row(st.cu[s] + tl);
 #pragma unroll
     for (int e = 0; e < CPL; ++e) {
         dk[krow * D + 64 * e + lane] = ak[e] * scale;
@@ -180,7 +184,7 @@ template <int D>
 hipError_t bwd_f32_t(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx, const float* q,
                      const float* k,
                      const float* v, const float* o, const float* lse, const float* dout, float scale,
-                     float* dq, float* dk, float* dv)
+                     float* dq, float* dk, float* dv, const uint8_t* own)
 {
     const SegTable& st = L.st;
     const int64_t rows = (int64_t)L.tokens * st.H;
@@ -195,12 +199,12 @@ hipError_t bwd_f32_t(const Launch& L, const WsLayout& ws, char* wsp, const int32
     }
     const dim3 grid((unsigned)L.tokens, (unsigned)st.H);
     hipLaunchKernelGGL((bwd_dq_f32_kernel<D>), grid, dim3(64), 0, L.stream, st, idx, q, k, v, dout,
-                       (const float2*)rowstat, sl2, scale, dq);
+                       (const float2*)rowstat, sl2, scale, dq, own);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_kv_f32_kernel<D>), grid, dim3(64), 0, L.stream, st,
                        (const int2*)(wsp + ws.lst_off), (const uint32_t*)(wsp + ws.ent_off), q, k, v, dout,
-                       (const float2*)rowstat, sl2, scale, dk, dv);
+                       (const float2*)rowstat, sl2, scale, dk, dv, own);
     return hipGetLastError();
 }
 
@@ -209,14 +213,14 @@ hipError_t bwd_f32_t(const Launch& L, const WsLayout& ws, char* wsp, const int32
 hipError_t launch_attn_bwd_f32(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
                                const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, float scale, void* dq, void* dk,
-                               void* dv)
+                               void* dv, const uint8_t* own)
 {
     if (L.D == 64)
         return bwd_f32_t<64>(L, ws, wsp, idx, (const float*)q, (const float*)k, (const float*)v, (const float*)o,
-                             lse, (const float*)dout, scale, (float*)dq, (float*)dk, (float*)dv);
+                             lse, (const float*)dout, scale, (float*)dq, (float*)dk, (float*)dv, own);
     if (L.D == 128)
         return bwd_f32_t<128>(L, ws, wsp, idx, (const float*)q, (const float*)k, (const float*)v, (const float*)o,
-                              lse, (const float*)dout, scale, (float*)dq, (float*)dk, (float*)dv);
+                              lse, (const float*)dout, scale, (float*)dq, (float*)dk, (float*)dv, own);
     return hipErrorInvalidValue;
 }
 

@@ -131,6 +131,7 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
         w.rs_bytes = rows * 8;
         const size_t ent_rows = st.K > 1 ? (size_t)st.ebase[st.nseq] : 0;
         w.pq_bytes = (ent_rows + rows) * L.D * 4;
+        w.own_bytes = rows;
     }
     if (expand) w.px_bytes = rows * st.K * 4;
     size_t off = 0;
@@ -145,6 +146,7 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
     w.rs_off = off;    off += align256(w.rs_bytes);
     w.pq_off = off;    off += align256(w.pq_bytes);
     w.px_off = off;    off += align256(w.px_bytes);
+    w.own_off = off;   off += align256(w.own_bytes);
     w.total = off;
     return w;
 }
@@ -495,7 +497,8 @@ moba_status attn_fwd_one(const moba_shape* shape, const void* q, const void* k, 
 
 moba_status attn_fwd_blasst_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                                 const int32_t* idx, float softmax_scale, float blasst_lambda, void* o,
-                                float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream)
+                                float* lse, int32_t* kept, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream)
 {
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
@@ -504,6 +507,7 @@ moba_status attn_fwd_blasst_one(const moba_shape* shape, const void* q, const vo
     if (expands(Ll)) return MOBA_ERR_UNSUPPORTED;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !idx_ok(idx) || !ptr_ok(o)) return MOBA_ERR_INVALID_ARG;
     if (lse && ((uintptr_t)lse & 3u)) return MOBA_ERR_INVALID_ARG;
+    if (kept && (!idx_ok(kept) || kept == idx)) return MOBA_ERR_INVALID_ARG;
     WsLayout ws;
     st = check_ws(L, workspace, workspace_bytes, &ws, false, false);
     if (st != MOBA_OK) return st;
@@ -512,18 +516,21 @@ moba_status attn_fwd_blasst_one(const moba_shape* shape, const void* q, const vo
     const float scale = resolve_scale(softmax_scale, L.D);
     hipError_t e = run_index(Ll, L, ws, wsp, idx);
     if (e == hipSuccess) e = launch_routed_attn(L, ws, wsp, q, k, v, scale, blasst_lambda > 0.f);
-    if (e == hipSuccess) e = launch_diag_combine(L, ws, wsp, q, k, v, idx, scale, o, lse, blasst_lambda);
+    if (e == hipSuccess) e = launch_diag_combine(L, ws, wsp, q, k, v, idx, scale, o, lse, blasst_lambda, kept);
     return hip_status(e);
 }
 
+// own_listed: the own block is attended only where idx lists it (the
+// kept selection of a BLASST forward); otherwise always, as in the forward
 moba_status attn_bwd_one(const moba_shape* shape, const void* q, const void* k, const void* v,
                           const int32_t* idx, float softmax_scale, const void* o, const float* lse,
                           const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream)
+                          size_t workspace_bytes, hipStream_t stream, bool own_listed = false)
 {
     Launch Ll, L;
     moba_status st = attn_launch(shape, stream, &Ll, &L);
     if (st != MOBA_OK) return st;
+    if (own_listed && expands(Ll)) return MOBA_ERR_UNSUPPORTED;
     if (!ptr_ok(q) || !ptr_ok(k) || !ptr_ok(v) || !idx_ok(idx) || !ptr_ok(o) || !ptr_ok(lse) ||
         !ptr_ok(dout) || !ptr_ok(dq) || !ptr_ok(dk) || !ptr_ok(dv))
         return MOBA_ERR_INVALID_ARG;
@@ -541,13 +548,20 @@ moba_status attn_bwd_one(const moba_shape* shape, const void* q, const void* k, 
     // repeatable list order: dK / dV sum each list's rows in that order
     hipError_t e = run_index(Ll, L, ws, (char*)workspace, idx, true);
     if (e != hipSuccess) return MOBA_ERR_HIP;
+    uint8_t* own = nullptr;
+    if (own_listed) {
+        own = (uint8_t*)workspace + ws.own_off;
+        e = launch_own_flags(L, idx, own);
+        if (e != hipSuccess) return MOBA_ERR_HIP;
+    }
     const float scale = resolve_scale(softmax_scale, L.D);
     if (L.dtype == MOBA_F32) {
         const int32_t* ia = expands(Ll) ? (const int32_t*)((char*)workspace + ws.px_off) : idx;
         return hip_status(launch_attn_bwd_f32(L, ws, (char*)workspace, ia, q, k, v, o, lse, dout, scale,
-                                              dq, dk, dv));
+                                              dq, dk, dv, own));
     }
-    return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout, scale, dq, dk, dv));
+    return hip_status(launch_attn_bwd(L, ws, (char*)workspace, q, k, v, o, lse, dout, scale, dq, dk, dv,
+                                      own));
 }
 
 }  // namespace one
@@ -848,11 +862,13 @@ moba_status moba_attn_fwd(const moba_shape* shape, const void* q, const void* k,
 
 moba_status moba_attn_fwd_blasst(const moba_shape* shape, const void* q, const void* k, const void* v,
                                  const int32_t* idx, float softmax_scale, float blasst_lambda, void* o,
-                                 float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream)
+                                 float* lse, int32_t* kept_idx, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream)
 {
     MOBA_GROUPS(shape);
     if (!ptr_ok(idx)) return MOBA_ERR_INVALID_ARG;
     if (lse && !aligned16(lse)) return MOBA_ERR_INVALID_ARG;
+    if (kept_idx && (!aligned16(kept_idx) || kept_idx == idx)) return MOBA_ERR_INVALID_ARG;
     MOBA_ATTN_GROUPS(false);
     const size_t er = row * esize(shape);
     for (int g = 0; g < G.n; ++g) {
@@ -862,7 +878,7 @@ moba_status moba_attn_fwd_blasst(const moba_shape* shape, const void* q, const v
         moba_status st = one::attn_fwd_blasst_one(&gr.sh, at(q, gr.tok0, er), at(k, gr.tok0, er),
                                                   at(v, gr.tok0, er), at(idx, gr.tok0, irow), softmax_scale,
                                                   blasst_lambda, at(o, gr.tok0, er), at(lse, gr.tok0, lrow),
-                                                  at(workspace, (int64_t)wsoff, 1),
+                                                  at(kept_idx, gr.tok0, irow), at(workspace, (int64_t)wsoff, 1),
                                                   G.n > 1 ? wsz : workspace_bytes, stream);
         if (st != MOBA_OK) return st;
         wsoff += wsz;
@@ -870,10 +886,10 @@ moba_status moba_attn_fwd_blasst(const moba_shape* shape, const void* q, const v
     return MOBA_OK;
 }
 
-moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,
-                          const int32_t* idx, float softmax_scale, const void* o, const float* lse,
-                          const void* dout, void* dq, void* dk, void* dv, void* workspace,
-                          size_t workspace_bytes, hipStream_t stream)
+static moba_status attn_bwd_groups(const moba_shape* shape, const void* q, const void* k, const void* v,
+                                   const int32_t* idx, float softmax_scale, const void* o, const float* lse,
+                                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream, bool own_listed)
 {
     MOBA_GROUPS(shape);
     if (!ptr_ok(idx) || !ptr_ok(lse)) return MOBA_ERR_INVALID_ARG;
@@ -888,11 +904,29 @@ moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k,
                                            at(lse, gr.tok0, lrow), at(dout, gr.tok0, er), at(dq, gr.tok0, er),
                                            at(dk, gr.tok0, er), at(dv, gr.tok0, er),
                                            at(workspace, (int64_t)wsoff, 1),
-                                           G.n > 1 ? wsz : workspace_bytes, stream);
+                                           G.n > 1 ? wsz : workspace_bytes, stream, own_listed);
         if (st != MOBA_OK) return st;
         wsoff += wsz;
     }
     return MOBA_OK;
+}
+
+moba_status moba_attn_bwd(const moba_shape* shape, const void* q, const void* k, const void* v,
+                          const int32_t* idx, float softmax_scale, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream)
+{
+    return attn_bwd_groups(shape, q, k, v, idx, softmax_scale, o, lse, dout, dq, dk, dv, workspace,
+                           workspace_bytes, stream, false);
+}
+
+moba_status moba_attn_bwd_blasst(const moba_shape* shape, const void* q, const void* k, const void* v,
+                                 const int32_t* kept_idx, float softmax_scale, const void* o,
+                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return attn_bwd_groups(shape, q, k, v, kept_idx, softmax_scale, o, lse, dout, dq, dk, dv, workspace,
+                           workspace_bytes, stream, true);
 }
 
 }  // extern "C"

@@ -159,6 +159,7 @@ struct WsLayout {
     size_t rs_off, rs_bytes;         // backward: float2 [tokens][H] (lse in log2 units, dO . O)
     size_t pq_off, pq_bytes;         // backward: fp32 dq pieces, list order, then own-block rows
     size_t px_off, px_bytes;         // block sizes > 128: int32 [tokens][H][K'] selection in 128-key blocks
+    size_t own_off, own_bytes;       // backward: uint8 [tokens][H], 1 where the row attends its own block
     size_t total;
 };
 
@@ -200,19 +201,25 @@ hipError_t launch_expand_idx(const Launch& Ll, int ab, int Kp, const int32_t* id
 hipError_t launch_routed_attn(const Launch& L, const WsLayout& ws, char* wsp,
                               const void* q, const void* k, const void* v, float scale,
                               bool block_max = false);
+// own (nullable, uint8 per (token, head)): rows with own[row] == 0 leave
+// their own block out of the key set (a BLASST selection); null: every row
+// attends its own block
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                            const void* k, const void* v, const void* o, const float* lse,
-                           const void* dout, float scale, void* dq, void* dk, void* dv);
+                           const void* dout, float scale, void* dq, void* dk, void* dv,
+                           const uint8_t* own = nullptr);
 // fp32 inputs; idx: the selection in the launch's blocks (expanded for B > 128)
 hipError_t launch_attn_bwd_f32(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
                                const void* q, const void* k, const void* v, const void* o,
                                const float* lse, const void* dout, float scale, void* dq, void* dk,
-                               void* dv);
+                               void* dv, const uint8_t* own = nullptr);
+// own[row] = 1 where idx's row lists the row's own block, else 0
+hipError_t launch_own_flags(const Launch& L, const int32_t* idx, uint8_t* own);
 // blasst_lambda > 0: the BLASST skip over the partials' block maxima
 // (which the routed pass must have stored, block_max = true)
 hipError_t launch_diag_combine(const Launch& L, const WsLayout& ws, char* wsp,
                                const void* q, const void* k, const void* v,
                                const int32_t* idx, float scale, void* o, float* lse,
-                               float blasst_lambda = 0.f);
+                               float blasst_lambda = 0.f, int32_t* kept = nullptr);
 
 }  // namespace moba

@@ -78,7 +78,7 @@
 extern "C" {
 #endif
 
-#define MOBA_ABI_VERSION 2
+#define MOBA_ABI_VERSION 3
 /* sequences per launch group (a call with more runs several groups) */
 #define MOBA_MAX_SEQS 64
 
@@ -258,6 +258,10 @@ moba_status moba_attn_fwd(const moba_shape *shape, const void *q,
  *   before any query's running maximum is known, so the skip is decided in
  *   the merge of the per-block partials: it saves the merge's reads of the
  *   skipped partials, not their computation.
+ *   kept_idx: NULL, or int32 [batch][seq][heads][top_k], 16-byte aligned,
+ *   not idx: receives the attended selection -- idx's past blocks that were
+ *   kept, then the own block if it was kept, ascending, -1 padded (with
+ *   lambda = 0: idx itself).  It is the selection moba_attn_bwd_blasst takes.
  *   Same workspace (moba_attn_fwd_workspace_bytes), other arguments and
  *   errors as moba_attn_fwd.
  */
@@ -265,8 +269,8 @@ moba_status moba_attn_fwd_blasst(const moba_shape *shape, const void *q,
                                  const void *k, const void *v,
                                  const int32_t *idx, float softmax_scale,
                                  float blasst_lambda, void *o, float *lse,
-                                 void *workspace, size_t workspace_bytes,
-                                 hipStream_t stream);
+                                 int32_t *kept_idx, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* The three stages of moba_attn_fwd, in order, for stage timing: the
  * index inversion, the routed (past-block) attention, and the own-block
@@ -319,7 +323,30 @@ moba_status moba_attn_bwd(const moba_shape *shape, const void *q,
                           void *workspace, size_t workspace_bytes,
                           hipStream_t stream);
 
-/* Bytes of workspace moba_attn_bwd needs for `shape` (0 on invalid shape). */
+/*
+ * moba_attn_bwd_blasst -- gradients of moba_attn_fwd_blasst's O (BLASST
+ * page, "Meccanismo di Pruning", and the page's sparsity-aware training):
+ * for the skip decisions that call took, the gradients of softmax attention
+ * over the kept blocks' keys.  The decisions are piecewise constant in q and
+ * k, so, as for the router, no gradient flows through them.
+ *   kept_idx: the forward's kept_idx output (rows ascending, -1 padded; a
+ *   row lists its own block only if the own block was kept, and attends it
+ *   causally then).  o, lse: that forward's outputs.  Other arguments,
+ *   workspace (moba_attn_bwd_workspace_bytes), repeatability and errors as
+ *   moba_attn_bwd; the shapes moba_attn_fwd_blasst takes (others:
+ *   MOBA_ERR_UNSUPPORTED).  A row that lists no block has no keys: its dq is
+ *   zero and it adds nothing to dk, dv.
+ */
+moba_status moba_attn_bwd_blasst(const moba_shape *shape, const void *q,
+                                 const void *k, const void *v,
+                                 const int32_t *kept_idx, float softmax_scale,
+                                 const void *o, const float *lse,
+                                 const void *dout, void *dq, void *dk,
+                                 void *dv, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace moba_attn_bwd (and moba_attn_bwd_blasst) needs for
+ * `shape` (0 on invalid shape). */
 size_t moba_attn_bwd_workspace_bytes(const moba_shape *shape);
 
 /* Bytes of workspace moba_attn_fwd needs for `shape` (0 on invalid shape). */

@@ -120,14 +120,24 @@ def test_entry_points_write_inside_their_buffers(case):
     _check(a, full=("o", "lse"))
     o, lse = a["o"].t, a["lse"].t
 
-    # one-call forward and the BLASST forward into guarded outputs
+    # one-call forward and the BLASST forward (with its kept selection) into
+    # guarded outputs
+    blasst = None
     for lam in ((None, 0.5) if B <= 128 else (None,)):   # BLASST takes whole blocks only
         f = {"ws": _ws(nws), "o": Guarded((T, H, d), dt)}
-        o2, _ = moba.moba_attn_fwd(q, kk, v, idx, B, K, cu_seqlens=cu, workspace=f["ws"].t,
-                                   return_lse=False, out=f["o"].t, blasst_lambda=lam)
-        _check(f, full=("o",))
         if lam is None:
+            o2, _ = moba.moba_attn_fwd(q, kk, v, idx, B, K, cu_seqlens=cu, workspace=f["ws"].t,
+                                       return_lse=False, out=f["o"].t)
+            _check(f, full=("o",))
             assert torch.equal(o2, o)
+        else:
+            f["kept"] = Guarded((T, H, K), torch.int32)
+            o3, lse3, kept3 = moba.moba_attn_fwd(q, kk, v, idx, B, K, cu_seqlens=cu,
+                                                 workspace=f["ws"].t, out=f["o"].t,
+                                                 blasst_lambda=lam, return_kept=True,
+                                                 kept_out=f["kept"].t)
+            _check(f, full=("o", "kept"))
+            blasst = (o3, lse3, kept3)
 
     # attention backward into guarded dq, dk, dv
     bw = {"ws": _ws(moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
@@ -135,6 +145,16 @@ def test_entry_points_write_inside_their_buffers(case):
     moba.moba_attn_bwd(q, kk, v, idx, o, lse, dout, B, K, cu_seqlens=cu, workspace=bw["ws"].t,
                        out=(bw["dq"].t, bw["dk"].t, bw["dv"].t))
     _check(bw, full=("dq", "dk", "dv"))
+    if blasst is not None:
+        kept = blasst[2]
+        kept_saved = kept.clone()
+        bb = {"ws": _ws(moba.moba_attn_bwd_workspace_bytes(q, B, K, cu)),
+              "dq": Guarded((T, H, d), dt), "dk": Guarded((T, H, d), dt),
+              "dv": Guarded((T, H, d), dt)}
+        moba.moba_attn_bwd_blasst(q, kk, v, kept, blasst[0], blasst[1], dout, B, K, cu_seqlens=cu,
+                                  workspace=bb["ws"].t, out=(bb["dq"].t, bb["dk"].t, bb["dv"].t))
+        _check(bb, full=("dq", "dk", "dv"))
+        assert torch.equal(kept, kept_saved), "kept_idx was modified by the backward"
 
     # key conv backward: its workspace stays inside the asked size
     if W:

@@ -38,7 +38,7 @@ def test_exports_every_declared_function(lib):
     assert "moba_attn_fwd" in names and "moba_route_topk" in names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
-    assert lib.moba_abi_version() == 2
+    assert lib.moba_abi_version() == 3
     assert lib.moba_status_string(0) == b"ok"
     assert lib.moba_status_string(WS_SMALL) == b"workspace too small"
 
@@ -117,7 +117,22 @@ def test_fp32_d128_attends_64_key_sub_blocks(lib):
     sh = _shape(batch=2, seq=4096, d=128, B=128, K=8, dtype=0)
     # BLASST takes whole blocks only
     assert lib.moba_attn_fwd_blasst(ctypes.byref(sh), p, p, p, p, ctypes.c_float(0.0),
-                                    ctypes.c_float(0.5), p, None, p, 1 << 40, None) == UNSUPPORTED
+                                    ctypes.c_float(0.5), p, None, None, p, 1 << 40, None) == UNSUPPORTED
+    # and so does its backward
+    assert lib.moba_attn_bwd_blasst(ctypes.byref(sh), p, p, p, p, ctypes.c_float(0.0), p, p, p,
+                                    ctypes.c_void_p(1 << 20), ctypes.c_void_p(1 << 21),
+                                    ctypes.c_void_p(1 << 22), p, 1 << 40, None) == UNSUPPORTED
+
+
+def test_blasst_kept_idx_checked_on_the_host(lib):
+    """kept_idx must be 16-byte aligned and must not be idx; refused
+    before any launch (no device memory is touched)."""
+    p = ctypes.c_void_p(16 * 1024)
+    sh = _shape(batch=1, seq=1024, B=64, K=4)
+    for bad in (ctypes.c_void_p(16 * 1024 + 4), p):
+        assert lib.moba_attn_fwd_blasst(ctypes.byref(sh), p, p, p, p, ctypes.c_float(0.0),
+                                        ctypes.c_float(0.5), p, None, bad, p, 1 << 40,
+                                        None) == INVALID
 
 
 def test_largest_accepted_shapes(lib):
