@@ -137,8 +137,10 @@ def test_random_blasst_matches_oracle(i):
     g = torch.Generator().manual_seed(9300 + i)
     dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     x = {n: torch.randn((T, H, d), generator=g).to(dt) for n in ("q", "k", "v")}
+    x["do"] = torch.randn((T, H, d), generator=g).to(dt)
     cu = [0]
     for L in lens:
         cu.append(cu[-1] + L)
     x["cu_seqlens"] = cu
-    tbl.check_blasst(x, cu, B, K, lam, dtype, f"sweep-blasst {i}")
+    # every third case also runs the BLASST backward on the GPU's decisions
+    tbl.check_blasst(x, cu, B, K, lam, dtype, f"sweep-blasst {i}", bwd=(i % 3 == 0))
