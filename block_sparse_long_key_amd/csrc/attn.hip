@@ -706,13 +706,23 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         if (pm) {
             float Mr = -INFINITY;
             keepm = 0u;
-            for (int p = 0; p < kmerge; ++p) {
-                const int ps = rrow[p];
-                if (ps < 0) continue;
-                const float mt = pm[eb + ps];
-                if (!(Mr > -INFINITY && mt - Mr < log2lam)) {
-                    keepm |= 1u << p;
-                    Mr = fmaxf(Mr, mt);
+            // PF slots' list positions, then their block maxima, are
+            // requested together; the decisions then run in registers, in
+            // slot order
+            for (int p0 = 0; p0 < kmerge; p0 += PF) {
+                int pos[PF];
+                float mt[PF];
+#pragma unroll
+                for (int u = 0; u < PF; ++u) pos[u] = p0 + u < kmerge ? rrow[p0 + u] : -1;
+#pragma unroll
+                for (int u = 0; u < PF; ++u) mt[u] = pos[u] >= 0 ? pm[eb + pos[u]] : 0.f;
+#pragma unroll
+                for (int u = 0; u < PF; ++u) {
+                    if (pos[u] < 0) continue;
+                    if (!(Mr > -INFINITY && mt[u] - Mr < log2lam)) {
+                        keepm |= 1u << (p0 + u);
+                        Mr = fmaxf(Mr, mt[u]);
+                    }
                 }
             }
             own_kept = !(Mr > -INFINITY && own_max[r] - Mr < log2lam);
