@@ -52,6 +52,13 @@ static void refused(const moba_shape *s, moba_status want_shape)
     EXPECT(moba_route_topk(s, odd, fp, ip, p, big, NULL) != MOBA_OK);
     EXPECT(moba_attn_fwd(s, NULL, p, p, ip, 0.0f, p, NULL, p, big, NULL) != MOBA_OK);
     EXPECT(moba_attn_index(s, NULL, p, big, NULL) != MOBA_OK);
+    EXPECT(moba_attn_fwd_blasst(s, NULL, p, p, ip, 0.0f, 0.5f, p, NULL, NULL, p, big, NULL) != MOBA_OK);
+    EXPECT(moba_attn_fwd_blasst(s, p, p, p, ip, 0.0f, 0.5f, p, NULL, ip, p, big, NULL) != MOBA_OK);
+    EXPECT(moba_attn_fwd_blasst(s, p, p, p, ip, 0.0f, 0.5f, p, NULL, (int32_t *)odd, p, big,
+                                NULL) != MOBA_OK);
+    EXPECT(moba_attn_fwd_blasst(s, p, p, p, ip, 0.0f, 1.5f, p, NULL, NULL, p, big, NULL) != MOBA_OK);
+    EXPECT(moba_attn_bwd(s, NULL, p, p, ip, 0.0f, p, fp, p, p, p, p, p, big, NULL) != MOBA_OK);
+    EXPECT(moba_attn_bwd_blasst(s, NULL, p, p, ip, 0.0f, p, fp, p, p, p, p, p, big, NULL) != MOBA_OK);
     EXPECT(moba_key_conv(s, p, fp, 3, 0, p, NULL, NULL) != MOBA_OK);   /* k' aliases k */
     if (want_shape != MOBA_OK) {
         EXPECT(moba_route_topk(s, p, fp, ip, p, big, NULL) == want_shape);
