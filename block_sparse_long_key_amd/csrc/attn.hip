@@ -451,6 +451,10 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
     const int L = seq_len(st, s);
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
+    // (debug builds: the item lies inside its (sequence, head) list region)
+    if (!MOBA_INBOUNDS(it.g >= 0 && it.g < st.total_blocks && h >= 0 && h < H && j < seq_nblk(st, s) &&
+                       it.begin >= 0 && (int64_t)it.begin + it.count <= (int64_t)L * K, kDbgItem))
+        return;
 
     // the item's (query, slot) entries go to LDS once; its partials are
     // written at the same (list-order) positions, so every tile writes one
@@ -479,8 +483,10 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
             const int r = b0 + 16 * sb + l16;
-            const bool ok = r < it.count;
             const uint32_t e = ev[sb];
+            const bool ok = r < it.count &&
+                            MOBA_INBOUNDS((int)(e >> 5) >= t0 && (int)(e >> 5) < t0 + L && (int)(e & 31u) < K,
+                                          kDbgEntry);
             const T* qrow = ok ? q + ((size_t)(e >> 5) * H + h) * D : nullptr;
             if constexpr (W::BF) {
 #pragma unroll
@@ -713,7 +719,10 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
                 int pos[PF];
                 float mt[PF];
 #pragma unroll
-                for (int u = 0; u < PF; ++u) pos[u] = p0 + u < kmerge ? rrow[p0 + u] : -1;
+                for (int u = 0; u < PF; ++u) {
+                    pos[u] = p0 + u < kmerge ? rrow[p0 + u] : -1;
+                    if (pos[u] >= 0 && !MOBA_INBOUNDS(pos[u] < L * K, kDbgMergePos)) pos[u] = -1;
+                }
 #pragma unroll
                 for (int u = 0; u < PF; ++u) mt[u] = pos[u] >= 0 ? pm[eb + pos[u]] : 0.f;
 #pragma unroll
@@ -751,8 +760,10 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         for (int p0 = 0; p0 < kmerge; p0 += PF) {
             int pos[PF];
 #pragma unroll
-            for (int u = 0; u < PF; ++u)
+            for (int u = 0; u < PF; ++u) {
                 pos[u] = (p0 + u < kmerge && ((keepm >> (p0 + u)) & 1u)) ? rrow[p0 + u] : -1;
+                if (pos[u] >= 0 && !MOBA_INBOUNDS(pos[u] < L * K, kDbgMergePos)) pos[u] = -1;
+            }
             float lp[PF];
             u32x4_t xv[PF];
 #pragma unroll
@@ -838,6 +849,15 @@ hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
 }
 
 }  // namespace
+
+uint32_t dbg_take_attn()
+{
+#ifdef MOBA_DEBUG_BOUNDS
+    return dbg_take_local();
+#else
+    return 0u;
+#endif
+}
 
 #define MOBA_DISPATCH(FN, ...)                                                        \
     do {                                                                              \

@@ -154,6 +154,9 @@ __global__ __launch_bounds__((64 * bwd_waves<D, BLK>()), 2) void bwd_list_kernel
     const int nq = min(BLK, L - j * BLK);        // rows of block j
     int2 li = make_int2(0, 0);
     if (routed) li = lst[item];
+    // (debug builds: the list lies inside its (sequence, head) region)
+    if (!MOBA_INBOUNDS(li.x >= 0 && li.y >= 0 && (int64_t)li.x + li.y <= (int64_t)L * K, kDbgBwdList))
+        li = make_int2(0, 0);
     const int64_t eb = st.ebase[s] + (int64_t)h * L * K;
     const int ndiag = (nq + kTileRows - 1) / kTileRows;
     const int ntiles = ndiag + (li.y + kTileRows - 1) / kTileRows;
@@ -209,8 +212,9 @@ __global__ __launch_bounds__((64 * bwd_waves<D, BLK>()), 2) void bwd_list_kernel
                 dest = diag_base + (int64_t)t * H + h;
             } else {
                 const int rr = kTileRows * (tile - ndiag) + r;
-                ok = rr < li.y;
                 t = (int)(pre_e[p] >> 5);
+                ok = rr < li.y &&
+                     MOBA_INBOUNDS(t >= t0 && t < t0 + L && (int)(pre_e[p] & 31u) < K, kDbgBwdEntry);
                 dest = eb + li.x + rr;
             }
             const size_t row = (size_t)t * H + h;
@@ -435,7 +439,10 @@ __global__ __launch_bounds__(kBwdThreads) void dq_combine_kernel(SegTable st, in
         for (int p0 = 0; p0 < K; p0 += PF) {
             int pos[PF];
 #pragma unroll
-            for (int u = 0; u < PF; ++u) pos[u] = p0 + u < K ? rrow[p0 + u] : -1;
+            for (int u = 0; u < PF; ++u) {
+                pos[u] = p0 + u < K ? rrow[p0 + u] : -1;
+                if (pos[u] >= 0 && !MOBA_INBOUNDS(pos[u] < seq_len(st, s) * K, kDbgDqPos)) pos[u] = -1;
+            }
             float4 x[PF];
 #pragma unroll
             for (int u = 0; u < PF; ++u)
@@ -507,6 +514,15 @@ hipError_t bwd_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q, 
 }
 
 }  // namespace
+
+uint32_t dbg_take_attn_bwd()
+{
+#ifdef MOBA_DEBUG_BOUNDS
+    return dbg_take_local();
+#else
+    return 0u;
+#endif
+}
 
 hipError_t launch_attn_bwd(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
                            const void* k, const void* v, const void* o, const float* lse,

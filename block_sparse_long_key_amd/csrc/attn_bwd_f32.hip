@@ -165,9 +165,14 @@ __global__ __launch_bounds__(64) void bwd_kv_f32_kernel(SegTable st, const int2*
     };
     // the queries that routed to block j, in list order
     if (K > 1) {
-        const int2 le = lst[(int64_t)h * st.total_blocks + st.boff[s] + j];
+        int2 le = lst[(int64_t)h * st.total_blocks + st.boff[s] + j];
+        if (!MOBA_INBOUNDS(le.x >= 0 && le.y >= 0 && (int64_t)le.x + le.y <= (int64_t)L * K, kDbgBwdList))
+            le = make_int2(0, 0);
         const uint32_t* ent = entries + st.ebase[s] + (int64_t)h * L * K + le.x;
-        for (int e = 0; e < le.y; ++e) add_row((int)(ent[e] >> 5));
+        for (int e = 0; e < le.y; ++e) {
+            const int t = (int)(ent[e] >> 5);
+            if (MOBA_INBOUNDS(t >= st.cu[s] && t < st.cu[s] + L, kDbgKvEntry)) add_row(t);
+        }
     }
     // the own-block queries t >= u (those that attend their own block)
     const int tend = min((j + 1) * B, L);
@@ -209,6 +214,15 @@ hipError_t bwd_f32_t(const Launch& L, const WsLayout& ws, char* wsp, const int32
 }
 
 }  // namespace
+
+uint32_t dbg_take_attn_bwd_f32()
+{
+#ifdef MOBA_DEBUG_BOUNDS
+    return dbg_take_local();
+#else
+    return 0u;
+#endif
+}
 
 hipError_t launch_attn_bwd_f32(const Launch& L, const WsLayout& ws, char* wsp, const int32_t* idx,
                                const void* q, const void* k, const void* v, const void* o,

@@ -293,10 +293,11 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
                 if (e >= e_hi) continue;
                 const int r = div.row(e), slot = e - r * K;
                 const uint32_t tok = (uint32_t)(t0 + tl0 + r) << 5;
-                if (pv[u].x >= 0) ent[pv[u].x] = tok | (uint32_t)slot;
-                if (pv[u].y >= 0) ent[pv[u].y] = tok | (uint32_t)(slot + 1);
-                if (pv[u].z >= 0) ent[pv[u].z] = tok | (uint32_t)(slot + 2);
-                if (pv[u].w >= 0) ent[pv[u].w] = tok | (uint32_t)(slot + 3);
+                // (debug builds: positions inside the (sequence, head) region)
+                if (pv[u].x >= 0 && MOBA_INBOUNDS(pv[u].x < L * K, kDbgScatter)) ent[pv[u].x] = tok | (uint32_t)slot;
+                if (pv[u].y >= 0 && MOBA_INBOUNDS(pv[u].y < L * K, kDbgScatter)) ent[pv[u].y] = tok | (uint32_t)(slot + 1);
+                if (pv[u].z >= 0 && MOBA_INBOUNDS(pv[u].z < L * K, kDbgScatter)) ent[pv[u].z] = tok | (uint32_t)(slot + 2);
+                if (pv[u].w >= 0 && MOBA_INBOUNDS(pv[u].w < L * K, kDbgScatter)) ent[pv[u].w] = tok | (uint32_t)(slot + 3);
                 *(int4*)(rv + e) = pv[u];
             }
         }
@@ -322,7 +323,8 @@ __global__ __launch_bounds__(kThreads) void inv_scatter_kernel(SegTable st, cons
         for (int u = 0; u < kBatch; ++u) {
             const int e = e0 + u * STEP;
             const int r = div.row(e), slot = e - r * K;
-            if (pv[u] >= 0) ent[pv[u]] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
+            if (pv[u] >= 0 && MOBA_INBOUNDS(pv[u] < L * K, kDbgScatter))
+                ent[pv[u]] = ((uint32_t)(t0 + tl0 + r) << 5) | (uint32_t)slot;
             // every slot is written, so each query's K positions form one
             // contiguous, fully written record
             if (e < e_hi) rv[e] = pv[u];
@@ -370,6 +372,15 @@ __global__ __launch_bounds__(kThreads) void expand_idx_kernel(SegTable stl, int 
 }
 
 }  // namespace
+
+uint32_t dbg_take_invert()
+{
+#ifdef MOBA_DEBUG_BOUNDS
+    return dbg_take_local();
+#else
+    return 0u;
+#endif
+}
 
 hipError_t launch_expand_idx(const Launch& Ll, int ab, int Kp, const int32_t* idx, int32_t* pidx)
 {

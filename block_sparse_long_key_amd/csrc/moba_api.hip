@@ -570,6 +570,18 @@ extern "C" {
 
 int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
 
+int32_t moba_debug_violations(uint32_t* flags)
+{
+#ifdef MOBA_DEBUG_BOUNDS
+    if (!flags) return MOBA_ERR_INVALID_ARG;
+    *flags = dbg_take_attn() | dbg_take_attn_bwd() | dbg_take_attn_bwd_f32() | dbg_take_invert();
+    return MOBA_OK;
+#else
+    (void)flags;
+    return MOBA_ERR_UNSUPPORTED;
+#endif
+}
+
 // (an int: a C caller may pass any value, which a C++ enum parameter of
 // this range could not hold without undefined behaviour)
 const char* moba_status_string(int32_t s)

@@ -99,6 +99,50 @@ __device__ inline int seq_of_chunk(const SegTable& st, int c) {
     return lo;
 }
 
+// ------------------------------------------------------ bounds checks --
+// Debug builds (-DMOBA_DEBUG_BOUNDS, libmoba_amd_debug.so) check every
+// index that kernels take from data -- list entries, list positions, work
+// items -- against the region it addresses before the access; a failed
+// check sets a bit in this source file's violation word and the kernel
+// skips or clamps the access instead of leaving its buffers.  Release
+// builds compile MOBA_INBOUNDS to true (the condition is not evaluated), so
+// their code is unchanged.  Bits:
+enum : unsigned {
+    kDbgItem = 1u,         // routed item outside its (sequence, head) list region
+    kDbgEntry = 2u,        // routed list entry: token outside the list's sequence, or slot >= K
+    kDbgMergePos = 4u,     // merge: list position outside the region
+    kDbgBwdList = 8u,      // backward: a list's (first, count) outside the region
+    kDbgBwdEntry = 16u,    // backward: list entry token outside the sequence, or slot >= K
+    kDbgDqPos = 32u,       // dq merge: list position outside the region
+    kDbgScatter = 64u,     // index pass: list position outside the region
+    kDbgKvEntry = 128u,    // fp32 backward (dk, dv): list entry outside the sequence
+};
+#ifdef MOBA_DEBUG_BOUNDS
+namespace {
+__device__ unsigned int g_dbg_violations = 0u;   // one per source file
+// this source file's violation word on the current device, then cleared
+// (a synchronous copy on the null stream)
+inline uint32_t dbg_take_local()
+{
+    uint32_t v = 0u;
+    const uint32_t z = 0u;
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dbg_violations), sizeof(v), 0, hipMemcpyDeviceToHost) != hipSuccess)
+        return 0x80000000u;
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_dbg_violations), &z, sizeof(z), 0, hipMemcpyHostToDevice) != hipSuccess)
+        return 0x80000000u;
+    return v;
+}
+}  // namespace
+#define MOBA_INBOUNDS(cond, bit) ((cond) || (atomicOr(&g_dbg_violations, (unsigned)(bit)), false))
+#else
+#define MOBA_INBOUNDS(cond, bit) true
+#endif
+// each source file's violation word (0 in release builds)
+uint32_t dbg_take_attn();
+uint32_t dbg_take_attn_bwd();
+uint32_t dbg_take_attn_bwd_f32();
+uint32_t dbg_take_invert();
+
 // ------------------------------------------------------------ bf16 ------
 // bf16 is carried as its 16-bit pattern.  Rounding is IEEE round to nearest,
 // ties to even, done by the hardware conversion (v_cvt_pk_bf16_f32).

@@ -360,6 +360,23 @@ int64_t moba_total_blocks(const moba_shape *shape);
 const char *moba_status_string(int32_t status);
 int32_t moba_abi_version(void);
 
+/*
+ * moba_debug_violations -- for the bounds-checking debug build of this
+ * library (libmoba_amd_debug.so, compiled with MOBA_DEBUG_BOUNDS), where the
+ * kernels check every index they take from data (list entries, list
+ * positions, work items) against the region it addresses and skip an
+ * access that would leave it.  Writes to *flags the OR of the violations
+ * seen on the current device since the last call (0: none; bits 0..7: the
+ * check that failed, in the order routed item, routed entry, merge
+ * position, backward list, backward entry, dq position, index-pass
+ * position, fp32 backward entry; bit 31: the flags could not be read) and
+ * clears them.  Synchronous (waits for the device).  The release library
+ * returns MOBA_ERR_UNSUPPORTED and writes nothing; a null flags pointer is
+ * MOBA_ERR_INVALID_ARG.  For tests of the kernels' indexing, not for use
+ * while other calls run.
+ */
+int32_t moba_debug_violations(uint32_t *flags);
+
 #ifdef __cplusplus
 }
 #endif

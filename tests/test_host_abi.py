@@ -43,6 +43,24 @@ def test_exports_every_declared_function(lib):
     assert lib.moba_status_string(WS_SMALL) == b"workspace too small"
 
 
+def test_debug_build_exports_and_release_has_no_checks(lib):
+    """The bounds-checking build exports every declared function under the
+    same ABI; the release build answers moba_debug_violations with
+    MOBA_ERR_UNSUPPORTED and leaves the flags alone (no device access)."""
+    from block_sparse_long_key_amd import build as mbuild
+    if not os.path.exists(mbuild.DEBUG_LIB):
+        pytest.skip("the debug library is not built")
+    dbg = ctypes.CDLL(mbuild.DEBUG_LIB)
+    for n in _declared():
+        assert hasattr(dbg, n), f"{n} not exported by the debug build"
+    assert dbg.moba_abi_version() == lib.moba_abi_version()
+    lib.moba_debug_violations.argtypes = [ctypes.c_void_p]
+    lib.moba_debug_violations.restype = ctypes.c_int32
+    f = ctypes.c_uint32(7)
+    assert lib.moba_debug_violations(ctypes.byref(f)) == UNSUPPORTED
+    assert f.value == 7
+
+
 def _shape(batch=1, seq=1024, heads=2, d=64, B=64, K=4, dtype=1, cu=None):
     if cu is not None:
         arr = (ctypes.c_int32 * len(cu))(*cu)

@@ -77,11 +77,13 @@ def _first_reads(lines, labels, start, dst, ws, seen):
 
 @pytest.mark.skipif(shutil.which(libbuild.HIPCC) is None and not os.path.exists(libbuild.HIPCC),
                     reason="hipcc not available")
+@pytest.mark.parametrize("debug", [False, True], ids=["release", "debug-bounds"])
 @pytest.mark.parametrize("src", SOURCES)
-def test_mfma_results_read_after_enough_wait_states(src, tmp_path):
+def test_mfma_results_read_after_enough_wait_states(src, debug, tmp_path):
+    """Both builds: the bounds-checking one adds branches of its own."""
     out = tmp_path / (src + ".s")
-    cmd = [libbuild.HIPCC, *libbuild.FLAGS, "--cuda-device-only", "-S",
-           os.path.join(libbuild.CSRC, src), "-o", str(out)]
+    cmd = [libbuild.HIPCC, *libbuild.FLAGS, *(["-DMOBA_DEBUG_BOUNDS"] if debug else []),
+           "--cuda-device-only", "-S", os.path.join(libbuild.CSRC, src), "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     asm = out.read_text()
     bad = []
