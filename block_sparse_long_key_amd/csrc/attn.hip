@@ -581,10 +581,17 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
             }
             if (ok[sb] && g4 == 0) {
                 const float lv = m2[sb] + __builtin_amdgcn_logf(sum[sb]);
-                if constexpr (STAGE) __builtin_nontemporal_store(lv, pl + prow);
-                else pl[prow] = lv;
-                // the block's maximum score (log2 units), for the BLASST skip
-                if (pm) pm[prow] = m2[sb];
+                if (pm) {
+                    // BLASST: the log2-sum-exp and the block's maximum score
+                    // (log2 units) side by side, so the merge's skip decision
+                    // and its weight come from one 8-byte read
+                    const f32x2_t lm = {lv, m2[sb]};
+                    __builtin_nontemporal_store(lm, (f32x2_t*)pm + prow);
+                } else if constexpr (STAGE) {
+                    __builtin_nontemporal_store(lv, pl + prow);
+                } else {
+                    pl[prow] = lv;
+                }
             }
         }
     }
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
                     if (pos[u] >= 0 && !MOBA_INBOUNDS(pos[u] < L * K, kDbgMergePos)) pos[u] = -1;
                 }
 #pragma unroll
-                for (int u = 0; u < PF; ++u) mt[u] = pos[u] >= 0 ? pm[eb + pos[u]] : 0.f;
+                for (int u = 0; u < PF; ++u) mt[u] = pos[u] >= 0 ? ((const f32x2_t*)pm)[eb + pos[u]][1] : 0.f;
 #pragma unroll
                 for (int u = 0; u < PF; ++u) {
                     if (pos[u] < 0) continue;
@@ -770,7 +777,8 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
             for (int u = 0; u < PF; ++u) {
                 if (pos[u] >= 0) {
                     const int64_t prow = eb + pos[u];
-                    lp[u] = pl[prow];
+                    // (BLASST: the pair the decision just read, now cached)
+                    lp[u] = pm ? ((const f32x2_t*)pm)[prow][0] : pl[prow];
                     xv[u] = *(const u32x4_t*)(po + prow * D + c * CH);
                 }
             }

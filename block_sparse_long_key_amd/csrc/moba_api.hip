@@ -124,7 +124,7 @@ WsLayout layout(const Launch& L, bool bwd = false, bool expand = false)
             // partials are indexed like the entries (list order)
             w.po_bytes = (size_t)st.ebase[st.nseq] * L.D * esz;
             w.pl_bytes = (size_t)st.ebase[st.nseq] * 4;
-            w.pm_bytes = (size_t)st.ebase[st.nseq] * 4;
+            w.pm_bytes = (size_t)st.ebase[st.nseq] * 8;
         }
     }
     if (bwd) {

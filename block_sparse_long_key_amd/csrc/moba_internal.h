@@ -198,7 +198,7 @@ struct WsLayout {
     size_t rev_off, rev_bytes;       // int32 [H][tokens][K]: list position of (t, slot), -1 if none
     size_t po_off, po_bytes;         // partial o rows, list order (I/O dtype, D per row)
     size_t pl_off, pl_bytes;         // partial lse, list order, fp32 (log2 units)
-    size_t pm_off, pm_bytes;         // partial block maximum, list order, fp32 (log2 units; BLASST)
+    size_t pm_off, pm_bytes;         // BLASST: (partial lse, block maximum) fp32 pairs, list order (log2 units)
     size_t lst_off, lst_bytes;       // int2 [H][total blocks]: (first entry, count) of each list
     size_t rs_off, rs_bytes;         // backward: float2 [tokens][H] (lse in log2 units, dO . O)
     size_t pq_off, pq_bytes;         // backward: fp32 dq pieces, list order, then own-block rows
