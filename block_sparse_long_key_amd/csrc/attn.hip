@@ -605,7 +605,9 @@ __global__ __launch_bounds__(64 * kRoutedWaves, (sizeof(T) == 2 && D == 64 ? 4 :
 // (query, 16-byte chunk); the query's list positions come from the reverse
 // map built by the index pass, its partial rows are gathered as coalesced
 // 16-byte chunks and merged with a running (max, sum) in log2 units.
-template <typename T, int D, int BLK>
+// BL: the BLASST variant (skip decisions, the kept selection, the partials'
+// (lse, maximum) pairs); the plain merge is compiled without that code.
+template <typename T, int D, int BLK, bool BL>
 __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void diag_combine_kernel(
     SegTable st, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ rev, const T* __restrict__ po, const float* __restrict__ pl,
@@ -716,7 +718,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         // kept blocks takes no part.  Without it every slot is kept.
         uint32_t keepm = 0xffffffffu;
         bool own_kept = true;
-        if (pm) {
+        if (BL && pm) {
             float Mr = -INFINITY;
             keepm = 0u;
             // PF slots' list positions, then their block maxima, are
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
         }
         // the attended selection: idx's routed blocks that were kept, then
         // the own block if kept, ascending, -1 padded
-        if (kept && c == 0) {
+        if (BL && kept && c == 0) {
             const int32_t* irow = idx + qrow * K;
             int32_t* krow = kept + qrow * K;
             int n = 0;
@@ -778,7 +780,7 @@ __global__ __launch_bounds__(2 * BLK, (sizeof(T) == 2 && D == 64 ? 4 : 1)) void 
                 if (pos[u] >= 0) {
                     const int64_t prow = eb + pos[u];
                     // (BLASST: the pair the decision just read, now cached)
-                    lp[u] = pm ? ((const f32x2_t*)pm)[prow][0] : pl[prow];
+                    lp[u] = (BL && pm) ? ((const f32x2_t*)pm)[prow][0] : pl[prow];
                     xv[u] = *(const u32x4_t*)(po + prow * D + c * CH);
                 }
             }
@@ -846,7 +848,9 @@ hipError_t diag_t(const Launch& L, const WsLayout& ws, char* wsp, const void* q,
     if (L.st.total_blocks == 0) return hipSuccess;
     // the index pass turned idx into the reverse map; idx itself is read
     // only to write the kept selection
-    hipLaunchKernelGGL((diag_combine_kernel<T, D, BLK>), dim3(L.st.total_blocks, L.st.H),
+    const bool bl = blasst_lambda > 0.f || kept;
+    auto kern = bl ? diag_combine_kernel<T, D, BLK, true> : diag_combine_kernel<T, D, BLK, false>;
+    hipLaunchKernelGGL(kern, dim3(L.st.total_blocks, L.st.H),
                        dim3(2 * BLK), 0, L.stream, L.st, (const T*)q, (const T*)k, (const T*)v,
                        (const int32_t*)(wsp + ws.rev_off), (const T*)(wsp + ws.po_off),
                        (const float*)(wsp + ws.pl_off),
