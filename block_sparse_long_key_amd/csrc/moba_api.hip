@@ -570,7 +570,7 @@ extern "C" {
 
 int32_t moba_abi_version(void) { return MOBA_ABI_VERSION; }
 
-int32_t moba_debug_violations(uint32_t* flags)
+moba_status moba_debug_violations(uint32_t* flags)
 {
 #ifdef MOBA_DEBUG_BOUNDS
     if (!flags) return MOBA_ERR_INVALID_ARG;

@@ -375,7 +375,7 @@ int32_t moba_abi_version(void);
  * MOBA_ERR_INVALID_ARG.  For tests of the kernels' indexing, not for use
  * while other calls run.
  */
-int32_t moba_debug_violations(uint32_t *flags);
+moba_status moba_debug_violations(uint32_t *flags);
 
 #ifdef __cplusplus
 }

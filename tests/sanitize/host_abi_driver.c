@@ -70,6 +70,10 @@ static void refused(const moba_shape *s, moba_status want_shape)
 int main(void)
 {
     EXPECT(moba_abi_version() > 0);
+    {
+        uint32_t f = 7u;      /* the release library has no bounds checks */
+        EXPECT(moba_debug_violations(&f) == MOBA_ERR_UNSUPPORTED && f == 7u);
+    }
     for (int c = -3; c < 16; ++c) EXPECT(moba_status_string((moba_status)c) != NULL);
 
     /* uniform batches over every supported block size, k and dtype */
