@@ -99,3 +99,61 @@ def test_selection_errors_tolerance_edges():
     assert parity.selection_errors([0, 1, 2, -1], s, 2, 4) == []
     assert parity.selection_errors([0, 2, -1, -1], s, 2, 4)
     assert parity.selection_errors([0, 1, 2, 5], s, 2, 4)
+
+
+# ------------------------------------------------- BLASST kept selections ----
+# The GPU tests' check of a BLASST forward's kept selection
+# (tests/test_blasst_gpu.py: _check_kept_format, _keep_of) on the CPU: the
+# oracle's own decisions written as a kept selection pass, and planted
+# mistakes are refused ("BLASST", summary page, "Meccanismo di Pruning": the
+# first block visited is never skipped; skipped blocks leave the row).
+def _kept_case(lam=0.3, seed=71):
+    import test_blasst_gpu as tbl
+    g = np.random.default_rng(seed)
+    B, K, H, d = 4, 4, 2, 8
+    cu = [0, 30, 30, 61]
+    T = cu[-1]
+    q, k, v = (g.standard_normal((T, H, d)).astype(np.float32) for _ in range(3))
+    idx, *_ = oracle.route(q, oracle.centroids(k, B, cu), B, K, cu)
+    *_, keep = oracle.attend_blasst(q, k, v, idx, B, K, cu, lam, return_keep=True)
+    kept = np.full(idx.shape, -1, np.int32)
+    for r in np.ndindex(idx.shape[:2]):
+        sel = [j for j, kk in zip(idx[r], keep[r]) if kk and j >= 0]
+        kept[r][:len(sel)] = sel
+    return tbl, idx, keep, kept
+
+
+def test_blasst_kept_from_the_oracle_passes_and_maps_back():
+    tbl, idx, keep, kept = _kept_case()
+    assert not keep[idx >= 0].all()              # something was skipped
+    tbl._check_kept_format(kept, idx)
+    assert np.array_equal(tbl._keep_of(kept, idx), keep)
+
+
+@pytest.mark.parametrize("mistake", ["first_dropped", "not_ascending", "hole", "foreign_block",
+                                     "duplicate"])
+def test_blasst_kept_planted_mistakes_are_refused(mistake):
+    tbl, idx, keep, kept = _kept_case()
+    bad = kept.copy()
+    K = idx.shape[-1]
+    n = (bad >= 0).sum(-1)
+    rows = np.argwhere((n >= 2) & (n < K))       # room for a hole after the last block
+    assert len(rows)
+    t, h = rows[len(rows) // 2]
+    m = int(n[t, h])
+    row = bad[t, h]
+    if mistake == "first_dropped":
+        row[:m - 1] = row[1:m].copy()
+        row[m - 1] = -1
+    elif mistake == "not_ascending":
+        row[0], row[1] = row[1], row[0]
+    elif mistake == "hole":
+        row[m] = row[m - 1]
+        row[m - 1] = -1
+    elif mistake == "foreign_block":
+        listed = set(idx[t, h].tolist())
+        row[m - 1] = next(j for j in range(1000, 2000) if j not in listed)
+    elif mistake == "duplicate":
+        row[1] = row[0]
+    with pytest.raises(AssertionError):
+        tbl._check_kept_format(bad, idx)
